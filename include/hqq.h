@@ -1,0 +1,117 @@
+/*
+ * hqq.h -- C ABI of the MI355X (gfx950) HQQ weight-quantization library.
+ *
+ * HQQ (half-quadratic quantization) quantizes each group of group_size
+ * weights of an fp16 Linear weight matrix to nbits-bit integer codes that
+ * share one fp32 scale and one fp32 zero point.  It needs no calibration data:
+ * the error is split through an auxiliary variable W_e and the zero point is
+ * refit by alternating minimisation.
+ *   Sources: lnwmold.com HQQ guide, section 2.1 (calibration-free
+ *   half-quadratic splitting into alternating sub-problems), section 2.2
+ *   (nbits, group_size, axis), section 3.2 (HQQLinear state W_q / scale /
+ *   zero, dequantize(), unpack()); devpress.csdn.net "dropbox/hqq" tutorial,
+ *   section 2 (auxiliary variable, robust non-convex loss) and section 3.3
+ *   (BaseQuantizeConfig).
+ *
+ * The solve, per group of gs weights w, with b = nbits and qmax = 2^b - 1:
+ *   scale = qmax / (max w - min w),  zero = -(min w * scale)
+ *   (a constant group has scale = 1, zero = -min w)
+ *   repeat iters times, beta starting at beta0:
+ *     W_q  = clamp(round_half_even(w * scale + zero), 0, qmax)
+ *     W_r  = (W_q - zero) / scale,  x = w - W_r
+ *     W_e  = sign(x) * max(|x| - |x|^(p-1) / beta, 0)
+ *     zero = mean(W_q - (w - W_e) * scale)
+ *     beta = beta * kappa
+ *   codes = clamp(round_half_even(w * scale + zero), 0, qmax)
+ * Defaults: p = 0.7, beta0 = 10, kappa = 1.01, iters = 20.  The result is
+ * bit-for-bit the fp32 evaluation in which w*scale+zero is one fused
+ * multiply-add and the mean is (sum W_q - scale*(sum w - sum W_e)) / gs in
+ * fp64 (the two first sums exact, sum W_e in ascending element order), then
+ * rounded once to fp32.
+ *
+ * Layout.  W is fp16 (IEEE binary16 bits), row-major [rows, cols] with
+ * rows = out_features and cols = in_features.
+ *   axis = 1: a group is group_size consecutive elements of one row
+ *             (along in_features, contiguous); scale/zero are [rows, cols/gs].
+ *   axis = 0: a group is group_size consecutive rows of one column
+ *             (along out_features, strided); scale/zero are [rows/gs, cols].
+ * Codes are packed along the group axis: C = 8 (4-bit), 10 (3-bit),
+ * 16 (2-bit) or 32 (1-bit) codes per uint32; word k of a line holds the
+ * line's codes k*C .. k*C+C-1, code j in bits [j*b, j*b+b) (LSB first); the
+ * unused fields of a line's last word, and bits 30-31 of 3-bit words, are 0.
+ *   axis = 1: packed is [rows, ceil(cols/C)];  axis = 0: [ceil(rows/C), cols].
+ * scale is codes per unit of weight: dequantization divides by it.
+ *
+ * Conventions for every entry point.
+ *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors), owned by
+ *     the caller; the library allocates nothing and keeps no state, so calls
+ *     are thread-safe.  Inputs are never written; outputs must not overlap
+ *     inputs.  Every pointer must be 16-byte aligned.
+ *   - stream is a hipStream_t passed as void*; NULL is the null stream.  Calls
+ *     only enqueue work: results are ready when the stream reaches them.
+ *   - Arguments are validated on the host before any HIP call; on failure
+ *     nothing is enqueued and a negative HQQ_E* status is returned.
+ *     HQQ_EHIP reports a failed kernel launch.  Contents of W that are NaN or
+ *     Inf are a precondition violation and are not checked.
+ *   - Supported: nbits in {1,2,3,4}; group_size in {8,16,32,64,128,256},
+ *     dividing the line length (cols for axis 1, rows for axis 0).
+ */
+#ifndef HQQ_H
+#define HQQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQQ_OK 0
+#define HQQ_EINVAL_NBITS (-1) /* nbits not in {1,2,3,4}                              */
+#define HQQ_EINVAL_AXIS (-2)  /* axis not in {0,1}                                   */
+#define HQQ_EINVAL_GROUP (-3) /* group_size unsupported or not dividing the line     */
+#define HQQ_EINVAL_SHAPE (-4) /* rows or cols < 1, or too large                      */
+#define HQQ_EINVAL_PTR (-5)   /* NULL or misaligned pointer                          */
+#define HQQ_EINVAL_PARAM (-6) /* iters < 0, or p, beta0, kappa not finite and > 0    */
+#define HQQ_EHIP (-7)         /* a HIP launch failed                                  */
+
+/* Quantize W with the HQQ solve above (lnwmold.com HQQ guide sections 2.1-2.2;
+ * devpress.csdn.net tutorial section 2).
+ *   W       fp16 bits [rows, cols], device, read only
+ *   packed  uint32, hqq_packed_words(rows, cols, nbits, axis) words, written
+ *   scale, zero  fp32, rows*cols/group_size values each, written
+ * Returns HQQ_OK or a negative HQQ_E* status. */
+int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols,
+                 int nbits, int group_size, int axis,
+                 int iters, float p, float beta0, float kappa,
+                 uint32_t *packed, float *scale, float *zero, void *stream);
+
+/* Dequantize: W_hat = fp16_round_half_even((W_q - zero) / scale) with an
+ * IEEE fp32 subtraction and division (lnwmold.com HQQ guide section 3.2,
+ * HQQLinear.dequantize()).  W_hat is fp16 bits [rows, cols], written. */
+int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero,
+                   int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                   uint16_t *W_hat, void *stream);
+
+/* Pack uint8 codes [rows, cols] (W's layout; only the low nbits of each byte
+ * are used) into the packed layout above (lnwmold.com HQQ guide section 3.2:
+ * W_q is stored packed).  group_size is validated as for hqq_quantize but
+ * does not change the layout. */
+int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
+             int nbits, int group_size, int axis, uint32_t *packed, void *stream);
+
+/* Unpack to uint8 codes [rows, cols] (lnwmold.com HQQ guide section 3.2,
+ * HQQLinear.unpack(dtype=uint8)). */
+int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
+               int nbits, int group_size, int axis, uint8_t *codes, void *stream);
+
+/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
+ * invalid arguments.  Host only, no HIP call. */
+int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
+
+/* Static description of a status code.  Host only. */
+const char *hqq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HQQ_H */

@@ -1,0 +1,89 @@
+/*
+ * hqq_oracle.h -- CPU oracle for the HQQ group-wise weight quantization solve.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library product links, loads or
+ * calls this code; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no source, header, table or helper with the
+ * HIP path.
+ *
+ * Sources (the web pages this project is built from):
+ *   [devpress]  devpress.csdn.net tutorial "dropbox/hqq", section 2 (core
+ *               principle: auxiliary variable, alternating optimisation) and
+ *               section 3.3 (nbits / group_size / axis meaning).
+ *   [lnwmold]   lnwmold.com HQQ guide, section 2.1 (calibration-free
+ *               half-quadratic splitting into two alternating sub-problems),
+ *               section 2.2 (nbits, group_size, axis: axis=0 groups along the
+ *               output dimension, axis=1 along the input dimension), section
+ *               3.2 (HQQLinear: W_q, scale, zero, dequantize(), unpack()).
+ *   [ainews]    ainews.cool Dropbox-HQQ analysis, "technical deep dive"
+ *               (reconstruction objective, auxiliary variable, alternation).
+ * The pages give the structure but no update equations; the equations this
+ * oracle implements are the HQQ solve as fixed for this library and written
+ * out in hqq_oracle.c.  Every reading of a point the pages leave open is
+ * listed there.
+ *
+ * Conventions: W is fp16 bits, row-major [rows, cols] (rows = out_features,
+ * cols = in_features).  axis=1: a group is gs consecutive elements of a row;
+ * axis=0: gs consecutive rows of one column.  Codes are packed along the
+ * group axis, LSB first, C = 8 (4b), 10 (3b), 16 (2b), 32 (1b) per uint32.
+ * All functions return 0 on success, a negative value on invalid arguments.
+ */
+#ifndef HQQ_ORACLE_H
+#define HQQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* exact fp16 -> fp32 widening, computed from the fields' values */
+float hqq_ref_f16_to_f32(uint16_t h);
+/* fp32 -> fp16, round to nearest even, subnormals and overflow handled */
+uint16_t hqq_ref_f32_to_f16(float f);
+
+/* the lp shrinkage W_e = sign(x) * max(|x| - |x|^(p-1) / beta, 0) for one residual */
+float hqq_ref_shrink(float x, float p, float beta);
+
+/* Solve one group of gs fp32 weights.  Optional traces (NULL to skip):
+ *   tr_zero[iters+1]  zero before iteration 0 .. after the last iteration
+ *   tr_beta[iters]    beta used in each iteration
+ *   tr_q[iters*gs]    W_q computed in each iteration
+ *   tr_x[iters*gs]    residual x = W - W_r in each iteration
+ *   tr_e[iters*gs]    W_e in each iteration                                  */
+int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
+                        float p, float beta0, float kappa,
+                        uint8_t *codes, float *scale, float *zero,
+                        float *tr_zero, float *tr_beta,
+                        float *tr_q, float *tr_x, float *tr_e);
+
+/* Whole-tensor solve: codes (uint8 [rows, cols], W's layout), scale and zero
+ * (axis=1: [rows, cols/gs]; axis=0: [rows/gs, cols]). */
+int hqq_ref_quantize_codes(const uint16_t *W, int64_t rows, int64_t cols,
+                           int nbits, int group_size, int axis, int iters,
+                           float p, float beta0, float kappa,
+                           uint8_t *codes, float *scale, float *zero);
+
+/* Whole-tensor solve with packed output. */
+int hqq_ref_quantize(const uint16_t *W, int64_t rows, int64_t cols,
+                     int nbits, int group_size, int axis, int iters,
+                     float p, float beta0, float kappa,
+                     uint32_t *packed, float *scale, float *zero);
+
+/* number of uint32 words of the packed layout, <0 on bad arguments */
+int64_t hqq_ref_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
+
+int hqq_ref_pack(const uint8_t *codes, int64_t rows, int64_t cols,
+                 int nbits, int axis, uint32_t *packed);
+int hqq_ref_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
+                   int nbits, int axis, uint8_t *codes);
+
+/* W_hat = fp16_rne((W_q - zero) / scale), fp32 arithmetic */
+int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *zero,
+                       int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                       uint16_t *W_hat);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
