@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the HQQ solve on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step quantizes every tensor of the workload once (one hqq_quantize launch
+per Linear weight), with all fp16 inputs already resident in HBM.  The default
+workload is the 7B-shaped stack: 32 decoder layers of q/k/v/o [4096,4096],
+gate/up [11008,4096], down [4096,11008] -- 6,476,005,376 fp16 weights
+(12.95 GB) -- at nbits=4, group_size=64, axis=1, 20 iterations, p=0.7,
+beta0=10, kappa=1.01.  Inputs are seeded synthetic weights generated on the
+GPU (synth/), standing in for the trained checkpoints the pages quantize.
+
+Prints one JSON line: the metric (GB/s of fp16 weights quantized), the
+roofline of the solve kernel (measured with HIP events around each launch
+inside the timed region, on the launch stream), and the CPU oracle timed on
+this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s of fp16 weights quantized (HQQ 4b g64, 20 it), 7B-shaped; % roofline"
+
+# MI355X (gfx950) peaks.  VALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz lane-ops
+# per second for non-packed fp32 (the 157.3 TFLOP/s headline counts an FMA as
+# 2 flops and packed fp32 as 2 lanes).  HBM3E: 8 TB/s.
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+
+# Algorithmic VALU ops per weight of the solve (the minimum the method needs
+# per element, per-group work excluded): per iteration fma, round, clamp,
+# accumulate W_q (4); once: widen, min, max, exact sum (2), final fma, round,
+# clamp, to-int, pack (5) -> 10.
+def valu_ops_per_weight(iters: int) -> int:
+    return 4 * iters + 10
+
+
+def hbm_bytes_per_weight(nbits: int, group_size: int) -> float:
+    C = {4: 8, 3: 10, 2: 16, 1: 32}[nbits]
+    return 2.0 + 4.0 / C + 8.0 / group_size
+
+
+def cpu_baseline(workload: str, iters: int, max_procs: int = 16):
+    """Time the oracle (single-threaded C, as it stands) on decoder layer 0 of
+    the workload, in P independent processes over row slices."""
+    import multiprocessing as mp
+
+    import synth
+
+    tensors = [t for t in synth.workload(workload) if t["layer"] == 0]
+    P = max(1, min(max_procs, os.cpu_count() or 1))
+    jobs = []
+    for t in tensors:
+        step = max(1, t["rows"] // P)
+        for r0 in range(0, t["rows"], step):
+            jobs.append((t, r0, min(step, t["rows"] - r0), iters))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(P) as pool:
+        res = pool.map(_cpu_job, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    n = sum(r[0] for r in res)
+    busy = sum(r[1] for r in res)
+    # throughput over the oracle's own time (generation excluded): total
+    # weights over the busy time spread across the P processes
+    eff_wall = busy / P
+    return dict(value=round(2.0 * n / eff_wall / 1e9, 6), unit="GB/s", cores=P, kind="oracle",
+                sample=f"decoder layer 0 of {workload} ({n:,} weights), oracle in {P} "
+                       f"single-threaded processes over row slices; {busy:.1f} core-s, "
+                       f"{wall:.1f} s wall incl. host generation",
+                weights_per_s=round(n / eff_wall, 1))
+
+
+def _cpu_job(job):
+    import oracle
+    import synth
+
+    t, r0, nr, iters = job
+    W = synth.generate_np(t["seed"], t["layer"], t["tensor_id"], t["rows"], t["cols"], row0=r0,
+                          nrows=nr)
+    t0 = time.perf_counter()
+    oracle.quantize(W, t["nbits"], t["group_size"], t["axis"], iters=iters)
+    return W.size, time.perf_counter() - t0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama7b_stack32_4b_g64")
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the solve shards with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    # the CPU baseline runs first, in forked processes, before this process
+    # touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.iters)
+
+    import torch
+
+    import synth
+    import weight_quantization_group_amd as hq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    hq.load_library()
+    dev = torch.device("cuda:0")
+    tensors = synth.workload(args.workload)
+
+    # resident inputs and outputs
+    ins, outs = [], []
+    for t in tensors:
+        W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
+        synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+        ins.append(W)
+        outs.append((torch.empty(hq.packed_shape(t["rows"], t["cols"], t["nbits"], t["axis"]),
+                                 dtype=torch.int32, device=dev),
+                     torch.empty(hq.meta_shape(t["rows"], t["cols"], t["group_size"], t["axis"]),
+                                 dtype=torch.float32, device=dev),
+                     torch.empty(hq.meta_shape(t["rows"], t["cols"], t["group_size"], t["axis"]),
+                                 dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    n_weights = sum(t["rows"] * t["cols"] for t in tensors)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(events=None):
+        for i, (t, W, (pk, sc, ze)) in enumerate(zip(tensors, ins, outs)):
+            if events is not None:
+                events[i][0].record()
+            hq.hqq_quantize(W, t["nbits"], t["group_size"], t["axis"], iters=args.iters,
+                            packed=pk, scale=sc, zero=ze)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in tensors] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-launch kernel durations (HIP events on the launch stream)
+    kdur = [[evs[k][i][0].elapsed_time(evs[k][i][1]) for i in range(len(tensors))]
+            for k in range(args.steps)]
+    # dominant kernel: the (nbits, group_size, axis) with the most weights
+    by_fmt = {}
+    for i, t in enumerate(tensors):
+        key = (t["nbits"], t["group_size"], t["axis"])
+        d = by_fmt.setdefault(key, dict(w=0, ms=0.0, launches=0))
+        d["w"] += t["rows"] * t["cols"] * args.steps
+        d["ms"] += sum(kdur[k][i] for k in range(args.steps))
+        d["launches"] += args.steps
+    (nb, gs, ax), dom = max(by_fmt.items(), key=lambda kv: kv[1]["w"])
+    w_per_launch = dom["w"] / dom["launches"]
+    avg_ms = dom["ms"] / dom["launches"]
+    ops = valu_ops_per_weight(args.iters) * w_per_launch
+    achieved_tops = ops / (avg_ms * 1e-3) / 1e12
+    hbm_gbs = hbm_bytes_per_weight(nb, gs) * w_per_launch / (avg_ms * 1e-3) / 1e9
+
+    gbs = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
+                   "nbits": nb, "group_size": gs, "axis": ax, "iters": args.iters,
+                   "p": 0.7, "beta0": 10.0, "kappa": 1.01},
+        "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                     "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4),
+                     "traffic": None,
+                     "kernel": f"solve_kernel<{nb},{gs},{ax}>",
+                     "avg_launch_ms": round(avg_ms, 5),
+                     "ops_per_weight": valu_ops_per_weight(args.iters),
+                     "hbm_achieved_GBs": round(hbm_gbs, 2),
+                     "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
+        "context": {"pages_hqq_llama7b_quantize_minutes": 8.2, "hardware": "not stated on the pages"},
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

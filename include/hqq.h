@@ -65,6 +65,10 @@
 extern "C" {
 #endif
 
+#ifndef HQQ_API
+#define HQQ_API __attribute__((visibility("default")))
+#endif
+
 #define HQQ_OK 0
 #define HQQ_EINVAL_NBITS (-1) /* nbits not in {1,2,3,4}                              */
 #define HQQ_EINVAL_AXIS (-2)  /* axis not in {0,1}                                   */
@@ -80,7 +84,7 @@ extern "C" {
  *   packed  uint32, hqq_packed_words(rows, cols, nbits, axis) words, written
  *   scale, zero  fp32, rows*cols/group_size values each, written
  * Returns HQQ_OK or a negative HQQ_E* status. */
-int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols,
+HQQ_API int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols,
                  int nbits, int group_size, int axis,
                  int iters, float p, float beta0, float kappa,
                  uint32_t *packed, float *scale, float *zero, void *stream);
@@ -88,7 +92,7 @@ int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols,
 /* Dequantize: W_hat = fp16_round_half_even((W_q - zero) / scale) with an
  * IEEE fp32 subtraction and division (lnwmold.com HQQ guide section 3.2,
  * HQQLinear.dequantize()).  W_hat is fp16 bits [rows, cols], written. */
-int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero,
+HQQ_API int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero,
                    int64_t rows, int64_t cols, int nbits, int group_size, int axis,
                    uint16_t *W_hat, void *stream);
 
@@ -96,20 +100,20 @@ int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero
  * are used) into the packed layout above (lnwmold.com HQQ guide section 3.2:
  * W_q is stored packed).  group_size is validated as for hqq_quantize but
  * does not change the layout. */
-int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
+HQQ_API int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
              int nbits, int group_size, int axis, uint32_t *packed, void *stream);
 
 /* Unpack to uint8 codes [rows, cols] (lnwmold.com HQQ guide section 3.2,
  * HQQLinear.unpack(dtype=uint8)). */
-int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
+HQQ_API int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
                int nbits, int group_size, int axis, uint8_t *codes, void *stream);
 
 /* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */
-int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
+HQQ_API int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
 
 /* Static description of a status code.  Host only. */
-const char *hqq_strerror(int status);
+HQQ_API const char *hqq_strerror(int status);
 
 #ifdef __cplusplus
 }

@@ -44,8 +44,9 @@
  *   R5 the mean is evaluated through linearity as
  *        (sum W_q - scale * (sum w - sum W_e)) / gs
  *      in fp64: sum W_q (small integers) and sum w (fp16 values) are exact in
- *      any order; sum W_e is accumulated in ascending element order; the
- *      result is rounded once to fp32.
+ *      any order; sum W_e is the pairwise tree over adjacent elements (pairs
+ *      (0,1), (2,3), ..., then pairs of those sums, and so on); the result is
+ *      rounded once to fp32.
  *   R6 the first iteration uses beta0 and beta is multiplied by kappa after
  *      the zero update; exactly iters steps, no early stop; iters = 0 is RTN.
  *   R7 zero is neither rounded nor clamped.
@@ -153,9 +154,11 @@ int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
 
     float *q = (float *)malloc(sizeof(float) * (size_t)gs);
     float *e = (float *)malloc(sizeof(float) * (size_t)gs);
-    if (!q || !e) {
+    double *te = (double *)malloc(sizeof(double) * (size_t)gs);
+    if (!q || !e || !te) {
         free(q);
         free(e);
+        free(te);
         return -2;
     }
 
@@ -175,12 +178,16 @@ int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
                 tr_x[(size_t)it * gs + i] = x;
         }
         /* zero = mean(W_q - (w - W_e) * scale), reading R5 */
-        double sum_q = 0.0, sum_w = 0.0, sum_e = 0.0;
+        double sum_q = 0.0, sum_w = 0.0;
         for (int i = 0; i < gs; ++i) {
             sum_q += (double)q[i];
             sum_w += (double)w[i];
-            sum_e += (double)e[i];
+            te[i] = (double)e[i];
         }
+        for (int st = 1; st < gs; st *= 2)
+            for (int i = 0; i + st < gs; i += 2 * st)
+                te[i] += te[i + st];
+        double sum_e = te[0];
         double num = sum_q - (double)scale * (sum_w - sum_e);
         zero = (float)(num / (double)gs);
 
@@ -201,6 +208,7 @@ int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
     *zero_out = zero;
     free(q);
     free(e);
+    free(te);
     return 0;
 }
 

@@ -1,0 +1,115 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+declared in include/hqq.h, and rejects invalid arguments on the host before
+any HIP call (so no GPU is needed; no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hqq.h")
+LIB = os.path.join(ROOT, "weight_quantization_group_amd", "libhqq.so")
+
+E = dict(OK=0, NBITS=-1, AXIS=-2, GROUP=-3, SHAPE=-4, PTR=-5, PARAM=-6, HIP=-7)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:HQQ_API\s+)?(?:int|int64_t|const char \*)\s*(hqq_\w+)\s*\(",
+                                 text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built (run __graft_entry__.build())")
+    import weight_quantization_group_amd as w
+    return w.load_library()
+
+
+def test_header_codes_match():
+    text = open(HEADER).read()
+    for name, val in E.items():
+        key = "HQQ_OK" if name == "OK" else ("HQQ_EHIP" if name == "HIP" else f"HQQ_EINVAL_{name}")
+        m = re.search(rf"#define {key} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == val, key
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared == sorted(["hqq_quantize", "hqq_dequantize", "hqq_pack", "hqq_unpack",
+                               "hqq_packed_words", "hqq_strerror"])
+    for name in declared:
+        assert hasattr(lib, name), name
+    # and nothing else: the dynamic symbol table holds exactly the C ABI
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared, exported
+
+
+def test_packed_words_matches_layout(lib, oracle_mod):
+    for nbits in (1, 2, 3, 4):
+        for axis in (0, 1):
+            for rows, cols in ((1, 1), (7, 33), (4096, 4096), (11008, 4096), (320, 11008)):
+                assert lib.hqq_packed_words(rows, cols, nbits, axis) == \
+                    oracle_mod.packed_words(rows, cols, nbits, axis)
+    assert lib.hqq_packed_words(4, 4, 5, 1) == E["NBITS"]
+    assert lib.hqq_packed_words(4, 4, 4, 2) == E["AXIS"]
+    assert lib.hqq_packed_words(0, 4, 4, 1) == E["SHAPE"]
+
+
+def test_strerror(lib):
+    for v in E.values():
+        assert len(lib.hqq_strerror(v)) > 0
+    assert lib.hqq_strerror(12345) == b"unknown status"
+
+
+# fake, 16-byte aligned, never dereferenced: every call below fails validation first
+A = ctypes.c_void_p(0x1000)
+MIS = ctypes.c_void_p(0x1002)
+
+
+def _q(lib, **kw):
+    args = dict(W=A, rows=64, cols=128, nbits=4, gs=64, axis=1, iters=20, p=0.7, beta0=10.0,
+                kappa=1.01, packed=A, scale=A, zero=A)
+    args.update(kw)
+    return lib.hqq_quantize(args["W"], args["rows"], args["cols"], args["nbits"], args["gs"],
+                            args["axis"], args["iters"], args["p"], args["beta0"], args["kappa"],
+                            args["packed"], args["scale"], args["zero"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nbits=0), "NBITS"), (dict(nbits=5), "NBITS"), (dict(nbits=8), "NBITS"),
+    (dict(axis=2), "AXIS"), (dict(axis=-1), "AXIS"),
+    (dict(gs=48), "GROUP"), (dict(gs=512), "GROUP"), (dict(gs=4), "GROUP"),
+    (dict(cols=96), "GROUP"), (dict(axis=0, rows=96), "GROUP"),
+    (dict(rows=0), "SHAPE"), (dict(cols=-5), "SHAPE"), (dict(rows=1 << 32), "SHAPE"),
+    (dict(W=None), "PTR"), (dict(packed=None), "PTR"), (dict(scale=MIS), "PTR"), (dict(zero=None), "PTR"),
+    (dict(iters=-1), "PARAM"), (dict(iters=1 << 20), "PARAM"), (dict(p=0.0), "PARAM"),
+    (dict(p=float("nan")), "PARAM"), (dict(beta0=-1.0), "PARAM"), (dict(kappa=0.0), "PARAM"),
+    (dict(kappa=float("inf")), "PARAM"),
+])
+def test_quantize_rejects(lib, kw, code):
+    assert _q(lib, **kw) == E[code]
+
+
+def test_codec_rejects(lib):
+    assert lib.hqq_dequantize(A, A, A, 64, 128, 3, 64, 1, None, None) == E["PTR"]
+    assert lib.hqq_dequantize(A, A, A, 64, 128, 4, 64, 3, A, None) == E["AXIS"]
+    assert lib.hqq_dequantize(A, A, A, 64, 100, 4, 64, 1, A, None) == E["GROUP"]
+    assert lib.hqq_pack(A, 64, 128, 6, 64, 1, A, None) == E["NBITS"]
+    assert lib.hqq_pack(MIS, 64, 128, 4, 64, 1, A, None) == E["PTR"]
+    assert lib.hqq_unpack(A, 0, 128, 4, 64, 1, A, None) == E["SHAPE"]
+    assert lib.hqq_unpack(A, 64, 128, 4, 32, 0, None, None) == E["PTR"]
+
+
+def test_product_does_not_touch_oracle():
+    """The library and its binding never reference the oracle."""
+    pkg = os.path.join(ROOT, "weight_quantization_group_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

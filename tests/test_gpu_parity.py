@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (the method's stated tolerances):
+  pack / unpack / dequantize  bit-exact given the codes
+  codes                       identical on >= 99.99% of elements, the rest within +-1
+  scale, zero                 within 1e-4 relative
+  per-tensor MSE              within 0.1% relative
+The kernel is built to reproduce the oracle's fp32 arithmetic exactly, so the
+tests also report (and for scale, require) exact agreement.
+
+Inputs are seeded synthetic weights (synth/); the oracle always receives the
+very fp16 bits the GPU quantized.
+"""
+import numpy as np
+import pytest
+
+import synth
+from helpers import random_f16, recon_mse
+
+pytestmark = pytest.mark.gpu
+
+QMAX = {1: 1, 2: 3, 3: 7, 4: 15}
+C_OF = {4: 8, 3: 10, 2: 16, 1: 32}
+
+
+@pytest.fixture(scope="module")
+def hq():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import weight_quantization_group_amd as w
+
+    w.load_library()
+    return w
+
+
+def _dev16(W16: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(W16).view(np.int16)).cuda()
+
+
+def _np_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def gpu_quantize(hq, W16, nbits, gs, axis, **kw):
+    import torch
+
+    Wd = _dev16(W16)
+    packed, scale, zero = hq.hqq_quantize(Wd, nbits, gs, axis, **kw)
+    torch.cuda.synchronize()
+    return _np_u32(packed), scale.cpu().numpy(), zero.cpu().numpy()
+
+
+def check_parity(oracle_mod, W16, nbits, gs, axis, g_packed, g_scale, g_zero, o=None, tag="",
+                 **kw):
+    """Compare GPU outputs with the oracle on the same W16; returns stats."""
+    rows, cols = W16.shape
+    if o is None:
+        o = oracle_mod.quantize_codes(W16, nbits, gs, axis, **kw)
+    o_codes, o_scale, o_zero = o
+    g_codes = oracle_mod.unpack(g_packed, rows, cols, nbits, axis)   # decode the GPU words
+    # codes
+    diff = g_codes.astype(np.int16) - o_codes.astype(np.int16)
+    mism = np.count_nonzero(diff)
+    assert np.abs(diff).max(initial=0) <= 1, f"{tag}: code differs by more than 1"
+    assert mism <= 1e-4 * diff.size, f"{tag}: {mism} of {diff.size} codes differ"
+    assert g_codes.max() <= QMAX[nbits]
+    # scale (computed identically: exact), zero (1e-4 relative)
+    assert np.array_equal(g_scale, o_scale), f"{tag}: scale differs"
+    rel = np.abs(g_zero.astype(np.float64) - o_zero) / np.maximum(np.abs(o_zero.astype(np.float64)), 1e-30)
+    bad = (rel > 1e-4) & (np.abs(g_zero - o_zero) > 1e-6)
+    assert not bad.any(), f"{tag}: {bad.sum()} zeros beyond 1e-4 (max rel {rel.max()})"
+    # MSE
+    mg = recon_mse(W16, g_codes, g_scale, g_zero, gs, axis)
+    mo = recon_mse(W16, o_codes, o_scale, o_zero, gs, axis)
+    assert abs(mg - mo) <= 1e-3 * mo + 1e-30, f"{tag}: MSE {mg} vs {mo}"
+    # the packed words must also be exactly the oracle's packing of the GPU codes
+    assert np.array_equal(g_packed, oracle_mod.pack(g_codes, nbits, axis))
+    return dict(code_mismatch=mism, zero_exact=float(np.mean(g_zero == o_zero)), mse=mg)
+
+
+# --------------------------------------------------------------------------
+# pack / unpack / dequantize: bit-exact
+# --------------------------------------------------------------------------
+
+SHAPES = [(8, 8), (16, 24), (40, 96), (96, 40), (64, 320), (320, 64), (56, 1024), (1024, 48), (48, 56)]
+
+
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_pack_unpack_bitexact(hq, oracle_mod, nbits, axis):
+    import torch
+
+    rng = np.random.RandomState(100 + nbits * 2 + axis)
+    for rows, cols in SHAPES:
+        codes = rng.randint(0, QMAX[nbits] + 1, size=(rows, cols)).astype(np.uint8)
+        ref = oracle_mod.pack(codes, nbits, axis)
+        got = _np_u32(hq.hqq_pack(torch.from_numpy(codes).cuda(), nbits, 8, axis))
+        assert np.array_equal(got, ref), (rows, cols)
+        back = hq.hqq_unpack(torch.from_numpy(ref.view(np.int32)).cuda(), rows, cols, nbits, 8, axis)
+        assert np.array_equal(back.cpu().numpy(), codes), (rows, cols)
+
+
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_dequantize_bitexact(hq, oracle_mod, nbits, axis):
+    import torch
+
+    rng = np.random.RandomState(200 + nbits * 2 + axis)
+    for gs, (rows, cols) in ((8, (40, 96)), (16, (64, 320)), (64, (320, 64)), (32, (96, 1024))):
+        codes = rng.randint(0, QMAX[nbits] + 1, size=(rows, cols)).astype(np.uint8)
+        packed = oracle_mod.pack(codes, nbits, axis)
+        ms = oracle_mod.meta_shape(rows, cols, gs, axis)
+        scale = np.exp(rng.uniform(-3, 12, ms)).astype(np.float32)
+        zero = rng.uniform(-20, 35, ms).astype(np.float32)
+        ref = oracle_mod.dequantize(packed, scale, zero, rows, cols, nbits, gs, axis)
+        got = hq.hqq_dequantize(torch.from_numpy(packed.view(np.int32)).cuda(),
+                                torch.from_numpy(scale).cuda(), torch.from_numpy(zero).cuda(),
+                                rows, cols, nbits, gs, axis)
+        assert np.array_equal(got.cpu().numpy().view(np.uint16), ref), (gs, rows, cols)
+
+
+# --------------------------------------------------------------------------
+# quantize: every format, ragged tails, both axes
+# --------------------------------------------------------------------------
+
+def _format_cases():
+    out = []
+    for nbits in (1, 2, 3, 4):
+        for gs in (8, 16, 32, 64, 128, 256):
+            for axis in (0, 1):
+                out.append((nbits, gs, axis))
+    return out
+
+
+@pytest.mark.parametrize("nbits,gs,axis", _format_cases())
+def test_quantize_formats(hq, oracle_mod, nbits, gs, axis):
+    rng = np.random.RandomState(nbits * 1000 + gs * 2 + axis)
+    # several work items per wave plus a ragged last block along the line
+    ngroups = 7 if gs <= 64 else 3
+    if axis == 1:
+        shape = (67, gs * ngroups)
+    else:
+        shape = (gs * ngroups, 67)
+    W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.002)
+    g = gpu_quantize(hq, W16, nbits, gs, axis)
+    check_parity(oracle_mod, W16, nbits, gs, axis, *g, tag=f"{nbits}b g{gs} ax{axis}")
+
+
+@pytest.mark.parametrize("nbits,gs,axis,p,beta0,kappa", [
+    (4, 64, 1, 0.7, 1000.0, 1.01),   # shrink active on most residuals: slow mode everywhere
+    (2, 16, 0, 0.7, 1000.0, 1.01),
+    (3, 64, 0, 0.7, 300.0, 1.05),
+    (1, 16, 1, 0.7, 100.0, 1.01),
+    (4, 64, 1, 1.0, 50.0, 1.01),     # soft thresholding
+    (2, 16, 1, 1.5, 0.1, 1.5),       # drifting zero, clamp engaged
+    (3, 64, 1, 1.0, 0.1, 1.5),
+    (4, 32, 0, 2.5, 10.0, 1.01),     # p > 2: no certificate, every residual evaluated
+    (4, 64, 1, 0.3, 1.0, 1.01),
+])
+def test_quantize_shrink_paths(hq, oracle_mod, nbits, gs, axis, p, beta0, kappa):
+    rng = np.random.RandomState(int(p * 100) + nbits * 7 + gs + axis)
+    shape = (64, gs * 9) if axis == 1 else (gs * 9, 64)
+    W16 = random_f16(rng, shape, std=0.05, outlier_frac=0.01)
+    kw = dict(p=p, beta0=beta0, kappa=kappa)
+    g = gpu_quantize(hq, W16, nbits, gs, axis, **kw)
+    st = check_parity(oracle_mod, W16, nbits, gs, axis, *g, tag=f"p={p} b0={beta0}", **kw)
+    print("shrink path", nbits, gs, axis, p, beta0, st)
+
+
+def test_quantize_edge_values(hq, oracle_mod):
+    rng = np.random.RandomState(7)
+    gs = 64
+    W = (rng.randn(16, gs * 8) * 0.02).astype(np.float16)
+    W[0, :gs] = 0.0                                  # all-zero group
+    W[1, :gs] = np.float16(0.3)                      # constant group
+    W[2, :gs] = np.float16(-7.25)
+    W[3, :gs] = np.float16(6e-8) * rng.randint(-3, 4, gs)      # subnormals only
+    W[4, :gs] = np.where(rng.rand(gs) < 0.5, 65504.0, -65504.0)  # extremes
+    W[5, :gs] = np.float16(60000.0) + rng.randint(0, 64, gs).astype(np.float16)  # huge, tiny range
+    W[6, :gs] = rng.randn(gs).astype(np.float16) * np.float16(1000.0)
+    W[7, :2 * gs] = np.float16(1e-3) * rng.randint(0, 16, 2 * gs)  # grid values
+    W16 = W.view(np.uint16)
+    for iters in (0, 1, 20):
+        for nbits in (1, 2, 3, 4):
+            g = gpu_quantize(hq, W16, nbits, gs, 1, iters=iters)
+            check_parity(oracle_mod, W16, nbits, gs, 1, *g, iters=iters, tag=f"edge it={iters}")
+            WT = np.ascontiguousarray(W16.T)
+            g = gpu_quantize(hq, WT, nbits, gs, 0, iters=iters)
+            check_parity(oracle_mod, WT, nbits, gs, 0, *g, iters=iters, tag=f"edgeT it={iters}")
+
+
+def test_single_linear_workload_full(hq, oracle_mod):
+    """The 4096 x 1024 single-Linear workload (4-bit, g64, axis 1), every element."""
+    t = synth.workload("linear_4096x1024_4b_g64")[0]
+    W16 = synth.generate_np(t["seed"], t["layer"], t["tensor_id"], t["rows"], t["cols"])
+    g = gpu_quantize(hq, W16, 4, 64, 1)
+    st = check_parity(oracle_mod, W16, 4, 64, 1, *g, tag="single linear")
+    assert st["code_mismatch"] == 0 and st["zero_exact"] == 1.0
+    print("single linear", st)
+
+
+def test_determinism_and_streams(hq):
+    import torch
+
+    rng = np.random.RandomState(9)
+    W16 = random_f16(rng, (512, 2048), outlier_frac=0.001)
+    a = gpu_quantize(hq, W16, 3, 64, 0)
+    b = gpu_quantize(hq, W16, 3, 64, 0)
+    s = torch.cuda.Stream()
+    Wd = _dev16(W16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = hq.hqq_quantize(Wd, 3, 64, 0)
+    s.synchronize()
+    for x, y, z in zip(a, b, (_np_u32(c[0]), c[1].cpu().numpy(), c[2].cpu().numpy())):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(x.view(np.uint32), z.view(np.uint32))
+
+
+def test_binding_raises(hq):
+    import torch
+
+    W = torch.zeros((64, 100), dtype=torch.float16, device="cuda")
+    with pytest.raises(hq.HQQError):
+        hq.hqq_quantize(W, 4, 64, 1)
+    with pytest.raises(TypeError):
+        hq.hqq_quantize(W.cpu(), 4, 64, 1)
+
+
+def test_synth_gpu_generator_matches_numpy():
+    import torch
+
+    for seed, layer, tid, rows, cols in ((synth.SEED_7B, 3, 4, 11008, 4096),
+                                         (synth.SEED_70B, 79, 6, 8192, 28672)):
+        out = torch.empty((16, cols), dtype=torch.float16, device="cuda")
+        synth.generate_gpu(out, seed, layer, tid, row0=rows - 16)
+        torch.cuda.synchronize()
+        g = out.cpu().numpy().view(np.uint16)
+        c = synth.generate_np(seed, layer, tid, rows, cols, row0=rows - 16, nrows=16)
+        same = np.mean(g == c)
+        d = np.abs(g.astype(np.int32) - c.astype(np.int32))
+        assert same > 0.9999 and d.max() <= 1, (same, d.max())
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, in the benchmark's launch configuration, sampled
+# --------------------------------------------------------------------------
+
+def _sampled_parity(hq, oracle_mod, t, nsample, seed_extra=0):
+    import torch
+
+    rows, cols, nb, gs, axis = t["rows"], t["cols"], t["nbits"], t["group_size"], t["axis"]
+    W = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
+    synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+    packed, scale, zero = hq.hqq_quantize(W, nb, gs, axis)
+    torch.cuda.synchronize()
+    rng = np.random.RandomState((t["tensor_id"] * 131 + t["layer"] * 7 + seed_extra) & 0xFFFF)
+    if axis == 1:
+        idx = np.sort(rng.choice(rows, nsample, replace=False))
+        it = torch.from_numpy(idx).cuda()
+        W16 = W.index_select(0, it).cpu().numpy().view(np.uint16)
+        gp = _np_u32(packed.index_select(0, it))
+        gsc = scale.index_select(0, it).cpu().numpy()
+        gz = zero.index_select(0, it).cpu().numpy()
+    else:
+        idx = np.sort(rng.choice(cols, nsample, replace=False))
+        it = torch.from_numpy(idx).cuda()
+        W16 = np.ascontiguousarray(W.index_select(1, it).cpu().numpy().view(np.uint16))
+        gp = np.ascontiguousarray(_np_u32(packed.index_select(1, it)))
+        gsc = np.ascontiguousarray(scale.index_select(1, it).cpu().numpy())
+        gz = np.ascontiguousarray(zero.index_select(1, it).cpu().numpy())
+    del W, packed, scale, zero
+    st = check_parity(oracle_mod, W16, nb, gs, axis, gp, gsc, gz,
+                      tag=f"L{t['layer']} {t['name']} {nb}b g{gs} ax{axis}")
+    return st
+
+
+@pytest.mark.parametrize("wl", ["llama7b_layer_4b_g64", "llama7b_layer_3b2b_axis0"])
+def test_7b_layer_sampled(hq, oracle_mod, wl):
+    for t in synth.workload(wl):
+        n = 48 if t["axis"] == 1 else 24
+        st = _sampled_parity(hq, oracle_mod, t, n)
+        print(wl, t["name"], st)
+
+
+def test_7b_stack_last_layer_sampled(hq, oracle_mod):
+    for t in synth.workload("llama7b_stack32_4b_g64"):
+        if t["layer"] in (17, 31):
+            _sampled_parity(hq, oracle_mod, t, 24)
+
+
+def test_70b_stack_sampled(hq, oracle_mod):
+    for t in synth.workload("llama70b_stack80_mixed"):
+        if t["layer"] in (0, 79):
+            st = _sampled_parity(hq, oracle_mod, t, 16 if t["name"] in ("gate", "up") else 32)
+            print("70b", t["layer"], t["name"], st)

@@ -14,7 +14,8 @@ MUTATIONS = [
     ("W_r multiplies by scale", "float wr = (q[i] - zero) / scale;", "float wr = (q[i] - zero) * scale;"),
     ("residual sign", "float x = w[i] - wr;", "float x = wr - w[i];"),
     ("W_e added instead of subtracted", "(sum_w - sum_e)", "(sum_w + sum_e)"),
-    ("W_e dropped from the mean", "sum_e += (double)e[i];", "(void)0;"),
+    ("W_e dropped from the mean", "te[i] = (double)e[i];", "te[i] = 0.0;"),
+    ("tree sum skips its last level", "for (int st = 1; st < gs; st *= 2)", "for (int st = 1; st < gs / 2; st *= 2)"),
     ("mean over gs-1", "zero = (float)(num / (double)gs);", "zero = (float)(num / (double)(gs - 1));"),
     ("exponent p instead of p-1", "float pm1 = p - 1.0f;", "float pm1 = p;"),
     ("beta divides", "float v = a - pw / beta;", "float v = a - pw * beta;"),

@@ -1,0 +1,168 @@
+"""Python binding of the MI355X HQQ library (``libhqq.so``, C ABI in include/hqq.h).
+
+Argument marshalling only: every step of quantize / dequantize / pack / unpack
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current stream.  There is no fallback: if the library is not built, or a
+tensor is not on the GPU, the call raises.
+
+Tensor conventions (all CUDA tensors, contiguous):
+    W        fp16 (or int16/uint16 holding fp16 bits) [rows, cols]
+    packed   int32 (bit pattern of the uint32 words), shape
+             [rows, ceil(cols/C)] for axis=1, [ceil(rows/C), cols] for axis=0
+    scale    float32, [rows, cols/gs] (axis=1) or [rows/gs, cols] (axis=0)
+    zero     float32, same shape as scale
+    codes    uint8 [rows, cols]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhqq.so")
+
+CODES_PER_WORD = {4: 8, 3: 10, 2: 16, 1: 32}
+P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
+
+# exported symbols, in include/hqq.h order
+EXPORTS = ("hqq_quantize", "hqq_dequantize", "hqq_pack", "hqq_unpack",
+           "hqq_packed_words", "hqq_strerror")
+
+_lib = None
+
+
+class HQQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {hqq_strerror(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libhqq.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m weight_quantization_group_amd.build`")
+    L = ctypes.CDLL(path)
+    P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.hqq_quantize.argtypes = [P, i64, i64, i32, i32, i32, i32, f32, f32, f32, P, P, P, P]
+    L.hqq_quantize.restype = i32
+    L.hqq_dequantize.argtypes = [P, P, P, i64, i64, i32, i32, i32, P, P]
+    L.hqq_dequantize.restype = i32
+    L.hqq_pack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
+    L.hqq_pack.restype = i32
+    L.hqq_unpack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
+    L.hqq_unpack.restype = i32
+    L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
+    L.hqq_packed_words.restype = i64
+    L.hqq_strerror.argtypes = [i32]
+    L.hqq_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def hqq_strerror(status: int) -> str:
+    return load_library().hqq_strerror(int(status)).decode()
+
+
+def hqq_packed_words(rows: int, cols: int, nbits: int, axis: int) -> int:
+    n = load_library().hqq_packed_words(rows, cols, nbits, axis)
+    if n < 0:
+        raise HQQError("hqq_packed_words", n)
+    return int(n)
+
+
+def packed_shape(rows, cols, nbits, axis):
+    C = CODES_PER_WORD[nbits]
+    return (rows, -(-cols // C)) if axis == 1 else (-(-rows // C), cols)
+
+
+def meta_shape(rows, cols, group_size, axis):
+    return (rows, cols // group_size) if axis == 1 else (rows // group_size, cols)
+
+
+def _dev_ptr(t: torch.Tensor, name: str, dtypes) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_F16 = (torch.float16, torch.int16)
+try:
+    _F16 = _F16 + (torch.uint16,)
+except AttributeError:  # pragma: no cover
+    pass
+_U32 = (torch.int32,) + ((torch.uint32,) if hasattr(torch, "uint32") else ())
+
+
+def hqq_quantize(W: torch.Tensor, nbits: int, group_size: int, axis: int,
+                 iters: int = ITERS_DEFAULT, p: float = P_DEFAULT, beta0: float = BETA0_DEFAULT,
+                 kappa: float = KAPPA_DEFAULT, packed=None, scale=None, zero=None):
+    """HQQ-quantize W [rows, cols] (fp16).  Returns (packed, scale, zero)."""
+    L = load_library()
+    rows, cols = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_shape(rows, cols, nbits, axis), dtype=torch.int32, device=dev)
+    line = cols if axis == 1 else rows
+    ms = meta_shape(rows, cols, group_size, axis) if group_size > 0 and line % group_size == 0 else (1,)
+    if scale is None:
+        scale = torch.empty(ms, dtype=torch.float32, device=dev)
+    if zero is None:
+        zero = torch.empty(ms, dtype=torch.float32, device=dev)
+    st = L.hqq_quantize(_dev_ptr(W, "W", _F16), rows, cols, nbits, group_size, axis, iters,
+                        p, beta0, kappa, _dev_ptr(packed, "packed", _U32),
+                        _dev_ptr(scale, "scale", (torch.float32,)),
+                        _dev_ptr(zero, "zero", (torch.float32,)), _stream(dev))
+    if st != 0:
+        raise HQQError("hqq_quantize", st)
+    return packed, scale, zero
+
+
+def hqq_dequantize(packed, scale, zero, rows: int, cols: int, nbits: int, group_size: int,
+                   axis: int, out=None) -> torch.Tensor:
+    """W_hat = fp16((W_q - zero) / scale) as an fp16 tensor [rows, cols]."""
+    L = load_library()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
+    st = L.hqq_dequantize(_dev_ptr(packed, "packed", _U32), _dev_ptr(scale, "scale", (torch.float32,)),
+                          _dev_ptr(zero, "zero", (torch.float32,)), rows, cols, nbits, group_size,
+                          axis, _dev_ptr(out, "out", _F16), _stream(packed.device))
+    if st != 0:
+        raise HQQError("hqq_dequantize", st)
+    return out
+
+
+def hqq_pack(codes: torch.Tensor, nbits: int, group_size: int, axis: int, out=None) -> torch.Tensor:
+    L = load_library()
+    rows, cols = codes.shape
+    if out is None:
+        out = torch.empty(packed_shape(rows, cols, nbits, axis), dtype=torch.int32, device=codes.device)
+    st = L.hqq_pack(_dev_ptr(codes, "codes", (torch.uint8,)), rows, cols, nbits, group_size, axis,
+                    _dev_ptr(out, "out", _U32), _stream(codes.device))
+    if st != 0:
+        raise HQQError("hqq_pack", st)
+    return out
+
+
+def hqq_unpack(packed: torch.Tensor, rows: int, cols: int, nbits: int, group_size: int, axis: int,
+               out=None) -> torch.Tensor:
+    L = load_library()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=packed.device)
+    st = L.hqq_unpack(_dev_ptr(packed, "packed", _U32), rows, cols, nbits, group_size, axis,
+                      _dev_ptr(out, "out", (torch.uint8,)), _stream(packed.device))
+    if st != 0:
+        raise HQQError("hqq_unpack", st)
+    return out

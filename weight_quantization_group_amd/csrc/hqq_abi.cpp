@@ -1,0 +1,191 @@
+// hqq_abi.cpp -- the C ABI of include/hqq.h: argument validation on the host,
+// the shrink certificate, and the kernel launches.  No allocation, no state.
+#include "hqq.h"
+#include "hqq_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kMaxIters = 1 << 16;
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_common(int64_t rows, int64_t cols, int nbits, int group_size, int axis)
+{
+    if (nbits < 1 || nbits > 4)
+        return HQQ_EINVAL_NBITS;
+    if (axis != 0 && axis != 1)
+        return HQQ_EINVAL_AXIS;
+    if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems)
+        return HQQ_EINVAL_SHAPE;
+    switch (group_size) {
+    case 8: case 16: case 32: case 64: case 128: case 256: break;
+    default: return HQQ_EINVAL_GROUP;
+    }
+    const int64_t line = axis == 1 ? cols : rows;
+    if (line % group_size != 0)
+        return HQQ_EINVAL_GROUP;
+    return HQQ_OK;
+}
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+bool finite_pos(float v) { return isfinite(v) && v > 0.0f; }
+
+// Threshold below which the lp shrinkage is provably inactive in every
+// iteration.  The shrink is nonzero iff |x|^(1-pm1) > 1/beta_k, i.e.
+// |x| > tau_k = beta_k^(-1/(1-pm1)) when 1 - pm1 > 0; beta_k is the fp32
+// sequence beta0 * kappa * ... * kappa exactly as the kernel forms it.  The
+// returned thr is 2% below min_k tau_k; 0 disables the certificate (p - 1
+// close to or above 1, where no such threshold exists).
+void certificate(int iters, float pm1, float beta0, float kappa, float *thr, float *thr_m)
+{
+    *thr = 0.0f;
+    *thr_m = 0.0f;
+    const double ex = 1.0 - (double)pm1;
+    if (iters == 0 || !(ex > 0.01))
+        return;
+    double tau_min = INFINITY;
+    float b = beta0;
+    for (int k = 0; k < iters; ++k) {
+        const double tau = pow((double)b, -1.0 / ex);
+        if (tau < tau_min)
+            tau_min = tau;
+        b = b * kappa;
+    }
+    const double t = 0.98 * tau_min;
+    float f = (float)t;
+    if ((double)f > t)
+        f = nextafterf(f, 0.0f);
+    if (!(f > 0.0f))
+        return;
+    *thr = f;
+    *thr_m = f * 2048.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis)
+{
+    if (nbits < 1 || nbits > 4)
+        return HQQ_EINVAL_NBITS;
+    if (axis != 0 && axis != 1)
+        return HQQ_EINVAL_AXIS;
+    if (rows < 1 || cols < 1 || rows > kMaxDim || cols > kMaxDim || rows * cols > kMaxElems)
+        return HQQ_EINVAL_SHAPE;
+    const int64_t C = hqq::codes_per_word(nbits);
+    return axis == 1 ? rows * ((cols + C - 1) / C) : ((rows + C - 1) / C) * cols;
+}
+
+const char *hqq_strerror(int status)
+{
+    switch (status) {
+    case HQQ_OK: return "ok";
+    case HQQ_EINVAL_NBITS: return "nbits must be 1, 2, 3 or 4";
+    case HQQ_EINVAL_AXIS: return "axis must be 0 or 1";
+    case HQQ_EINVAL_GROUP: return "group_size must be 8, 16, 32, 64, 128 or 256 and divide the line length";
+    case HQQ_EINVAL_SHAPE: return "rows and cols must be >= 1 (and rows, cols <= 2^31, rows*cols <= 2^40)";
+    case HQQ_EINVAL_PTR: return "a pointer is NULL or not 16-byte aligned";
+    case HQQ_EINVAL_PARAM: return "iters must be in [0, 65536] and p, beta0, kappa finite and > 0";
+    case HQQ_EHIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int group_size,
+                 int axis, int iters, float p, float beta0, float kappa, uint32_t *packed,
+                 float *scale, float *zero, void *stream)
+{
+    int st = check_common(rows, cols, nbits, group_size, axis);
+    if (st)
+        return st;
+    if (!aligned16(W) || !aligned16(packed) || !aligned16(scale) || !aligned16(zero))
+        return HQQ_EINVAL_PTR;
+    if (iters < 0 || iters > kMaxIters || !finite_pos(p) || !finite_pos(beta0) || !finite_pos(kappa))
+        return HQQ_EINVAL_PARAM;
+
+    hqq::SolveArgs a{};
+    a.W = W;
+    a.packed = packed;
+    a.scale = scale;
+    a.zero = zero;
+    a.rows = rows;
+    a.cols = cols;
+    a.iters = iters;
+    a.pm1 = p - 1.0f;
+    a.beta0 = beta0;
+    a.kappa = kappa;
+    certificate(iters, a.pm1, beta0, kappa, &a.thr, &a.thr_m);
+    const int C = hqq::codes_per_word(nbits);
+    const int64_t lb = hqq::lcm_c(group_size, C);
+    const int64_t L = axis == 1 ? cols : rows;
+    a.nblk = (L + lb - 1) / lb;
+    a.n_items = a.nblk * (axis == 1 ? rows : cols);
+    const hipError_t e = hqq::launch_solve(nbits, group_size, axis, a, (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
+int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero, int64_t rows,
+                   int64_t cols, int nbits, int group_size, int axis, uint16_t *W_hat, void *stream)
+{
+    int st = check_common(rows, cols, nbits, group_size, axis);
+    if (st)
+        return st;
+    if (!aligned16(packed) || !aligned16(scale) || !aligned16(zero) || !aligned16(W_hat))
+        return HQQ_EINVAL_PTR;
+    hqq::CodecArgs a{};
+    a.packed_in = packed;
+    a.scale = scale;
+    a.zero = zero;
+    a.W_hat = W_hat;
+    a.rows = rows;
+    a.cols = cols;
+    a.group_size = group_size;
+    a.n_words = hqq_packed_words(rows, cols, nbits, axis);
+    const hipError_t e = hqq::launch_dequantize(nbits, axis, a, (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
+int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+             uint32_t *packed, void *stream)
+{
+    int st = check_common(rows, cols, nbits, group_size, axis);
+    if (st)
+        return st;
+    if (!aligned16(codes) || !aligned16(packed))
+        return HQQ_EINVAL_PTR;
+    hqq::CodecArgs a{};
+    a.codes_in = codes;
+    a.packed_out = packed;
+    a.rows = rows;
+    a.cols = cols;
+    a.group_size = group_size;
+    a.n_words = hqq_packed_words(rows, cols, nbits, axis);
+    const hipError_t e = hqq::launch_pack(nbits, axis, a, (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
+int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols, int nbits, int group_size,
+               int axis, uint8_t *codes, void *stream)
+{
+    int st = check_common(rows, cols, nbits, group_size, axis);
+    if (st)
+        return st;
+    if (!aligned16(packed) || !aligned16(codes))
+        return HQQ_EINVAL_PTR;
+    hqq::CodecArgs a{};
+    a.packed_in = packed;
+    a.codes_out = codes;
+    a.rows = rows;
+    a.cols = cols;
+    a.group_size = group_size;
+    a.n_words = hqq_packed_words(rows, cols, nbits, axis);
+    const hipError_t e = hqq::launch_unpack(nbits, axis, a, (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// hqq_internal.h -- declarations shared by the library's own translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hqq {
+
+constexpr int codes_per_word(int nb) { return nb == 4 ? 8 : nb == 3 ? 10 : nb == 2 ? 16 : 32; }
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+// Arguments of the solve kernels (passed by value as the kernel argument).
+struct SolveArgs {
+    const uint16_t *W;   // fp16 bits [rows, cols]
+    uint32_t *packed;    // packed codes
+    float *scale;        // per-group scale
+    float *zero;         // per-group zero
+    int64_t rows, cols;
+    int64_t n_items;     // work items (lanes): one block of lcm(gs, C) elements of one line
+    int64_t nblk;        // blocks per line
+    int iters;
+    float pm1;           // p - 1 (fp32)
+    float beta0, kappa;
+    // Shrink certificate: W_e is provably 0 for every residual |x| <= thr in
+    // every iteration (thr = 0: no certificate).  thr_m bounds the group
+    // magnitude for which the cheap residual estimate |t - q| / scale is
+    // accurate enough to use it.
+    float thr, thr_m;
+};
+
+struct CodecArgs {
+    const uint32_t *packed_in;
+    uint32_t *packed_out;
+    const uint8_t *codes_in;
+    uint8_t *codes_out;
+    const float *scale;
+    const float *zero;
+    uint16_t *W_hat;
+    int64_t rows, cols;
+    int group_size;
+    int64_t n_words;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_solve(int nbits, int group_size, int axis, const SolveArgs &a, hipStream_t s);
+hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
+hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
+hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
+
+}  // namespace hqq

@@ -1,0 +1,493 @@
+// hqq_solve_impl.h -- the HQQ solve kernels for gfx950 (included by the
+// per-bit-width translation units hqq_solve_b{1,2,3,4}.hip).
+//
+// Method (lnwmold.com HQQ guide, section 2.1: calibration-free half-quadratic
+// splitting into alternating sub-problems; devpress.csdn.net "dropbox/hqq"
+// tutorial, section 2: auxiliary error variable, robust non-convex loss;
+// section 2.2 of the guide and section 3.3 of the tutorial: nbits,
+// group_size, axis).  Per group of gs weights w, qmax = 2^b - 1:
+//   scale = qmax / (max - min), zero = -(min * scale)
+//   iters times: W_q = clamp(rne(w*scale + zero), 0, qmax)
+//                W_e = shrink_p(w - (W_q - zero)/scale, beta)
+//                zero = (sum W_q - scale * (sum w - sum W_e)) / gs
+//                beta *= kappa
+//   codes = clamp(rne(w*scale + zero), 0, qmax)
+//
+// Mapping to CDNA4.  The solve is elementwise work plus per-group sums: no
+// dense contraction, so no MFMA.  One lane owns a whole group: its gs weights
+// are loaded from HBM once, widened exactly to fp32 and stay in VGPRs for all
+// iterations; min, max and the sums are in-lane, so the 64 lanes of a wave
+// run 64 independent groups with no cross-lane traffic.  Where C (codes per
+// uint32) and gs do not divide each other (3-bit, or gs < C) a lane owns
+// lcm(gs, C) consecutive elements of a line (several groups, solved one after
+// the other), so every packed word is assembled in-register by one lane and
+// written once.  axis = 1: lanes take consecutive blocks of a row; axis = 0:
+// lanes take consecutive columns, so each load and store instruction of a
+// wave touches 64 consecutive columns (coalesced).
+//
+// Exactness.  The arithmetic is the fp32 evaluation with w*scale+zero as one
+// fma and the mean in fp64: sum W_q (small integers) and sum w (fp16 values)
+// are exact in fp64 in any order; sum W_e is the pairwise tree over adjacent
+// elements.  W_e = 0 exactly when |x| <= tau_k = beta_k^(-1/(1-(p-1))); the
+// host passes thr <= 0.98 * min_k tau_k.  |x_i| * scale is within a tiny,
+// bounded error of |t_i - q_i|, t_i = w_i*scale + zero, and
+// max_i |t_i - q_i| <= max(0.5, -t(min w), t(max w) - qmax) because the fma
+// is monotone in w.
+//   fast loop:  while that bound is below thr*scale (and the group's
+//               magnitude keeps the estimate's error far below the 2% margin)
+//               every W_e of the group is 0 and the update is
+//               (sum W_q - scale * sum w) / gs: 4 VALU ops per weight.
+//   freeze:     a group that fails the test stops in its lane (the lane idles
+//               while the wave's other groups finish their iterations).
+//   finish:     the wave then completes its frozen groups together, one lane
+//               per element (64/gs groups at a time): every residual the
+//               estimate cannot clear is evaluated exactly (IEEE division,
+//               |x|^(p-1) in fp64 rounded once to fp32) and the sums are
+//               butterflies across the group's lanes -- for sum W_e exactly
+//               the pairwise tree.  Rare, outlier-heavy groups therefore cost
+//               a short SIMD phase instead of a long serial tail.
+#pragma once
+#include "hqq_internal.h"
+
+namespace hqq {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;   // threads per workgroup of the solve kernels
+constexpr int kWaves = kBlock / 64;
+
+// Load one group (gs fp16 values) and widen exactly to fp32.
+template <int GS, int AXIS>
+__device__ __forceinline__ void load_group(const uint16_t *__restrict__ W, int64_t cols,
+                                           int64_t line, int64_t e0, float (&w)[GS])
+{
+    if constexpr (AXIS == 1) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(W + line * cols + e0);
+#pragma unroll
+        for (int j = 0; j < GS / 8; ++j) {
+            u32x4 v = __builtin_nontemporal_load(src + j);
+            _Float16 h[8];
+            __builtin_memcpy(h, &v, 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[j * 8 + i] = (float)h[i];
+        }
+    } else {
+        const uint16_t *src = W + e0 * cols + line;
+#pragma unroll
+        for (int i = 0; i < GS; ++i) {
+            uint16_t b = __builtin_nontemporal_load(src + (int64_t)i * cols);
+            _Float16 h;
+            __builtin_memcpy(&h, &b, 2);
+            w[i] = (float)h;
+        }
+    }
+}
+
+__device__ __forceinline__ float quant(float w, float s, float z, float qmax)
+{
+    return __builtin_amdgcn_fmed3f(__builtin_rintf(__builtin_fmaf(w, s, z)), 0.0f, qmax);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b)
+{
+    _Float16 h;
+    __builtin_memcpy(&h, &b, 2);
+    return (float)h;
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f)   // exact for fp16 values
+{
+    const _Float16 h = (_Float16)f;
+    uint16_t b;
+    __builtin_memcpy(&b, &h, 2);
+    return b;
+}
+
+// Exact sum of the group's weights: fp16 values are multiples of 2^-24 below
+// 2^16, so any partial sum of <= 256 of them is an integer multiple of 2^-24
+// below 2^24, exactly representable in fp64.
+template <int GS>
+__device__ __forceinline__ double exact_sum(const float (&w)[GS])
+{
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < GS; ++i)
+        acc[i & 3] += (double)w[i];
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// |x|^(p-1) evaluated in fp64 and rounded once to fp32 (x > 0 finite).
+// exp((p-1) ln x): ln x = k ln2 + 2 atanh(u), u = (m-1)/(m+1) for the
+// significand m in [sqrt(1/2), sqrt(2)) (the atanh power series to u^21);
+// exp by reduction y = j ln2 + r, |r| <= ln2/2, and its Taylor polynomial to
+// r^13.  Relative error ~1e-15, far below the fp32 rounding it feeds.
+__device__ __forceinline__ float pow_rounded(float xf, float pm1f)
+{
+    int e;
+    double m = frexp((double)xf, &e);
+    if (m < 0.70710678118654752440) {
+        m *= 2.0;
+        e -= 1;
+    }
+    const double f = m - 1.0;
+    const double u = f / (2.0 + f);
+    const double u2 = u * u;
+    double p = 1.0 / 21;
+    p = __builtin_fma(p, u2, 1.0 / 19);
+    p = __builtin_fma(p, u2, 1.0 / 17);
+    p = __builtin_fma(p, u2, 1.0 / 15);
+    p = __builtin_fma(p, u2, 1.0 / 13);
+    p = __builtin_fma(p, u2, 1.0 / 11);
+    p = __builtin_fma(p, u2, 1.0 / 9);
+    p = __builtin_fma(p, u2, 1.0 / 7);
+    p = __builtin_fma(p, u2, 1.0 / 5);
+    p = __builtin_fma(p, u2, 1.0 / 3);
+    const double lnm = __builtin_fma(2.0 * u, u2 * p, 2.0 * u);
+    const double lnx = __builtin_fma((double)e, 0.69314718055994530942, lnm);
+    double y = (double)pm1f * lnx;
+    y = fmin(fmax(y, -800.0), 800.0);
+    const double j = rint(y * 1.44269504088896340736);
+    double r = __builtin_fma(-j, 0.69314718055994530942, y);
+    r = __builtin_fma(-j, 2.319046813846299558e-17, r);
+    double q = 1.0 / 6227020800.0;
+    q = __builtin_fma(q, r, 1.0 / 479001600.0);
+    q = __builtin_fma(q, r, 1.0 / 39916800.0);
+    q = __builtin_fma(q, r, 1.0 / 3628800.0);
+    q = __builtin_fma(q, r, 1.0 / 362880.0);
+    q = __builtin_fma(q, r, 1.0 / 40320.0);
+    q = __builtin_fma(q, r, 1.0 / 5040.0);
+    q = __builtin_fma(q, r, 1.0 / 720.0);
+    q = __builtin_fma(q, r, 1.0 / 120.0);
+    q = __builtin_fma(q, r, 1.0 / 24.0);
+    q = __builtin_fma(q, r, 1.0 / 6.0);
+    q = __builtin_fma(q, r, 0.5);
+    q = __builtin_fma(q, r, 1.0);
+    q = __builtin_fma(q, r, 1.0);
+    return (float)ldexp(q, (int)j);
+}
+
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Layout of the finish phase: a frozen group is spread over SEG lanes with EPL
+// consecutive elements each; B groups are finished at once.
+template <int GS>
+struct Finish {
+    static constexpr int SEG = GS < 64 ? GS : 64;
+    static constexpr int EPL = GS / SEG;
+    static constexpr int B = 64 / SEG;
+};
+
+struct FrozenGroup {   // state of a frozen group handed to the finish phase
+    float s, z, beta, mn, mx, amag;
+    int it;
+    int pad;
+    double sw;
+};
+
+template <int GS>
+struct WaveFinish {
+    uint16_t w[64 * Finish<GS>::EPL];    // B groups x GS fp16 weights
+    FrozenGroup g[Finish<GS>::B];
+};
+
+// Pack a group's final codes (small integers held in fp32) into the work item's words.
+template <int NB, int GS, int G, int WPB>
+__device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float z,
+                                           uint32_t (&words)[WPB])
+{
+    constexpr int C = codes_per_word(NB);
+    constexpr float QMAX = (float)((1 << NB) - 1);
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+        const int n = G * GS + i;
+        words[n / C] |= (uint32_t)quant(w[i], s, z, QMAX) << ((n % C) * NB);
+    }
+}
+
+// Finish the frozen groups of the wave (every lane of the wave takes part).
+// frozen: this lane's group is frozen; on return its z is the final zero.
+template <int NB, int GS>
+__device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS> &wf, bool frozen,
+                                              const float (&w)[GS], float s, float &z, float beta,
+                                              float mn, float mx, float amag, int it_f, double sw)
+{
+    using F = Finish<GS>;
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    constexpr double INV_GS = 1.0 / GS;
+    const uint32_t lane = __lane_id();
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint64_t pending = __ballot(frozen);
+    while (pending) {
+        // the next (up to) B frozen groups, in lane order
+        uint64_t take = 0;
+#pragma unroll
+        for (int b = 0; b < F::B; ++b) {
+            if (pending & ~take)
+                take |= (pending & ~take) & (~(pending & ~take) + 1ull);
+        }
+        pending &= ~take;
+        const int nb = __popcll(take);
+        const bool mine = (take >> lane) & 1ull;
+        if (mine) {
+            const int slot = __popcll(take & below);
+#pragma unroll
+            for (int i = 0; i < GS; ++i)
+                wf.w[slot * GS + i] = float_to_half_bits(w[i]);
+            wf.g[slot] = FrozenGroup{s, z, beta, mn, mx, amag, it_f, 0, sw};
+        }
+        wave_sync();
+
+        // one lane per element (EPL consecutive elements per lane)
+        const int slot = (int)lane / F::SEG;
+        const int pos = (int)lane % F::SEG;
+        const bool ok = slot < nb;
+        const FrozenGroup st = wf.g[ok ? slot : 0];
+        float we[F::EPL];
+#pragma unroll
+        for (int k = 0; k < F::EPL; ++k)
+            we[k] = half_bits_to_float(wf.w[(ok ? slot : 0) * GS + pos * F::EPL + k]);
+        const float gs_s = st.s;
+        const float thr_s = a.thr * gs_s;
+        const float lim = a.thr_m * gs_s;
+        float gz = st.z, gbeta = st.beta;
+        int it = ok ? st.it : a.iters;
+        while (__any(it < a.iters)) {
+            const bool act = it < a.iters;
+            // certificate of the group for the current zero
+            const float tmin = __builtin_fmaf(st.mn, gs_s, gz);
+            const float tmax = __builtin_fmaf(st.mx, gs_s, gz);
+            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+            const bool est_ok = __builtin_fmaf(st.amag, gs_s, fabsf(gz)) + QMAX <= lim;
+            const bool cand = !(est_ok && bound <= thr_s);
+            float sq = 0.0f;
+            double te[F::EPL];
+#pragma unroll
+            for (int k = 0; k < F::EPL; ++k) {
+                const float t = __builtin_fmaf(we[k], gs_s, gz);
+                const float qk = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, QMAX);
+                sq += qk;
+                float e = 0.0f;
+                if (act && cand && !(est_ok && fabsf(t - qk) <= thr_s)) {
+                    const float wr = (qk - gz) / gs_s;
+                    const float x = we[k] - wr;
+                    const float ax = fabsf(x);
+                    if (ax > a.thr) {
+                        const float pw = pow_rounded(ax, a.pm1);
+                        const float v = ax - pw / gbeta;
+                        if (v > 0.0f)
+                            e = copysignf(v, x);
+                    }
+                }
+                te[k] = (double)e;
+            }
+            // sum W_e: in-lane levels of the pairwise tree, then the butterfly
+            // across the group's lanes (each level adds the sibling block)
+#pragma unroll
+            for (int st2 = 1; st2 < F::EPL; st2 *= 2)
+#pragma unroll
+                for (int k = 0; k + st2 < F::EPL; k += 2 * st2)
+                    te[k] += te[k + st2];
+            double se = te[0];
+#pragma unroll
+            for (int m = 1; m < F::SEG; m *= 2) {
+                sq += __shfl_xor(sq, m);
+                se += __shfl_xor(se, m);
+            }
+            const float zn = (float)(((double)sq - (double)gs_s * (st.sw - se)) * INV_GS);
+            if (act) {
+                gz = zn;
+                gbeta = gbeta * a.kappa;
+                ++it;
+            }
+        }
+        if (ok && pos == 0)
+            wf.g[slot].z = gz;
+        wave_sync();
+        if (mine)
+            z = wf.g[__popcll(take & below)].z;
+        wave_sync();
+    }
+}
+
+// Occupancy target per group size: the resident group (gs fp32 VGPRs) plus
+// the loop state must fit without spills.
+constexpr int waves_per_simd(int gs) { return gs <= 8 ? 8 : gs == 16 ? 6 : gs == 32 ? 6 : gs == 64 ? 4 : gs == 128 ? 2 : 1; }
+
+template <int NB, int GS, int G, int AXIS, int WPB>
+__device__ __forceinline__ void solve_one(const SolveArgs &a, WaveFinish<GS> &wf, bool valid,
+                                          int64_t line, int64_t eg, uint32_t (&words)[WPB])
+{
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    constexpr double INV_GS = 1.0 / GS;
+    float w[GS];
+    float mn = 0.0f, mx = 0.0f, s = 1.0f, z = 0.0f, amag = 0.0f;
+    double sw = 0.0;
+    if (valid) {
+        load_group<GS, AXIS>(a.W, a.cols, line, eg, w);
+        mn = w[0];
+        mx = w[0];
+#pragma unroll
+        for (int i = 1; i < GS; ++i) {
+            mn = fminf(mn, w[i]);
+            mx = fmaxf(mx, w[i]);
+        }
+        const float rng = mx - mn;
+        if (rng == 0.0f) {
+            s = 1.0f;
+            z = -mn;
+        } else {
+            s = QMAX / rng;
+            z = -(mn * s);
+        }
+        sw = exact_sum<GS>(w);
+        amag = fmaxf(fabsf(mn), fabsf(mx));
+    } else {
+#pragma unroll
+        for (int i = 0; i < GS; ++i)
+            w[i] = 0.0f;
+    }
+    const float thr_s = a.thr * s;
+    const float lim = a.thr_m * s;
+
+    // fast loop; a lane freezes its group at the first iteration whose
+    // certificate fails
+    bool run = valid, frozen = false;
+    float beta = a.beta0, beta_f = a.beta0;
+    int it_f = a.iters;
+    for (int it = 0; it < a.iters; ++it) {
+        if (!__any(run))
+            break;
+        if (run) {
+            const float tmin = __builtin_fmaf(mn, s, z);
+            const float tmax = __builtin_fmaf(mx, s, z);
+            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+            const bool est_ok = __builtin_fmaf(amag, s, fabsf(z)) + QMAX <= lim;
+            if (!(est_ok && bound <= thr_s)) {
+                run = false;
+                frozen = true;
+                it_f = it;
+                beta_f = beta;
+            }
+        }
+        if (run) {
+            // sums of small non-negative integers: exact in any order
+            float s0 = quant(w[0], s, z, QMAX), s1 = quant(w[1], s, z, QMAX);
+            float s2 = quant(w[2], s, z, QMAX), s3 = quant(w[3], s, z, QMAX);
+#pragma unroll
+            for (int i = 4; i < GS; i += 4) {
+                s0 += quant(w[i + 0], s, z, QMAX);
+                s1 += quant(w[i + 1], s, z, QMAX);
+                s2 += quant(w[i + 2], s, z, QMAX);
+                s3 += quant(w[i + 3], s, z, QMAX);
+            }
+            const float sq = (s0 + s1) + (s2 + s3);
+            z = (float)(((double)sq - (double)s * sw) * INV_GS);
+        }
+        beta = beta * a.kappa;
+    }
+    if (valid && !frozen)
+        pack_codes<NB, GS, G>(w, s, z, words);
+    if (__any(frozen)) {
+        finish_frozen<NB, GS>(a, wf, frozen, w, s, z, beta_f, mn, mx, amag, it_f, sw);
+        if (frozen) {
+            float w2[GS];
+            load_group<GS, AXIS>(a.W, a.cols, line, eg, w2);
+            pack_codes<NB, GS, G>(w2, s, z, words);
+        }
+    }
+    if (valid) {
+        const int64_t L = AXIS == 1 ? a.cols : a.rows;
+        const int64_t gi = AXIS == 1 ? line * (L / GS) + eg / GS : (eg / GS) * a.cols + line;
+        a.scale[gi] = s;
+        a.zero[gi] = z;
+    }
+}
+
+template <int NB, int GS, int AXIS, int G, int GSEQ, int WPB>
+__device__ __forceinline__ void solve_seq(const SolveArgs &a, WaveFinish<GS> &wf, int ng,
+                                          int64_t line, int64_t e0, uint32_t (&words)[WPB])
+{
+    if constexpr (G < GSEQ) {
+        solve_one<NB, GS, G, AXIS>(a, wf, G < ng, line, e0 + (int64_t)G * GS, words);
+        solve_seq<NB, GS, AXIS, G + 1, GSEQ>(a, wf, ng, line, e0, words);
+    }
+}
+
+template <int NB, int GS, int AXIS>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(waves_per_simd(GS))))
+void solve_kernel(SolveArgs a)
+{
+    constexpr int C = codes_per_word(NB);
+    constexpr int LB = lcm_c(GS, C);      // elements per work item
+    constexpr int GSEQ = LB / GS;         // groups per work item
+    constexpr int WPB = LB / C;           // words per work item
+    __shared__ WaveFinish<GS> finish[kWaves];
+
+    // every lane stays to the end: lanes past the last work item own no group
+    // but take part in the wave's finish phases
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = item < a.n_items;
+    const int64_t it_c = live ? item : 0;
+    int64_t line, blk;
+    if constexpr (AXIS == 1) {
+        line = it_c / a.nblk;
+        blk = it_c - line * a.nblk;
+    } else {
+        blk = it_c / a.cols;
+        line = it_c - blk * a.cols;
+    }
+    const int64_t L = AXIS == 1 ? a.cols : a.rows;
+    const int64_t e0 = blk * LB;
+    const int64_t rem = (L - e0) / GS;
+    const int ng = live ? (rem < GSEQ ? (int)rem : GSEQ) : 0;   // valid groups of this item
+    const int64_t words_per_line = (L + C - 1) / C;
+    const int64_t k0 = e0 / C;
+
+    uint32_t words[WPB];
+#pragma unroll
+    for (int k = 0; k < WPB; ++k)
+        words[k] = 0;
+    solve_seq<NB, GS, AXIS, 0, GSEQ>(a, finish[threadIdx.x / 64], ng, line, e0, words);
+#pragma unroll
+    for (int k = 0; k < WPB; ++k) {
+        if (k * C < ng * GS && k0 + k < words_per_line) {
+            const int64_t addr = AXIS == 1 ? line * words_per_line + k0 + k
+                                           : (k0 + k) * a.cols + line;
+            __builtin_nontemporal_store(words[k], a.packed + addr);
+        }
+    }
+}
+
+template <int NB, int AXIS>
+hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
+{
+    const dim3 block(kBlock);
+    const dim3 grid((unsigned)((a.n_items + kBlock - 1) / kBlock));
+    switch (group_size) {
+    case 8: hipLaunchKernelGGL((solve_kernel<NB, 8, AXIS>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((solve_kernel<NB, 16, AXIS>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((solve_kernel<NB, 32, AXIS>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((solve_kernel<NB, 64, AXIS>), grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL((solve_kernel<NB, 128, AXIS>), grid, block, 0, st, a); break;
+    case 256: hipLaunchKernelGGL((solve_kernel<NB, 256, AXIS>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// launcher of the NB-bit solve kernels (defined in hqq_solve_b<NB>.hip)
+template <int NB>
+hipError_t launch_solve_nb(int group_size, int axis, const SolveArgs &a, hipStream_t st)
+{
+    return axis == 1 ? launch_gs<NB, 1>(group_size, a, st) : launch_gs<NB, 0>(group_size, a, st);
+}
+
+}  // namespace hqq
