@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step quantizes every tensor of the workload once (one hqq_quantize launch
-per Linear weight), with all fp16 inputs already resident in HBM.  The default
+A step quantizes every tensor of the workload once, with all fp16 inputs
+already resident in HBM: consecutive tensors of one format go to
+hqq_quantize_batch in chunks of up to 24 (one kernel launch per chunk).  The default
 workload is the 7B-shaped stack: 32 decoder layers of q/k/v/o [4096,4096],
 gate/up [11008,4096], down [4096,11008] -- 6,476,005,376 fp16 weights
 (12.95 GB) -- at nbits=4, group_size=64, axis=1, 20 iterations, p=0.7,
@@ -29,23 +30,59 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GB/s of fp16 weights quantized (HQQ 4b g64, 20 it), 7B-shaped; % roofline"
 
-# MI355X (gfx950) peaks.  VALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz lane-ops
-# per second for non-packed fp32 (the 157.3 TFLOP/s headline counts an FMA as
-# 2 flops and packed fp32 as 2 lanes).  HBM3E: 8 TB/s.
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# MI355X (gfx950) peaks.  VALU: the 157.3 TFLOP/s fp32 vector figure is
+# 256 CUs x 2.4 GHz x 128 FMA lanes per clock per CU (an FMA counts as 2
+# flops), i.e. 78.6 T lane-ops/s; plain (non-packed) VALU instructions issue at
+# that rate too.  HBM3E: 8 TB/s.
+VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 
-# Algorithmic VALU ops per weight of the solve (the minimum the method needs
-# per element, per-group work excluded): per iteration fma, round, clamp,
-# accumulate W_q (4); once: widen, min, max, exact sum (2), final fma, round,
-# clamp, to-int, pack (5) -> 10.
-def valu_ops_per_weight(iters: int) -> int:
-    return 4 * iters + 10
+
+# VALU lane-ops per weight that the solve needs on gfx950 where the shrink is
+# certified zero (the whole of the 4b/3b/2b workloads): per iteration one fma,
+# one round-saturate-pack to a byte (v_cvt_pk_u8_f32), and two byte-sums per
+# four weights (v_sad_u8) that give sum W_q with the clamp at qmax -> 2.5;
+# once per weight: widen, min, max, exact fp64 sum (2), final fma, round,
+# clamp, insert into the word (4) -> 10.
+def valu_ops_per_weight(iters: int) -> float:
+    return 2.5 * iters + 10
 
 
 def hbm_bytes_per_weight(nbits: int, group_size: int) -> float:
     C = {4: 8, 3: 10, 2: 16, 1: 32}[nbits]
     return 2.0 + 4.0 / C + 8.0 / group_size
+
+
+# HBM traffic of the solve kernel per launch, from the committed rocprofv3
+# FETCH_SIZE / WRITE_SIZE summary; used only while the kernel's sources are
+# byte-identical to the ones the counters were taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "solve_4b_g64_llama7b_stack32.traffic.json")
+KERNEL_SOURCES = ["weight_quantization_group_amd/csrc/hqq_solve_impl.h",
+                  "weight_quantization_group_amd/csrc/hqq_solve_b4.hip",
+                  "weight_quantization_group_amd/csrc/hqq_internal.h"]
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(weights_per_launch: float):
+    """HBM bytes per launch of the dominant solve kernel (counter-measured,
+    calibrated on a plain copy), or None if stale or absent."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t["hbm_bytes_per_weight"] * weights_per_launch
 
 
 def cpu_baseline(workload: str, iters: int, max_procs: int = 16):
@@ -147,21 +184,32 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # launches: consecutive tensors of one format, up to MAX_BATCH per
+    # hqq_quantize_batch call (one kernel launch each)
+    chunks = []
+    for i, t in enumerate(tensors):
+        fmt = (t["nbits"], t["group_size"], t["axis"])
+        if chunks and chunks[-1][0] == fmt and len(chunks[-1][1]) < hq.MAX_BATCH:
+            chunks[-1][1].append(i)
+        else:
+            chunks.append((fmt, [i]))
+    calls = [(fmt, [(ins[i], *outs[i]) for i in idx], sum(tensors[i]["rows"] * tensors[i]["cols"] for i in idx))
+             for fmt, idx in chunks]
+
     def step(events=None):
-        for i, (t, W, (pk, sc, ze)) in enumerate(zip(tensors, ins, outs)):
+        for j, ((nb_, gs_, ax_), items, _) in enumerate(calls):
             if events is not None:
-                events[i][0].record()
-            hq.hqq_quantize(W, t["nbits"], t["group_size"], t["axis"], iters=args.iters,
-                            packed=pk, scale=sc, zero=ze)
+                events[j][0].record()
+            hq.hqq_quantize_batch(items, nb_, gs_, ax_, iters=args.iters)
             if events is not None:
-                events[i][1].record()
+                events[j][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in tensors] for _ in range(args.steps)]
+            for _ in calls] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -171,16 +219,13 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # per-launch kernel durations (HIP events on the launch stream)
-    kdur = [[evs[k][i][0].elapsed_time(evs[k][i][1]) for i in range(len(tensors))]
-            for k in range(args.steps)]
-    # dominant kernel: the (nbits, group_size, axis) with the most weights
     by_fmt = {}
-    for i, t in enumerate(tensors):
-        key = (t["nbits"], t["group_size"], t["axis"])
-        d = by_fmt.setdefault(key, dict(w=0, ms=0.0, launches=0))
-        d["w"] += t["rows"] * t["cols"] * args.steps
-        d["ms"] += sum(kdur[k][i] for k in range(args.steps))
+    for j, (fmt, items, w) in enumerate(calls):
+        d = by_fmt.setdefault(fmt, dict(w=0, ms=0.0, launches=0))
+        d["w"] += w * args.steps
+        d["ms"] += sum(evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps))
         d["launches"] += args.steps
+    # dominant kernel: the format with the most weights
     (nb, gs, ax), dom = max(by_fmt.items(), key=lambda kv: kv[1]["w"])
     w_per_launch = dom["w"] / dom["launches"]
     avg_ms = dom["ms"] / dom["launches"]
@@ -203,12 +248,13 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
+                   "launches_per_step": len(calls),
                    "nbits": nb, "group_size": gs, "axis": ax, "iters": args.iters,
                    "p": 0.7, "beta0": 10.0, "kappa": 1.01},
         "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "alu", "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "TOP/s", "frac": round(achieved_tops / VALU_PEAK_TOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(w_per_launch),
                      "kernel": f"solve_kernel<{nb},{gs},{ax}>",
                      "avg_launch_ms": round(avg_ms, 5),
                      "ops_per_weight": valu_ops_per_weight(args.iters),

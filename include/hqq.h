@@ -73,7 +73,7 @@ extern "C" {
 #define HQQ_EINVAL_NBITS (-1) /* nbits not in {1,2,3,4}                              */
 #define HQQ_EINVAL_AXIS (-2)  /* axis not in {0,1}                                   */
 #define HQQ_EINVAL_GROUP (-3) /* group_size unsupported or not dividing the line     */
-#define HQQ_EINVAL_SHAPE (-4) /* rows or cols < 1, or too large                      */
+#define HQQ_EINVAL_SHAPE (-4) /* rows or cols < 1 or too large, or batch count < 0    */
 #define HQQ_EINVAL_PTR (-5)   /* NULL or misaligned pointer                          */
 #define HQQ_EINVAL_PARAM (-6) /* iters < 0, or p, beta0, kappa not finite and > 0    */
 #define HQQ_EHIP (-7)         /* a HIP launch failed                                  */
@@ -88,6 +88,29 @@ HQQ_API int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols,
                  int nbits, int group_size, int axis,
                  int iters, float p, float beta0, float kappa,
                  uint32_t *packed, float *scale, float *zero, void *stream);
+
+/* One tensor of a batched quantize call (all pointers device, 16-byte aligned;
+ * layouts as for hqq_quantize). */
+typedef struct hqq_tensor {
+    const uint16_t *W;   /* fp16 bits [rows, cols], read only */
+    int64_t rows, cols;
+    uint32_t *packed;    /* hqq_packed_words(rows, cols, nbits, axis) words, written */
+    float *scale;        /* rows*cols/group_size values, written */
+    float *zero;         /* rows*cols/group_size values, written */
+} hqq_tensor;
+
+/* Quantize n tensors that share one format (nbits, group_size, axis) and one
+ * set of solve parameters, with results identical to n hqq_quantize calls.
+ * This is the pages' whole-model quantization (lnwmold.com HQQ guide section
+ * 3.3, AutoHQQHFModel.quantize_model walks a model's Linear layers) in as few
+ * kernel launches as possible: up to 24 tensors per launch, so the GPU is not
+ * idle between small launches and a wave's tail overlaps other tensors' work.
+ *   tensors  HOST array of n descriptors (read during the call only)
+ * Every descriptor is validated before anything is enqueued.  n = 0 is a
+ * no-op.  Returns HQQ_OK or a negative HQQ_E* status. */
+HQQ_API int hqq_quantize_batch(const hqq_tensor *tensors, int n,
+                               int nbits, int group_size, int axis,
+                               int iters, float p, float beta0, float kappa, void *stream);
 
 /* Dequantize: W_hat = fp16_round_half_even((W_q - zero) / scale) with an
  * IEEE fp32 subtraction and division (lnwmold.com HQQ guide section 3.2,

@@ -38,8 +38,8 @@ def test_header_codes_match():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
-    assert declared == sorted(["hqq_quantize", "hqq_dequantize", "hqq_pack", "hqq_unpack",
-                               "hqq_packed_words", "hqq_strerror"])
+    assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack",
+                               "hqq_unpack", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -103,6 +103,30 @@ def test_codec_rejects(lib):
     assert lib.hqq_pack(MIS, 64, 128, 4, 64, 1, A, None) == E["PTR"]
     assert lib.hqq_unpack(A, 0, 128, 4, 64, 1, A, None) == E["SHAPE"]
     assert lib.hqq_unpack(A, 64, 128, 4, 32, 0, None, None) == E["PTR"]
+
+
+def test_batch_rejects(lib):
+    import weight_quantization_group_amd as w
+
+    def call(tensors, n, **kw):
+        args = dict(nbits=4, gs=64, axis=1, iters=20, p=0.7, beta0=10.0, kappa=1.01)
+        args.update(kw)
+        ptr = ctypes.cast(tensors, ctypes.c_void_p) if tensors is not None else None
+        return lib.hqq_quantize_batch(ptr, n, args["nbits"], args["gs"], args["axis"], args["iters"],
+                                      args["p"], args["beta0"], args["kappa"], None)
+
+    good = w.HqqTensor(0x1000, 64, 128, 0x1000, 0x1000, 0x1000)
+    bad_shape = w.HqqTensor(0x1000, 64, 100, 0x1000, 0x1000, 0x1000)
+    bad_ptr = w.HqqTensor(0x1000, 64, 128, 0x1002, 0x1000, 0x1000)
+    arr = (w.HqqTensor * 3)(good, good, bad_shape)
+    assert call(arr, 3) == E["GROUP"]          # the third descriptor fails: nothing is launched
+    arr = (w.HqqTensor * 2)(good, bad_ptr)
+    assert call(arr, 2) == E["PTR"]
+    assert call(None, 2) == E["PTR"]
+    assert call(arr, -1) == E["SHAPE"]
+    assert call(arr, 2, iters=-3) == E["PARAM"]
+    assert call(arr, 2, nbits=7) == E["NBITS"]
+    assert call(None, 0) == E["OK"]           # empty batch: a no-op, no HIP call
 
 
 def test_product_does_not_touch_oracle():

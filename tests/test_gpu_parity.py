@@ -220,6 +220,36 @@ def test_determinism_and_streams(hq):
         assert np.array_equal(x.view(np.uint32), z.view(np.uint32))
 
 
+@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (3, 64, 0), (2, 16, 1), (1, 16, 0)])
+def test_batch_equals_single_calls(hq, oracle_mod, nbits, gs, axis):
+    """hqq_quantize_batch over 30 same-format tensors of mixed shapes (two
+    launches) equals per-tensor calls bit for bit, and the oracle on a few."""
+    import torch
+
+    rng = np.random.RandomState(nbits * 100 + gs + axis)
+    items, Ws = [], []
+    for i in range(30):
+        lines = 1 + rng.randint(0, 40)
+        other = gs * (1 + rng.randint(0, 12))
+        shape = (lines, other) if axis == 1 else (other, lines)
+        W16 = random_f16(rng, shape, std=0.03, outlier_frac=0.005)
+        Wd = _dev16(W16)
+        rows, cols = shape
+        items.append((Wd, torch.empty(hq.packed_shape(rows, cols, nbits, axis), dtype=torch.int32, device="cuda"),
+                      torch.empty(hq.meta_shape(rows, cols, gs, axis), dtype=torch.float32, device="cuda"),
+                      torch.empty(hq.meta_shape(rows, cols, gs, axis), dtype=torch.float32, device="cuda")))
+        Ws.append(W16)
+    hq.hqq_quantize_batch(items, nbits, gs, axis)
+    torch.cuda.synchronize()
+    for i, (Wd, pk, sc, ze) in enumerate(items):
+        p1, s1, z1 = hq.hqq_quantize(Wd, nbits, gs, axis)
+        torch.cuda.synchronize()
+        assert torch.equal(pk, p1) and torch.equal(sc, s1) and torch.equal(ze, z1), i
+        if i % 7 == 0:
+            check_parity(oracle_mod, Ws[i], nbits, gs, axis, _np_u32(pk), sc.cpu().numpy(),
+                         ze.cpu().numpy(), tag=f"batch item {i}")
+
+
 def test_binding_raises(hq):
     import torch
 

@@ -27,8 +27,17 @@ CODES_PER_WORD = {4: 8, 3: 10, 2: 16, 1: 32}
 P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
-EXPORTS = ("hqq_quantize", "hqq_dequantize", "hqq_pack", "hqq_unpack",
+EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack", "hqq_unpack",
            "hqq_packed_words", "hqq_strerror")
+
+# tensors per kernel launch of hqq_quantize_batch
+MAX_BATCH = 24
+
+
+class HqqTensor(ctypes.Structure):
+    """struct hqq_tensor of include/hqq.h"""
+    _fields_ = [("W", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p)]
 
 _lib = None
 
@@ -50,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     L.hqq_quantize.argtypes = [P, i64, i64, i32, i32, i32, i32, f32, f32, f32, P, P, P, P]
     L.hqq_quantize.restype = i32
+    L.hqq_quantize_batch.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P]
+    L.hqq_quantize_batch.restype = i32
     L.hqq_dequantize.argtypes = [P, P, P, i64, i64, i32, i32, i32, P, P]
     L.hqq_dequantize.restype = i32
     L.hqq_pack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
@@ -128,6 +139,26 @@ def hqq_quantize(W: torch.Tensor, nbits: int, group_size: int, axis: int,
     if st != 0:
         raise HQQError("hqq_quantize", st)
     return packed, scale, zero
+
+
+def hqq_quantize_batch(items, nbits: int, group_size: int, axis: int,
+                       iters: int = ITERS_DEFAULT, p: float = P_DEFAULT,
+                       beta0: float = BETA0_DEFAULT, kappa: float = KAPPA_DEFAULT):
+    """Quantize several same-format tensors in as few launches as possible.
+    items: list of (W, packed, scale, zero) CUDA tensors (outputs preallocated)."""
+    L = load_library()
+    n = len(items)
+    arr = (HqqTensor * max(n, 1))()
+    for i, (W, pk, sc, ze) in enumerate(items):
+        rows, cols = W.shape
+        arr[i] = HqqTensor(_dev_ptr(W, "W", _F16).value, rows, cols,
+                           _dev_ptr(pk, "packed", _U32).value, _dev_ptr(sc, "scale", (torch.float32,)).value,
+                           _dev_ptr(ze, "zero", (torch.float32,)).value)
+    dev = items[0][0].device if n else torch.device("cuda", torch.cuda.current_device())
+    st = L.hqq_quantize_batch(ctypes.cast(arr, ctypes.c_void_p), n, nbits, group_size, axis, iters,
+                              p, beta0, kappa, _stream(dev))
+    if st != 0:
+        raise HQQError("hqq_quantize_batch", st)
 
 
 def hqq_dequantize(packed, scale, zero, rows: int, cols: int, nbits: int, group_size: int,

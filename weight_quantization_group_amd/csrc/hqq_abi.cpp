@@ -96,25 +96,27 @@ const char *hqq_strerror(int status)
     }
 }
 
-int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int group_size,
-                 int axis, int iters, float p, float beta0, float kappa, uint32_t *packed,
-                 float *scale, float *zero, void *stream)
+int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_size, int axis,
+                       int iters, float p, float beta0, float kappa, void *stream)
 {
-    int st = check_common(rows, cols, nbits, group_size, axis);
-    if (st)
-        return st;
-    if (!aligned16(W) || !aligned16(packed) || !aligned16(scale) || !aligned16(zero))
+    if (n < 0)
+        return HQQ_EINVAL_SHAPE;
+    if (n > 0 && !tensors)
         return HQQ_EINVAL_PTR;
     if (iters < 0 || iters > kMaxIters || !finite_pos(p) || !finite_pos(beta0) || !finite_pos(kappa))
         return HQQ_EINVAL_PARAM;
+    for (int i = 0; i < n; ++i) {
+        const hqq_tensor &t = tensors[i];
+        int st = check_common(t.rows, t.cols, nbits, group_size, axis);
+        if (st)
+            return st;
+        if (!aligned16(t.W) || !aligned16(t.packed) || !aligned16(t.scale) || !aligned16(t.zero))
+            return HQQ_EINVAL_PTR;
+    }
+    if (n == 0)
+        return HQQ_OK;
 
     hqq::SolveArgs a{};
-    a.W = W;
-    a.packed = packed;
-    a.scale = scale;
-    a.zero = zero;
-    a.rows = rows;
-    a.cols = cols;
     a.iters = iters;
     a.pm1 = p - 1.0f;
     a.beta0 = beta0;
@@ -122,11 +124,44 @@ int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int g
     certificate(iters, a.pm1, beta0, kappa, &a.thr, &a.thr_m);
     const int C = hqq::codes_per_word(nbits);
     const int64_t lb = hqq::lcm_c(group_size, C);
-    const int64_t L = axis == 1 ? cols : rows;
-    a.nblk = (L + lb - 1) / lb;
-    a.n_items = a.nblk * (axis == 1 ? rows : cols);
-    const hipError_t e = hqq::launch_solve(nbits, group_size, axis, a, (hipStream_t)stream);
-    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+    const int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+    int i = 0;
+    while (i < n) {
+        a.n = 0;
+        a.blocks = 0;
+        while (i < n && a.n < hqq::kMaxBatch) {
+            const hqq_tensor &t = tensors[i];
+            hqq::SolveTensor &d = a.t[a.n];
+            const int64_t L = axis == 1 ? t.cols : t.rows;
+            d.W = t.W;
+            d.packed = t.packed;
+            d.scale = t.scale;
+            d.zero = t.zero;
+            d.rows = t.rows;
+            d.cols = t.cols;
+            d.nblk = (L + lb - 1) / lb;
+            d.n_items = d.nblk * (axis == 1 ? t.rows : t.cols);
+            const int64_t nb = (d.n_items + hqq::kSolveBlock - 1) / hqq::kSolveBlock;
+            if (a.n > 0 && a.blocks + nb > kMaxBlocks)
+                break;
+            d.block0 = a.blocks;
+            a.blocks += nb;
+            ++a.n;
+            ++i;
+        }
+        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, a, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return HQQ_EHIP;
+    }
+    return HQQ_OK;
+}
+
+int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int group_size,
+                 int axis, int iters, float p, float beta0, float kappa, uint32_t *packed,
+                 float *scale, float *zero, void *stream)
+{
+    const hqq_tensor t{W, rows, cols, packed, scale, zero};
+    return hqq_quantize_batch(&t, 1, nbits, group_size, axis, iters, p, beta0, kappa, stream);
 }
 
 int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero, int64_t rows,

@@ -10,15 +10,25 @@ constexpr int codes_per_word(int nb) { return nb == 4 ? 8 : nb == 3 ? 10 : nb ==
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 
-// Arguments of the solve kernels (passed by value as the kernel argument).
-struct SolveArgs {
+// One tensor of a solve launch.
+struct SolveTensor {
     const uint16_t *W;   // fp16 bits [rows, cols]
     uint32_t *packed;    // packed codes
     float *scale;        // per-group scale
     float *zero;         // per-group zero
     int64_t rows, cols;
     int64_t n_items;     // work items (lanes): one block of lcm(gs, C) elements of one line
-    int64_t nblk;        // blocks per line
+    int64_t nblk;        // work items per line
+    int64_t block0;      // first workgroup of this tensor in the launch
+};
+
+// Up to this many same-format tensors share one launch (kernel-argument size).
+constexpr int kMaxBatch = 24;
+// Threads per workgroup of the solve kernels.
+constexpr int kSolveBlock = 256;
+
+// Arguments of the solve kernels (passed by value as the kernel argument).
+struct SolveArgs {
     int iters;
     float pm1;           // p - 1 (fp32)
     float beta0, kappa;
@@ -27,6 +37,9 @@ struct SolveArgs {
     // magnitude for which the cheap residual estimate |t - q| / scale is
     // accurate enough to use it.
     float thr, thr_m;
+    int n;               // tensors in this launch
+    int64_t blocks;      // workgroups of the launch
+    SolveTensor t[kMaxBatch];
 };
 
 struct CodecArgs {

@@ -36,7 +36,9 @@
 //   fast loop:  while that bound is below thr*scale (and the group's
 //               magnitude keeps the estimate's error far below the 2% margin)
 //               every W_e of the group is 0 and the update is
-//               (sum W_q - scale * sum w) / gs: 4 VALU ops per weight.
+//               (sum W_q - scale * sum w) / gs: per weight one fma and one
+//               round-and-pack to a byte (v_cvt_pk_u8_f32), and two byte-sums
+//               per four weights that apply the clamp to the sum.
 //   freeze:     a group that fails the test stops in its lane (the lane idles
 //               while the wave's other groups finish their iterations).
 //   finish:     the wave then completes its frozen groups together, one lane
@@ -54,7 +56,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;   // threads per workgroup of the solve kernels
+constexpr int kBlock = kSolveBlock;
 constexpr int kWaves = kBlock / 64;
 
 // Load one group (gs fp16 values) and widen exactly to fp32.
@@ -320,7 +322,8 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
 constexpr int waves_per_simd(int gs) { return gs <= 8 ? 8 : gs == 16 ? 6 : gs == 32 ? 6 : gs == 64 ? 4 : gs == 128 ? 2 : 1; }
 
 template <int NB, int GS, int G, int AXIS, int WPB>
-__device__ __forceinline__ void solve_one(const SolveArgs &a, WaveFinish<GS> &wf, bool valid,
+__device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor &T,
+                                          WaveFinish<GS> &wf, bool valid,
                                           int64_t line, int64_t eg, uint32_t (&words)[WPB])
 {
     constexpr float QMAX = (float)((1 << NB) - 1);
@@ -329,7 +332,7 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, WaveFinish<GS> &wf
     float mn = 0.0f, mx = 0.0f, s = 1.0f, z = 0.0f, amag = 0.0f;
     double sw = 0.0;
     if (valid) {
-        load_group<GS, AXIS>(a.W, a.cols, line, eg, w);
+        load_group<GS, AXIS>(T.W, T.cols, line, eg, w);
         mn = w[0];
         mx = w[0];
 #pragma unroll
@@ -376,17 +379,29 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, WaveFinish<GS> &wf
             }
         }
         if (run) {
-            // sums of small non-negative integers: exact in any order
-            float s0 = quant(w[0], s, z, QMAX), s1 = quant(w[1], s, z, QMAX);
-            float s2 = quant(w[2], s, z, QMAX), s3 = quant(w[3], s, z, QMAX);
+            // W_q and sum W_q.  v_cvt_pk_u8_f32 rounds half to even and
+            // saturates to [0, 255] (the clamp at 0), four codes to a word;
+            // v_sad_u8 against 0 adds a word's four codes c, against qmax in
+            // every byte their |c - qmax|, and min(c, qmax) is
+            // (c + qmax - |c - qmax|) / 2: 2.5 VALU ops per weight.
+            static_assert(GS % 8 == 0, "two byte-sum chains of whole words");
+            constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
+            uint32_t c0 = 0, c1 = 0, a0 = 0, a1 = 0;
 #pragma unroll
-            for (int i = 4; i < GS; i += 4) {
-                s0 += quant(w[i + 0], s, z, QMAX);
-                s1 += quant(w[i + 1], s, z, QMAX);
-                s2 += quant(w[i + 2], s, z, QMAX);
-                s3 += quant(w[i + 3], s, z, QMAX);
+            for (int k = 0; k < GS / 4; k += 2) {
+                uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 0], s, z), 0, 0u);
+                uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4], s, z), 0, 0u);
+#pragma unroll
+                for (int j = 1; j < 4; ++j) {
+                    d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + j], s, z), j, d0);
+                    d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4 + j], s, z), j, d1);
+                }
+                c0 = __builtin_amdgcn_sad_u8(d0, 0u, c0);
+                c1 = __builtin_amdgcn_sad_u8(d1, 0u, c1);
+                a0 = __builtin_amdgcn_sad_u8(d0, QB, a0);
+                a1 = __builtin_amdgcn_sad_u8(d1, QB, a1);
             }
-            const float sq = (s0 + s1) + (s2 + s3);
+            const uint32_t sq = ((c0 + c1) + (uint32_t)(GS * ((1 << NB) - 1)) - (a0 + a1)) >> 1;
             z = (float)(((double)sq - (double)s * sw) * INV_GS);
         }
         beta = beta * a.kappa;
@@ -397,25 +412,26 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, WaveFinish<GS> &wf
         finish_frozen<NB, GS>(a, wf, frozen, w, s, z, beta_f, mn, mx, amag, it_f, sw);
         if (frozen) {
             float w2[GS];
-            load_group<GS, AXIS>(a.W, a.cols, line, eg, w2);
+            load_group<GS, AXIS>(T.W, T.cols, line, eg, w2);
             pack_codes<NB, GS, G>(w2, s, z, words);
         }
     }
     if (valid) {
-        const int64_t L = AXIS == 1 ? a.cols : a.rows;
-        const int64_t gi = AXIS == 1 ? line * (L / GS) + eg / GS : (eg / GS) * a.cols + line;
-        a.scale[gi] = s;
-        a.zero[gi] = z;
+        const int64_t L = AXIS == 1 ? T.cols : T.rows;
+        const int64_t gi = AXIS == 1 ? line * (L / GS) + eg / GS : (eg / GS) * T.cols + line;
+        T.scale[gi] = s;
+        T.zero[gi] = z;
     }
 }
 
 template <int NB, int GS, int AXIS, int G, int GSEQ, int WPB>
-__device__ __forceinline__ void solve_seq(const SolveArgs &a, WaveFinish<GS> &wf, int ng,
+__device__ __forceinline__ void solve_seq(const SolveArgs &a, const SolveTensor &T,
+                                          WaveFinish<GS> &wf, int ng,
                                           int64_t line, int64_t e0, uint32_t (&words)[WPB])
 {
     if constexpr (G < GSEQ) {
-        solve_one<NB, GS, G, AXIS>(a, wf, G < ng, line, e0 + (int64_t)G * GS, words);
-        solve_seq<NB, GS, AXIS, G + 1, GSEQ>(a, wf, ng, line, e0, words);
+        solve_one<NB, GS, G, AXIS>(a, T, wf, G < ng, line, e0 + (int64_t)G * GS, words);
+        solve_seq<NB, GS, AXIS, G + 1, GSEQ>(a, T, wf, ng, line, e0, words);
     }
 }
 
@@ -429,20 +445,26 @@ void solve_kernel(SolveArgs a)
     constexpr int WPB = LB / C;           // words per work item
     __shared__ WaveFinish<GS> finish[kWaves];
 
+    // the launch's tensor of this workgroup (tensors start on workgroup
+    // boundaries, so the search is uniform)
+    int ti = 0;
+    while (ti + 1 < a.n && (int64_t)blockIdx.x >= a.t[ti + 1].block0)
+        ++ti;
+    const SolveTensor &T = a.t[ti];
     // every lane stays to the end: lanes past the last work item own no group
     // but take part in the wave's finish phases
-    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool live = item < a.n_items;
+    const int64_t item = ((int64_t)blockIdx.x - T.block0) * blockDim.x + threadIdx.x;
+    const bool live = item < T.n_items;
     const int64_t it_c = live ? item : 0;
     int64_t line, blk;
     if constexpr (AXIS == 1) {
-        line = it_c / a.nblk;
-        blk = it_c - line * a.nblk;
+        line = it_c / T.nblk;
+        blk = it_c - line * T.nblk;
     } else {
-        blk = it_c / a.cols;
-        line = it_c - blk * a.cols;
+        blk = it_c / T.cols;
+        line = it_c - blk * T.cols;
     }
-    const int64_t L = AXIS == 1 ? a.cols : a.rows;
+    const int64_t L = AXIS == 1 ? T.cols : T.rows;
     const int64_t e0 = blk * LB;
     const int64_t rem = (L - e0) / GS;
     const int ng = live ? (rem < GSEQ ? (int)rem : GSEQ) : 0;   // valid groups of this item
@@ -453,13 +475,26 @@ void solve_kernel(SolveArgs a)
 #pragma unroll
     for (int k = 0; k < WPB; ++k)
         words[k] = 0;
-    solve_seq<NB, GS, AXIS, 0, GSEQ>(a, finish[threadIdx.x / 64], ng, line, e0, words);
+    solve_seq<NB, GS, AXIS, 0, GSEQ>(a, T, finish[threadIdx.x / 64], ng, line, e0, words);
+    // Words go out through L2 (ordinary stores) so that lanes' partial lines
+    // merge before reaching HBM.  axis = 1: a lane's words are contiguous and
+    // leave as 16-byte stores when the row pitch allows; axis = 0: each word
+    // store of the wave covers 64 consecutive columns.
+    if constexpr (AXIS == 1 && WPB % 4 == 0) {
+        if ((words_per_line & 3) == 0 && ng == GSEQ) {
+            u32x4 *dst = reinterpret_cast<u32x4 *>(T.packed + line * words_per_line + k0);
+#pragma unroll
+            for (int k = 0; k < WPB / 4; ++k)
+                dst[k] = u32x4{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
+            return;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < WPB; ++k) {
         if (k * C < ng * GS && k0 + k < words_per_line) {
             const int64_t addr = AXIS == 1 ? line * words_per_line + k0 + k
-                                           : (k0 + k) * a.cols + line;
-            __builtin_nontemporal_store(words[k], a.packed + addr);
+                                           : (k0 + k) * T.cols + line;
+            T.packed[addr] = words[k];
         }
     }
 }
@@ -468,7 +503,7 @@ template <int NB, int AXIS>
 hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 {
     const dim3 block(kBlock);
-    const dim3 grid((unsigned)((a.n_items + kBlock - 1) / kBlock));
+    const dim3 grid((unsigned)a.blocks);
     switch (group_size) {
     case 8: hipLaunchKernelGGL((solve_kernel<NB, 8, AXIS>), grid, block, 0, st, a); break;
     case 16: hipLaunchKernelGGL((solve_kernel<NB, 16, AXIS>), grid, block, 0, st, a); break;
