@@ -272,6 +272,32 @@ def _objective(w, s, z, q):
     return float(np.sum((w.astype(np.float64) * s + z - q) ** 2))
 
 
+@pytest.mark.parametrize("nbits,gs", [(4, 64), (3, 64), (2, 16), (1, 16), (4, 8)])
+def test_zero_sequence_monotone_and_settles(oracle_mod, nbits, gs):
+    """While every W_e is 0 the zero update reads the zero only through the
+    codes, and the codes are a non-decreasing function of the zero (fma, round
+    and clamp are monotone): so the zero sequence is monotone, and once an
+    update returns the zero it was given, every later one does too, bit for
+    bit.  The solve kernels stop a group at that point."""
+    rng = np.random.RandomState(70 + nbits * 10 + gs)
+    settled = 0
+    for _ in range(60):
+        w = f16_bits_to_f32(random_f16(rng, (gs,), std=0.02, outlier_frac=0.01))
+        r = oracle_mod.solve_group(w, nbits, iters=30, trace=True)   # default p, beta0, kappa
+        if np.any(r["e"] != 0):
+            continue
+        zt = r["zero_trace"].astype(np.float64)
+        d = np.diff(zt)
+        assert np.all(d >= 0) or np.all(d <= 0), zt
+        bits = r["zero_trace"].view(np.uint32)
+        rep = np.nonzero(bits[1:] == bits[:-1])[0]
+        if rep.size:
+            k = int(rep[0])
+            assert np.all(bits[k:] == bits[k]), zt
+            settled += 1
+    assert settled >= 30
+
+
 @pytest.mark.parametrize("nbits,gs", [(4, 64), (3, 64), (2, 16), (1, 16)])
 def test_alternation_descends_when_we_zero(oracle_mod, nbits, gs):
     """With W_e = 0 (beta0 tiny, so the shrink threshold is huge) each half-step minimises J(q, z) = sum (w s + z - q)^2

@@ -127,10 +127,11 @@ int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_si
     const int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
     int i = 0;
     while (i < n) {
+        // the tensors of this launch, and its work items
         a.n = 0;
-        a.blocks = 0;
-        while (i < n && a.n < hqq::kMaxBatch) {
-            const hqq_tensor &t = tensors[i];
+        int64_t items = 0;
+        while (i + a.n < n && a.n < hqq::kMaxBatch) {
+            const hqq_tensor &t = tensors[i + a.n];
             hqq::SolveTensor &d = a.t[a.n];
             const int64_t L = axis == 1 ? t.cols : t.rows;
             d.W = t.W;
@@ -141,14 +142,25 @@ int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_si
             d.cols = t.cols;
             d.nblk = (L + lb - 1) / lb;
             d.n_items = d.nblk * (axis == 1 ? t.rows : t.cols);
-            const int64_t nb = (d.n_items + hqq::kSolveBlock - 1) / hqq::kSolveBlock;
-            if (a.n > 0 && a.blocks + nb > kMaxBlocks)
-                break;
-            d.block0 = a.blocks;
-            a.blocks += nb;
+            items += d.n_items;
             ++a.n;
-            ++i;
         }
+        // work items per lane: deep enough to overlap each item's loads with
+        // the previous item's solve, shallow enough to keep many workgroups
+        int64_t depth = items / (hqq::kSolveBlock * hqq::kTargetBlocks);
+        a.depth = (int)(depth < 1 ? 1 : depth > hqq::kMaxDepth ? hqq::kMaxDepth : depth);
+        const int64_t per_block = (int64_t)hqq::kSolveBlock * a.depth;
+        a.blocks = 0;
+        int used = 0;
+        for (; used < a.n; ++used) {
+            const int64_t nb = (a.t[used].n_items + per_block - 1) / per_block;
+            if (used > 0 && a.blocks + nb > kMaxBlocks)
+                break;
+            a.block0[used] = a.blocks;
+            a.blocks += nb;
+        }
+        a.n = used;
+        i += used;
         const hipError_t e = hqq::launch_solve(nbits, group_size, axis, a, (hipStream_t)stream);
         if (e != hipSuccess)
             return HQQ_EHIP;

@@ -17,15 +17,19 @@ struct SolveTensor {
     float *scale;        // per-group scale
     float *zero;         // per-group zero
     int64_t rows, cols;
-    int64_t n_items;     // work items (lanes): one block of lcm(gs, C) elements of one line
+    int64_t n_items;     // work items: one block of lcm(gs, C) elements of one line
     int64_t nblk;        // work items per line
-    int64_t block0;      // first workgroup of this tensor in the launch
 };
 
 // Up to this many same-format tensors share one launch (kernel-argument size).
 constexpr int kMaxBatch = 24;
 // Threads per workgroup of the solve kernels.
 constexpr int kSolveBlock = 256;
+// A workgroup solves depth * kSolveBlock work items (depth steps per lane);
+// the host picks depth so that a launch still has about kTargetBlocks
+// workgroups.
+constexpr int kMaxDepth = 8;
+constexpr int64_t kTargetBlocks = 8192;
 
 // Arguments of the solve kernels (passed by value as the kernel argument).
 struct SolveArgs {
@@ -38,7 +42,9 @@ struct SolveArgs {
     // accurate enough to use it.
     float thr, thr_m;
     int n;               // tensors in this launch
+    int depth;           // work items per lane
     int64_t blocks;      // workgroups of the launch
+    int64_t block0[kMaxBatch];   // first workgroup of each tensor (increasing)
     SolveTensor t[kMaxBatch];
 };
 

@@ -15,15 +15,15 @@
 //
 // Mapping to CDNA4.  The solve is elementwise work plus per-group sums: no
 // dense contraction, so no MFMA.  One lane owns a whole group: its gs weights
-// are loaded from HBM once, widened exactly to fp32 and stay in VGPRs for all
-// iterations; min, max and the sums are in-lane, so the 64 lanes of a wave
-// run 64 independent groups with no cross-lane traffic.  Where C (codes per
-// uint32) and gs do not divide each other (3-bit, or gs < C) a lane owns
-// lcm(gs, C) consecutive elements of a line (several groups, solved one after
-// the other), so every packed word is assembled in-register by one lane and
-// written once.  axis = 1: lanes take consecutive blocks of a row; axis = 0:
-// lanes take consecutive columns, so each load and store instruction of a
-// wave touches 64 consecutive columns (coalesced).
+// cross HBM once (DMA into LDS one group ahead of the solve, then into VGPRs),
+// are widened exactly to fp32 and stay in VGPRs for all iterations; min, max
+// and the sums are in-lane, so the 64 lanes of a wave run 64 independent
+// groups with no cross-lane traffic.  Where C (codes per uint32) and gs do
+// not divide each other (3-bit, or gs < C) a lane owns lcm(gs, C) consecutive
+// elements of a line (several groups, solved one after the other), so every
+// packed word is assembled in-register by one lane and written once.
+// axis = 1: lanes take consecutive blocks of a row; axis = 0: lanes take
+// consecutive columns, so each access of a wave covers 64 consecutive columns.
 //
 // Exactness.  The arithmetic is the fp32 evaluation with w*scale+zero as one
 // fma and the mean in fp64: sum W_q (small integers) and sum w (fp16 values)
@@ -38,7 +38,11 @@
 //               every W_e of the group is 0 and the update is
 //               (sum W_q - scale * sum w) / gs: per weight one fma and one
 //               round-and-pack to a byte (v_cvt_pk_u8_f32), and two byte-sums
-//               per four weights that apply the clamp to the sum.
+//               per four weights that apply the clamp to the sum.  That update
+//               reads the zero only through the codes and no later iteration
+//               can fail the test (thr bounds every iteration), so once an
+//               update returns the zero it was given, every later one does:
+//               the group stops there with the result of all iterations.
 //   freeze:     a group that fails the test stops in its lane (the lane idles
 //               while the wave's other groups finish their iterations).
 //   finish:     the wave then completes its frozen groups together, one lane
@@ -49,6 +53,8 @@
 //               the pairwise tree.  Rare, outlier-heavy groups therefore cost
 //               a short SIMD phase instead of a long serial tail.
 #pragma once
+#include <type_traits>
+
 #include "hqq_internal.h"
 
 namespace hqq {
@@ -58,34 +64,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = kSolveBlock;
 constexpr int kWaves = kBlock / 64;
-
-// Load one group (gs fp16 values) and widen exactly to fp32.
-template <int GS, int AXIS>
-__device__ __forceinline__ void load_group(const uint16_t *__restrict__ W, int64_t cols,
-                                           int64_t line, int64_t e0, float (&w)[GS])
-{
-    if constexpr (AXIS == 1) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(W + line * cols + e0);
-#pragma unroll
-        for (int j = 0; j < GS / 8; ++j) {
-            u32x4 v = __builtin_nontemporal_load(src + j);
-            _Float16 h[8];
-            __builtin_memcpy(h, &v, 16);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[j * 8 + i] = (float)h[i];
-        }
-    } else {
-        const uint16_t *src = W + e0 * cols + line;
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-            uint16_t b = __builtin_nontemporal_load(src + (int64_t)i * cols);
-            _Float16 h;
-            __builtin_memcpy(&h, &b, 2);
-            w[i] = (float)h;
-        }
-    }
-}
 
 __device__ __forceinline__ float quant(float w, float s, float z, float qmax)
 {
@@ -105,6 +83,43 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f)   // exact for f
     uint16_t b;
     __builtin_memcpy(&b, &h, 2);
     return b;
+}
+
+// Column line of rows eg..eg+gs-1, widened to fp32.  The pointer advances one
+// row per load (the empty asm keeps the compiler from holding gs addresses).
+template <int GS>
+__device__ __forceinline__ void load_column(const uint16_t *__restrict__ W, int64_t cols, int64_t line,
+                                            int64_t eg, float (&w)[GS])
+{
+    const uint16_t *q = W + eg * cols + line;
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+        w[i] = half_bits_to_float(__builtin_nontemporal_load(q));
+        q += cols;
+        asm volatile("" : "+v"(q));
+    }
+}
+
+// Load one group (gs fp16 values) directly from global memory and widen
+// exactly to fp32.
+template <int GS, int AXIS>
+__device__ __forceinline__ void load_group(const uint16_t *__restrict__ W, int64_t cols,
+                                           int64_t line, int64_t e0, float (&w)[GS])
+{
+    if constexpr (AXIS == 1) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(W + line * cols + e0);
+#pragma unroll
+        for (int j = 0; j < GS / 8; ++j) {
+            u32x4 v = __builtin_nontemporal_load(src + j);
+            _Float16 h[8];
+            __builtin_memcpy(h, &v, 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[j * 8 + i] = (float)h[i];
+        }
+    } else {
+        load_column<GS>(W, cols, line, e0, w);
+    }
 }
 
 // Exact sum of the group's weights: fp16 values are multiples of 2^-24 below
@@ -317,49 +332,47 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
     }
 }
 
-// Occupancy target per group size: the resident group (gs fp32 VGPRs) plus
-// the loop state must fit without spills.
-constexpr int waves_per_simd(int gs) { return gs <= 8 ? 8 : gs == 16 ? 6 : gs == 32 ? 6 : gs == 64 ? 4 : gs == 128 ? 2 : 1; }
+// Occupancy target (waves per SIMD): the largest at which the kernel needs
+// no scratch.  A spill reload is a vector memory load, and the in-order
+// vmcnt would make it wait for the DMA of the next group as well.
+constexpr int waves_per_simd(int nb, int gs)
+{
+    return nb == 3 ? (gs <= 8 ? 4 : gs <= 32 ? 3 : 2) : (gs <= 32 ? 4 : gs == 64 ? 3 : gs == 128 ? 2 : 1);
+}
 
 template <int NB, int GS, int G, int AXIS, int WPB>
 __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor &T,
-                                          WaveFinish<GS> &wf, bool valid,
-                                          int64_t line, int64_t eg, uint32_t (&words)[WPB])
+                                          WaveFinish<GS> &wf, bool valid, int64_t line, int64_t eg,
+                                          const float (&w)[GS], uint32_t (&words)[WPB],
+                                          float &s_out, float &z_out)
 {
     constexpr float QMAX = (float)((1 << NB) - 1);
     constexpr double INV_GS = 1.0 / GS;
-    float w[GS];
-    float mn = 0.0f, mx = 0.0f, s = 1.0f, z = 0.0f, amag = 0.0f;
-    double sw = 0.0;
-    if (valid) {
-        load_group<GS, AXIS>(T.W, T.cols, line, eg, w);
-        mn = w[0];
-        mx = w[0];
+    // Lanes without a valid group hold in-bounds weights (staged from the
+    // item's first group) and run the set-up on them; they never enter the
+    // loop and their results are not stored.
+    float mn = w[0], mx = w[0];
 #pragma unroll
-        for (int i = 1; i < GS; ++i) {
-            mn = fminf(mn, w[i]);
-            mx = fmaxf(mx, w[i]);
-        }
-        const float rng = mx - mn;
-        if (rng == 0.0f) {
-            s = 1.0f;
-            z = -mn;
-        } else {
-            s = QMAX / rng;
-            z = -(mn * s);
-        }
-        sw = exact_sum<GS>(w);
-        amag = fmaxf(fabsf(mn), fabsf(mx));
-    } else {
-#pragma unroll
-        for (int i = 0; i < GS; ++i)
-            w[i] = 0.0f;
+    for (int i = 1; i < GS; ++i) {
+        mn = fminf(mn, w[i]);
+        mx = fmaxf(mx, w[i]);
     }
+    float s, z;
+    const float rng = mx - mn;
+    if (rng == 0.0f) {
+        s = 1.0f;
+        z = -mn;
+    } else {
+        s = QMAX / rng;
+        z = -(mn * s);
+    }
+    const double sw = exact_sum<GS>(w);
+    const float amag = fmaxf(fabsf(mn), fabsf(mx));
     const float thr_s = a.thr * s;
     const float lim = a.thr_m * s;
 
     // fast loop; a lane freezes its group at the first iteration whose
-    // certificate fails
+    // certificate fails, and stops early once its zero is a fixed point
     bool run = valid, frozen = false;
     float beta = a.beta0, beta_f = a.beta0;
     int it_f = a.iters;
@@ -402,7 +415,15 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
                 a1 = __builtin_amdgcn_sad_u8(d1, QB, a1);
             }
             const uint32_t sq = ((c0 + c1) + (uint32_t)(GS * ((1 << NB) - 1)) - (a0 + a1)) >> 1;
-            z = (float)(((double)sq - (double)s * sw) * INV_GS);
+            const float zn = (float)(((double)sq - (double)s * sw) * INV_GS);
+            // Fixed point: the next zero depends on the current one only
+            // through the codes, which are equal for equal zeros (+0 and -0
+            // included), and the certificate is the same for every remaining
+            // iteration; so every later iteration returns zn again, bit for
+            // bit, and the group is done.
+            if (zn == z)
+                run = false;
+            z = zn;
         }
         beta = beta * a.kappa;
     }
@@ -416,73 +437,150 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
             pack_codes<NB, GS, G>(w2, s, z, words);
         }
     }
-    if (valid) {
-        const int64_t L = AXIS == 1 ? T.cols : T.rows;
-        const int64_t gi = AXIS == 1 ? line * (L / GS) + eg / GS : (eg / GS) * T.cols + line;
-        T.scale[gi] = s;
-        T.zero[gi] = z;
-    }
+    s_out = s;
+    z_out = z;
 }
 
-template <int NB, int GS, int AXIS, int G, int GSEQ, int WPB>
-__device__ __forceinline__ void solve_seq(const SolveArgs &a, const SolveTensor &T,
-                                          WaveFinish<GS> &wf, int ng,
-                                          int64_t line, int64_t e0, uint32_t (&words)[WPB])
-{
-    if constexpr (G < GSEQ) {
-        solve_one<NB, GS, G, AXIS>(a, T, wf, G < ng, line, e0 + (int64_t)G * GS, words);
-        solve_seq<NB, GS, AXIS, G + 1, GSEQ>(a, T, wf, ng, line, e0, words);
-    }
-}
+// Shape of the work item of a kernel: lcm(gs, C) consecutive elements of a
+// line, so that whole words belong to one lane.
+template <int NB, int GS, int AXIS>
+struct Item {
+    static constexpr int C = codes_per_word(NB);
+    static constexpr int LB = lcm_c(GS, C);      // elements per work item
+    static constexpr int GSEQ = LB / GS;         // groups per work item
+    static constexpr int WPB = LB / C;           // words per work item
+};
+
+// Where a work item lies: its line, first element and valid groups.
+struct ItemPos {
+    int64_t line, e0;
+    int ng;
+};
 
 template <int NB, int GS, int AXIS>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(waves_per_simd(GS))))
-void solve_kernel(SolveArgs a)
+__device__ __forceinline__ ItemPos item_pos(const SolveTensor &T, int64_t item)
 {
-    constexpr int C = codes_per_word(NB);
-    constexpr int LB = lcm_c(GS, C);      // elements per work item
-    constexpr int GSEQ = LB / GS;         // groups per work item
-    constexpr int WPB = LB / C;           // words per work item
-    __shared__ WaveFinish<GS> finish[kWaves];
-
-    // the launch's tensor of this workgroup (tensors start on workgroup
-    // boundaries, so the search is uniform)
-    int ti = 0;
-    while (ti + 1 < a.n && (int64_t)blockIdx.x >= a.t[ti + 1].block0)
-        ++ti;
-    const SolveTensor &T = a.t[ti];
-    // every lane stays to the end: lanes past the last work item own no group
-    // but take part in the wave's finish phases
-    const int64_t item = ((int64_t)blockIdx.x - T.block0) * blockDim.x + threadIdx.x;
+    using I = Item<NB, GS, AXIS>;
     const bool live = item < T.n_items;
     const int64_t it_c = live ? item : 0;
-    int64_t line, blk;
+    ItemPos p;
+    int64_t blk;
     if constexpr (AXIS == 1) {
-        line = it_c / T.nblk;
-        blk = it_c - line * T.nblk;
+        p.line = it_c / T.nblk;
+        blk = it_c - p.line * T.nblk;
     } else {
         blk = it_c / T.cols;
-        line = it_c - blk * T.cols;
+        p.line = it_c - blk * T.cols;
     }
     const int64_t L = AXIS == 1 ? T.cols : T.rows;
-    const int64_t e0 = blk * LB;
-    const int64_t rem = (L - e0) / GS;
-    const int ng = live ? (rem < GSEQ ? (int)rem : GSEQ) : 0;   // valid groups of this item
-    const int64_t words_per_line = (L + C - 1) / C;
-    const int64_t k0 = e0 / C;
+    p.e0 = blk * I::LB;
+    const int64_t rem = (L - p.e0) / GS;
+    p.ng = live ? (rem < I::GSEQ ? (int)rem : I::GSEQ) : 0;
+    return p;
+}
 
-    uint32_t words[WPB];
+// Staging of one group per wave in LDS, filled by DMA one group ahead:
+// gs rows of 64 lanes x 2 bytes (row i of lane l at [i][l]).  axis = 1: lane
+// l's group is gs consecutive halves, fetched as gs/8 16-byte chunks
+// (global_load_lds_dwordx4 puts lane l's 16 bytes at base + 16 l, so chunk j
+// of lane l lands at [8j..8j+7][l] read as 16-byte rows).  axis = 0: lane l's
+// group is column line_l of rows eg..eg+gs-1; when the wave's 64 columns are
+// consecutive and 16-byte aligned (cols % 64 == 0), 8 lanes fetch one row's
+// 128 bytes, so a 16-byte DMA moves 8 rows and the data lands row-major.
+// Other axis = 0 shapes are read directly from global memory when the group
+// is solved (a sub-dword DMA gives every lane a whole dword, which would
+// double the staging area).  Every address is inside the tensor.
+template <int GS, int AXIS>
+struct Stage {
+    u32x4 v[GS / 8][64];
+};
+
+template <int GS, int AXIS>
+__device__ __forceinline__ void stage_group(const SolveTensor &T, int64_t line, int64_t eg, bool rows64,
+                                            Stage<GS, AXIS> &st)
+{
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    const int lane = (int)(threadIdx.x & 63);
+    if constexpr (AXIS == 1) {
+        const uint16_t *src = T.W + line * T.cols + eg;
 #pragma unroll
-    for (int k = 0; k < WPB; ++k)
-        words[k] = 0;
-    solve_seq<NB, GS, AXIS, 0, GSEQ>(a, T, finish[threadIdx.x / 64], ng, line, e0, words);
+        for (int j = 0; j < GS / 8; ++j)
+            __builtin_amdgcn_global_load_lds(src + 8 * j, (lds_ptr)&st.v[j][0], 16, 0, 0);
+    } else {
+        if (rows64) {
+            const int64_t c0 = line - lane;                  // the wave's first column
+            const uint16_t *src = T.W + (eg + (lane >> 3)) * T.cols + c0 + 8 * (lane & 7);
+            const int64_t step = 8 * T.cols;
+#pragma unroll
+            for (int j = 0; j < GS / 8; ++j)
+                __builtin_amdgcn_global_load_lds(src + j * step, (lds_ptr)&st.v[j][0], 16, 0, 0);
+        }
+    }
+}
+
+// Read this lane's staged group (or, for axis = 0 shapes that are not
+// staged, load it) and widen it exactly to fp32.
+template <int GS, int AXIS>
+__device__ __forceinline__ void read_group(const Stage<GS, AXIS> &st, const SolveTensor &T, int64_t line,
+                                           int64_t eg, bool rows64, float (&w)[GS])
+{
+    const int lane = (int)(threadIdx.x & 63);
+    if constexpr (AXIS == 1) {
+#pragma unroll
+        for (int j = 0; j < GS / 8; ++j) {
+            const u32x4 v = st.v[j][lane];
+            _Float16 h[8];
+            __builtin_memcpy(h, &v, 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[8 * j + i] = (float)h[i];
+        }
+    } else {
+        if (rows64) {
+            const uint16_t(*rows)[64] = reinterpret_cast<const uint16_t(*)[64]>(&st.v[0][0]);
+#pragma unroll
+            for (int i = 0; i < GS; ++i)
+                w[i] = half_bits_to_float(rows[i][lane]);
+        } else {
+            load_column<GS>(T.W, T.cols, line, eg, w);
+        }
+    }
+    // The group stays resident as fp32 only: without this the compiler keeps
+    // the fp16 originals alive too (to fold the widening into later fmas),
+    // which doubles the group's registers.
+#pragma unroll
+    for (int i = 0; i < GS; ++i)
+        asm volatile("" : "+v"(w[i]));
+}
+
+// Write a finished work item: packed words, then scale and zero per group.
+template <int NB, int GS, int AXIS>
+__device__ __forceinline__ void store_item(const SolveTensor &T, const ItemPos &p,
+                                           const uint32_t (&words)[Item<NB, GS, AXIS>::WPB],
+                                           const float (&sv)[Item<NB, GS, AXIS>::GSEQ],
+                                           const float (&zv)[Item<NB, GS, AXIS>::GSEQ])
+{
+    using I = Item<NB, GS, AXIS>;
+    constexpr int C = I::C, WPB = I::WPB;
+    const int64_t L = AXIS == 1 ? T.cols : T.rows;
+    const int64_t words_per_line = (L + C - 1) / C;
+    const int64_t k0 = p.e0 / C;
+#pragma unroll
+    for (int g = 0; g < I::GSEQ; ++g) {
+        if (g < p.ng) {
+            const int64_t eg = p.e0 + (int64_t)g * GS;
+            const int64_t gi = AXIS == 1 ? p.line * (L / GS) + eg / GS : (eg / GS) * T.cols + p.line;
+            T.scale[gi] = sv[g];
+            T.zero[gi] = zv[g];
+        }
+    }
     // Words go out through L2 (ordinary stores) so that lanes' partial lines
     // merge before reaching HBM.  axis = 1: a lane's words are contiguous and
     // leave as 16-byte stores when the row pitch allows; axis = 0: each word
     // store of the wave covers 64 consecutive columns.
     if constexpr (AXIS == 1 && WPB % 4 == 0) {
-        if ((words_per_line & 3) == 0 && ng == GSEQ) {
-            u32x4 *dst = reinterpret_cast<u32x4 *>(T.packed + line * words_per_line + k0);
+        if ((words_per_line & 3) == 0 && p.ng == I::GSEQ) {
+            u32x4 *dst = reinterpret_cast<u32x4 *>(T.packed + p.line * words_per_line + k0);
 #pragma unroll
             for (int k = 0; k < WPB / 4; ++k)
                 dst[k] = u32x4{words[4 * k], words[4 * k + 1], words[4 * k + 2], words[4 * k + 3]};
@@ -491,11 +589,88 @@ void solve_kernel(SolveArgs a)
     }
 #pragma unroll
     for (int k = 0; k < WPB; ++k) {
-        if (k * C < ng * GS && k0 + k < words_per_line) {
-            const int64_t addr = AXIS == 1 ? line * words_per_line + k0 + k
-                                           : (k0 + k) * T.cols + line;
+        if (k * C < p.ng * GS && k0 + k < words_per_line) {
+            const int64_t addr = AXIS == 1 ? p.line * words_per_line + k0 + k : (k0 + k) * T.cols + p.line;
             T.packed[addr] = words[k];
         }
+    }
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
+
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, F, I + 1>(static_cast<F &&>(f));
+    }
+}
+
+// A workgroup owns depth * 256 consecutive work items of one tensor; at step m
+// lane l of the workgroup takes item base + 256 m + l and solves its groups
+// in order.  Per group: wait for its DMA, read it into registers, start the
+// DMA of the lane's next group, solve the group; a finished item is stored.
+// The loads of a group thus overlap the solve of the one before.
+template <int NB, int GS, int AXIS>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NB, GS))))
+void solve_kernel(SolveArgs a)
+{
+    using I = Item<NB, GS, AXIS>;
+    constexpr int GSEQ = I::GSEQ, WPB = I::WPB;
+    __shared__ WaveFinish<GS> finish[kWaves];
+    __shared__ Stage<GS, AXIS> stage[kWaves];
+
+    // the launch's tensor of this workgroup: block0 is increasing and
+    // tensors start on workgroup boundaries (uniform, no dependent loads)
+    int ti = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxBatch; ++j)
+        ti += (j < a.n && (int64_t)blockIdx.x >= a.block0[j]) ? 1 : 0;
+    const SolveTensor &T = a.t[ti];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    Stage<GS, AXIS> &st = stage[wave];
+    WaveFinish<GS> &wf = finish[wave];
+    const int64_t first = ((int64_t)blockIdx.x - a.block0[ti]) * kBlock * a.depth + threadIdx.x;
+    const int64_t wave_first = first - (threadIdx.x & 63);
+    // axis = 0 waves cover 64 consecutive, 16-byte aligned columns of one
+    // row block exactly when cols % 64 == 0 (items start at multiples of 64)
+    const bool rows64 = AXIS == 0 && (T.cols & 63) == 0;
+
+    // first element of group G of item q, or of the item's first group when
+    // G is not valid (always inside the tensor)
+    auto group_e = [](const ItemPos &q, int G) { return q.e0 + (int64_t)(G < q.ng ? G : 0) * GS; };
+    auto stage_of = [&](const ItemPos &q, int G) { stage_group<GS, AXIS>(T, q.line, group_e(q, G), rows64, st); };
+    if (wave_first < T.n_items)
+        stage_of(item_pos<NB, GS, AXIS>(T, first), 0);
+    for (int m = 0; m < a.depth; ++m) {
+        // every lane of a wave with work stays to the end of the step: lanes
+        // past the last item own no group but take part in the finish phases
+        if (wave_first + (int64_t)m * kBlock >= T.n_items)
+            break;
+        const ItemPos p = item_pos<NB, GS, AXIS>(T, first + (int64_t)m * kBlock);
+        const bool more = m + 1 < a.depth && wave_first + (int64_t)(m + 1) * kBlock < T.n_items;
+        uint32_t words[WPB];
+#pragma unroll
+        for (int k = 0; k < WPB; ++k)
+            words[k] = 0;
+        float sv[GSEQ], zv[GSEQ];
+        static_for<GSEQ>([&](auto Gc) {
+            constexpr int G = decltype(Gc)::value;
+            float w[GS];
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            read_group<GS, AXIS>(st, T, p.line, group_e(p, G), rows64, w);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            if constexpr (G + 1 < GSEQ)
+                stage_of(p, G + 1);
+            else if (more)
+                stage_of(item_pos<NB, GS, AXIS>(T, first + (int64_t)(m + 1) * kBlock), 0);
+            solve_one<NB, GS, G, AXIS>(a, T, wf, G < p.ng, p.line, p.e0 + (int64_t)G * GS, w, words,
+                                       sv[G], zv[G]);
+        });
+        store_item<NB, GS, AXIS>(T, p, words, sv, zv);
     }
 }
 
