@@ -189,14 +189,17 @@ def main():
             chunks[-1][1].append(i)
         else:
             chunks.append((fmt, [i]))
-    calls = [(fmt, [(ins[i], *outs[i]) for i in idx], sum(tensors[i]["rows"] * tensors[i]["cols"] for i in idx))
+    # the descriptor arrays are marshalled once (host metadata only); a step
+    # is then one C-ABI call per launch
+    calls = [(fmt, hq.QuantizeBatch([(ins[i], *outs[i]) for i in idx], *fmt, iters=args.iters),
+              sum(tensors[i]["rows"] * tensors[i]["cols"] for i in idx))
              for fmt, idx in chunks]
 
     def step(events=None):
-        for j, ((nb_, gs_, ax_), items, _) in enumerate(calls):
+        for j, (_, batch, _) in enumerate(calls):
             if events is not None:
                 events[j][0].record()
-            hq.hqq_quantize_batch(items, nb_, gs_, ax_, iters=args.iters)
+            batch.run()
             if events is not None:
                 events[j][1].record()
 

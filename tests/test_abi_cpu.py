@@ -137,3 +137,19 @@ def test_product_does_not_touch_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_binding_batch_validates_before_any_call(lib):
+    """QuantizeBatch marshals once and rejects host tensors and wrong dtypes
+    while building its descriptor array (no HIP call is made)."""
+    import torch
+
+    import weight_quantization_group_amd as w
+
+    W = torch.zeros((64, 128), dtype=torch.float16)
+    pk = torch.zeros((64, 16), dtype=torch.int32)
+    sc = torch.zeros((64, 2), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        w.QuantizeBatch([(W, pk, sc, sc)], 4, 64, 1)
+    with pytest.raises(TypeError):
+        w.hqq_quantize_batch([(W.float(), pk, sc, sc)], 4, 64, 1)

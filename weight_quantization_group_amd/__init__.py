@@ -141,24 +141,43 @@ def hqq_quantize(W: torch.Tensor, nbits: int, group_size: int, axis: int,
     return packed, scale, zero
 
 
+class QuantizeBatch:
+    """Several same-format tensors for hqq_quantize_batch, validated and
+    marshalled into the C descriptor array once; run() is then a single
+    C-ABI call (one launch per 24 tensors) on the current stream.
+    items: list of (W, packed, scale, zero) CUDA tensors (outputs
+    preallocated); the tensors are kept alive by the object."""
+
+    def __init__(self, items, nbits: int, group_size: int, axis: int,
+                 iters: int = ITERS_DEFAULT, p: float = P_DEFAULT,
+                 beta0: float = BETA0_DEFAULT, kappa: float = KAPPA_DEFAULT):
+        self._lib = load_library()
+        self._items = [tuple(it) for it in items]
+        n = len(self._items)
+        self._arr = (HqqTensor * max(n, 1))()
+        for i, (W, pk, sc, ze) in enumerate(self._items):
+            rows, cols = W.shape
+            self._arr[i] = HqqTensor(_dev_ptr(W, "W", _F16).value, rows, cols,
+                                     _dev_ptr(pk, "packed", _U32).value,
+                                     _dev_ptr(sc, "scale", (torch.float32,)).value,
+                                     _dev_ptr(ze, "zero", (torch.float32,)).value)
+        self._n = n
+        self._ptr = ctypes.cast(self._arr, ctypes.c_void_p)
+        self._dev = self._items[0][0].device if n else torch.device("cuda", torch.cuda.current_device())
+        self._args = (nbits, group_size, axis, iters, p, beta0, kappa)
+
+    def run(self):
+        st = self._lib.hqq_quantize_batch(self._ptr, self._n, *self._args, _stream(self._dev))
+        if st != 0:
+            raise HQQError("hqq_quantize_batch", st)
+
+
 def hqq_quantize_batch(items, nbits: int, group_size: int, axis: int,
                        iters: int = ITERS_DEFAULT, p: float = P_DEFAULT,
                        beta0: float = BETA0_DEFAULT, kappa: float = KAPPA_DEFAULT):
     """Quantize several same-format tensors in as few launches as possible.
     items: list of (W, packed, scale, zero) CUDA tensors (outputs preallocated)."""
-    L = load_library()
-    n = len(items)
-    arr = (HqqTensor * max(n, 1))()
-    for i, (W, pk, sc, ze) in enumerate(items):
-        rows, cols = W.shape
-        arr[i] = HqqTensor(_dev_ptr(W, "W", _F16).value, rows, cols,
-                           _dev_ptr(pk, "packed", _U32).value, _dev_ptr(sc, "scale", (torch.float32,)).value,
-                           _dev_ptr(ze, "zero", (torch.float32,)).value)
-    dev = items[0][0].device if n else torch.device("cuda", torch.cuda.current_device())
-    st = L.hqq_quantize_batch(ctypes.cast(arr, ctypes.c_void_p), n, nbits, group_size, axis, iters,
-                              p, beta0, kappa, _stream(dev))
-    if st != 0:
-        raise HQQError("hqq_quantize_batch", st)
+    QuantizeBatch(items, nbits, group_size, axis, iters, p, beta0, kappa).run()
 
 
 def hqq_dequantize(packed, scale, zero, rows: int, cols: int, nbits: int, group_size: int,
