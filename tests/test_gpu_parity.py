@@ -327,3 +327,15 @@ def test_70b_stack_sampled(hq, oracle_mod):
         if t["layer"] in (0, 79):
             st = _sampled_parity(hq, oracle_mod, t, 16 if t["name"] in ("gate", "up") else 32)
             print("70b", t["layer"], t["name"], st)
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])
+@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1)])
+def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters):
+    """Groups that stop before, at and after the point where the solve parks
+    unfinished groups for later batches, and long runs, match the oracle."""
+    rng = np.random.RandomState(iters * 100 + nbits * 10 + gs + axis)
+    shape = (96, 1024) if axis == 1 else (1024, 96)
+    W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.001)
+    g = gpu_quantize(hq, W16, nbits, gs, axis, iters=iters)
+    check_parity(oracle_mod, W16, nbits, gs, axis, *g, tag=f"{nbits}b g{gs} ax{axis} it{iters}", iters=iters)

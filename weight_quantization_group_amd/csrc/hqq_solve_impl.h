@@ -318,9 +318,12 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
             }
             const float zn = (float)(((double)sq - (double)gs_s * (st.sw - se)) * INV_GS);
             if (act) {
+                // where the certificate holds every W_e is 0 and the update is
+                // the fast one: a returned zero is then a fixed point
+                const bool fixed = !cand && zn == gz;
                 gz = zn;
                 gbeta = gbeta * a.kappa;
-                ++it;
+                it = fixed ? a.iters : it + 1;
             }
         }
         if (ok && pos == 0)
@@ -340,58 +343,73 @@ constexpr int waves_per_simd(int nb, int gs)
     return nb == 3 ? (gs <= 8 ? 4 : gs <= 32 ? 3 : 2) : (gs <= 32 ? 4 : gs == 64 ? 3 : gs == 128 ? 2 : 1);
 }
 
-template <int NB, int GS, int G, int AXIS, int WPB>
-__device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor &T,
-                                          WaveFinish<GS> &wf, bool valid, int64_t line, int64_t eg,
-                                          const float (&w)[GS], uint32_t (&words)[WPB],
-                                          float &s_out, float &z_out)
+// Per-group set-up: min, max, scale, initial zero, exact sum of the weights.
+struct GroupInit {
+    float mn, mx, s, z, amag;
+    double sw;
+};
+
+template <int NB, int GS>
+__device__ __forceinline__ GroupInit group_init(const float (&w)[GS])
+{
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    GroupInit g;
+    g.mn = w[0];
+    g.mx = w[0];
+#pragma unroll
+    for (int i = 1; i < GS; ++i) {
+        g.mn = fminf(g.mn, w[i]);
+        g.mx = fmaxf(g.mx, w[i]);
+    }
+    const float rng = g.mx - g.mn;
+    if (rng == 0.0f) {
+        g.s = 1.0f;
+        g.z = -g.mn;
+    } else {
+        g.s = QMAX / rng;
+        g.z = -(g.mn * g.s);
+    }
+    g.sw = exact_sum<GS>(w);
+    g.amag = fmaxf(fabsf(g.mn), fabsf(g.mx));
+    return g;
+}
+
+// Where a lane's group stands in the fast loop.
+struct LaneRun {
+    float z;        // current zero
+    float beta;     // beta of iteration `it`
+    int it;         // next iteration
+    bool run;       // still iterating
+    bool frozen;    // certificate failed at iteration it (beta is its beta)
+};
+
+// Fast iterations of the lanes with r.run, up to iters: a lane freezes its
+// group at the first iteration whose certificate fails, and stops once its
+// zero is a fixed point (r.it = iters then).
+template <int NB, int GS>
+__device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[GS], const GroupInit &g,
+                                           LaneRun &r)
 {
     constexpr float QMAX = (float)((1 << NB) - 1);
     constexpr double INV_GS = 1.0 / GS;
-    // Lanes without a valid group hold in-bounds weights (staged from the
-    // item's first group) and run the set-up on them; they never enter the
-    // loop and their results are not stored.
-    float mn = w[0], mx = w[0];
-#pragma unroll
-    for (int i = 1; i < GS; ++i) {
-        mn = fminf(mn, w[i]);
-        mx = fmaxf(mx, w[i]);
-    }
-    float s, z;
-    const float rng = mx - mn;
-    if (rng == 0.0f) {
-        s = 1.0f;
-        z = -mn;
-    } else {
-        s = QMAX / rng;
-        z = -(mn * s);
-    }
-    const double sw = exact_sum<GS>(w);
-    const float amag = fmaxf(fabsf(mn), fabsf(mx));
+    const float s = g.s;
     const float thr_s = a.thr * s;
     const float lim = a.thr_m * s;
-
-    // fast loop; a lane freezes its group at the first iteration whose
-    // certificate fails, and stops early once its zero is a fixed point
-    bool run = valid, frozen = false;
-    float beta = a.beta0, beta_f = a.beta0;
-    int it_f = a.iters;
-    for (int it = 0; it < a.iters; ++it) {
-        if (!__any(run))
-            break;
-        if (run) {
-            const float tmin = __builtin_fmaf(mn, s, z);
-            const float tmax = __builtin_fmaf(mx, s, z);
+    const double ssw = (double)s * g.sw;
+    if (a.iters == 0)
+        r.run = false;
+    while (__any(r.run)) {
+        if (r.run) {
+            const float tmin = __builtin_fmaf(g.mn, s, r.z);
+            const float tmax = __builtin_fmaf(g.mx, s, r.z);
             const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
-            const bool est_ok = __builtin_fmaf(amag, s, fabsf(z)) + QMAX <= lim;
+            const bool est_ok = __builtin_fmaf(g.amag, s, fabsf(r.z)) + QMAX <= lim;
             if (!(est_ok && bound <= thr_s)) {
-                run = false;
-                frozen = true;
-                it_f = it;
-                beta_f = beta;
+                r.run = false;
+                r.frozen = true;
             }
         }
-        if (run) {
+        if (r.run) {
             // W_q and sum W_q.  v_cvt_pk_u8_f32 rounds half to even and
             // saturates to [0, 255] (the clamp at 0), four codes to a word;
             // v_sad_u8 against 0 adds a word's four codes c, against qmax in
@@ -399,6 +417,7 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
             // (c + qmax - |c - qmax|) / 2: 2.5 VALU ops per weight.
             static_assert(GS % 8 == 0, "two byte-sum chains of whole words");
             constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
+            const float z = r.z;
             uint32_t c0 = 0, c1 = 0, a0 = 0, a1 = 0;
 #pragma unroll
             for (int k = 0; k < GS / 4; k += 2) {
@@ -415,30 +434,55 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
                 a1 = __builtin_amdgcn_sad_u8(d1, QB, a1);
             }
             const uint32_t sq = ((c0 + c1) + (uint32_t)(GS * ((1 << NB) - 1)) - (a0 + a1)) >> 1;
-            const float zn = (float)(((double)sq - (double)s * sw) * INV_GS);
+            const float zn = (float)(((double)sq - ssw) * INV_GS);
             // Fixed point: the next zero depends on the current one only
             // through the codes, which are equal for equal zeros (+0 and -0
             // included), and the certificate is the same for every remaining
             // iteration; so every later iteration returns zn again, bit for
             // bit, and the group is done.
-            if (zn == z)
-                run = false;
-            z = zn;
+            r.it = zn == z ? a.iters : r.it + 1;
+            r.beta = r.beta * a.kappa;
+            r.z = zn;
+            if (r.it >= a.iters)
+                r.run = false;
         }
-        beta = beta * a.kappa;
     }
-    if (valid && !frozen)
-        pack_codes<NB, GS, G>(w, s, z, words);
-    if (__any(frozen)) {
-        finish_frozen<NB, GS>(a, wf, frozen, w, s, z, beta_f, mn, mx, amag, it_f, sw);
-        if (frozen) {
+}
+
+// Finish: frozen lanes complete their iterations together (one lane per
+// element); then every valid lane packs its final codes.
+template <int NB, int GS, int G, int AXIS, int WPB>
+__device__ __forceinline__ void finish_group(const SolveArgs &a, const SolveTensor &T, WaveFinish<GS> &wf,
+                                             bool valid, int64_t line, int64_t eg, const float (&w)[GS],
+                                             const GroupInit &g, LaneRun &r, uint32_t (&words)[WPB])
+{
+    if (valid && !r.frozen)
+        pack_codes<NB, GS, G>(w, g.s, r.z, words);
+    if (__any(r.frozen)) {
+        finish_frozen<NB, GS>(a, wf, r.frozen, w, g.s, r.z, r.beta, g.mn, g.mx, g.amag, r.it, g.sw);
+        if (r.frozen) {
             float w2[GS];
             load_group<GS, AXIS>(T.W, T.cols, line, eg, w2);
-            pack_codes<NB, GS, G>(w2, s, z, words);
+            pack_codes<NB, GS, G>(w2, g.s, r.z, words);
         }
     }
-    s_out = s;
-    z_out = z;
+}
+
+template <int NB, int GS, int G, int AXIS, int WPB>
+__device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor &T,
+                                          WaveFinish<GS> &wf, bool valid, int64_t line, int64_t eg,
+                                          const float (&w)[GS], uint32_t (&words)[WPB],
+                                          float &s_out, float &z_out)
+{
+    // Lanes without a valid group hold in-bounds weights (staged from the
+    // item's first group) and run the set-up on them; they never enter the
+    // loop and their results are not stored.
+    const GroupInit g = group_init<NB, GS>(w);
+    LaneRun r{g.z, a.beta0, 0, valid, false};
+    fast_iters<NB, GS>(a, w, g, r);
+    finish_group<NB, GS, G, AXIS>(a, T, wf, valid, line, eg, w, g, r, words);
+    s_out = g.s;
+    z_out = r.z;
 }
 
 // Shape of the work item of a kernel: lcm(gs, C) consecutive elements of a
@@ -674,18 +718,24 @@ void solve_kernel(SolveArgs a)
     }
 }
 
+template <int NB, int GS, int AXIS>
+void launch_one(dim3 grid, dim3 block, const SolveArgs &a, hipStream_t st)
+{
+    hipLaunchKernelGGL((solve_kernel<NB, GS, AXIS>), grid, block, 0, st, a);
+}
+
 template <int NB, int AXIS>
 hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 {
     const dim3 block(kBlock);
     const dim3 grid((unsigned)a.blocks);
     switch (group_size) {
-    case 8: hipLaunchKernelGGL((solve_kernel<NB, 8, AXIS>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((solve_kernel<NB, 16, AXIS>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((solve_kernel<NB, 32, AXIS>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((solve_kernel<NB, 64, AXIS>), grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL((solve_kernel<NB, 128, AXIS>), grid, block, 0, st, a); break;
-    case 256: hipLaunchKernelGGL((solve_kernel<NB, 256, AXIS>), grid, block, 0, st, a); break;
+    case 8: launch_one<NB, 8, AXIS>(grid, block, a, st); break;
+    case 16: launch_one<NB, 16, AXIS>(grid, block, a, st); break;
+    case 32: launch_one<NB, 32, AXIS>(grid, block, a, st); break;
+    case 64: launch_one<NB, 64, AXIS>(grid, block, a, st); break;
+    case 128: launch_one<NB, 128, AXIS>(grid, block, a, st); break;
+    case 256: launch_one<NB, 256, AXIS>(grid, block, a, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
