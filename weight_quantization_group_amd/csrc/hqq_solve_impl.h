@@ -140,7 +140,10 @@ __device__ __forceinline__ double exact_sum(const float (&w)[GS])
 // significand m in [sqrt(1/2), sqrt(2)) (the atanh power series to u^21);
 // exp by reduction y = j ln2 + r, |r| <= ln2/2, and its Taylor polynomial to
 // r^13.  Relative error ~1e-15, far below the fp32 rounding it feeds.
-__device__ __forceinline__ float pow_rounded(float xf, float pm1f)
+// Kept out of line: it runs only for the residuals of frozen groups, and
+// inlined its fp64 temporaries would set the register budget of the whole
+// kernel (149 VGPRs instead of 121 at gs = 64).
+__device__ __attribute__((noinline)) float pow_rounded(float xf, float pm1f)
 {
     int e;
     double m = frexp((double)xf, &e);
@@ -340,7 +343,9 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
 // vmcnt would make it wait for the DMA of the next group as well.
 constexpr int waves_per_simd(int nb, int gs)
 {
-    return nb == 3 ? (gs <= 8 ? 4 : gs <= 32 ? 3 : 2) : (gs <= 32 ? 4 : gs == 64 ? 3 : gs == 128 ? 2 : 1);
+    return nb == 3   ? (gs == 8 ? 5 : gs <= 32 ? 4 : gs == 64 ? 3 : 1)
+           : nb == 1 && gs == 8 ? 5
+                              : (gs <= 16 ? 6 : gs == 32 ? 5 : gs == 64 ? 4 : gs == 128 ? 2 : 1);
 }
 
 // Per-group set-up: min, max, scale, initial zero, exact sum of the weights.
