@@ -210,10 +210,28 @@ struct FrozenGroup {   // state of a frozen group handed to the finish phase
     double sw;
 };
 
+// Compact mode of the fast loop (32 <= gs <= 128): once at most B groups of a
+// wave still iterate, they are spread over SEG = gs/8 lanes each (8 elements
+// per lane) and the wave advances all of them in one pass per iteration.
+template <int GS>
+struct Compact {
+    static constexpr bool ON = GS >= 32 && GS <= 128;
+    static constexpr int SEG = ON ? GS / 8 : 1;
+    static constexpr int B = 64 / SEG;
+};
+
+struct CompactGroup {   // a group in compact mode: LaneRun and GroupInit fields
+    float s, z, mn, mx, amag, beta;
+    int it, frozen;
+    double sw;
+};
+
 template <int GS>
 struct WaveFinish {
     uint16_t w[64 * Finish<GS>::EPL];    // B groups x GS fp16 weights
     FrozenGroup g[Finish<GS>::B];
+    u32x4 cw[Compact<GS>::ON ? 64 : 1];                       // slot b, chunk j at [b SEG + j]
+    CompactGroup cg[Compact<GS>::ON ? Compact<GS>::B : 1];
 };
 
 // Pack a group's final codes (small integers held in fp32) into the work item's words.
@@ -388,12 +406,126 @@ struct LaneRun {
     bool frozen;    // certificate failed at iteration it (beta is its beta)
 };
 
+// Sum over the SEG lanes of a compact group (aligned blocks of 4, 8 or 16
+// lanes) with DPP row permutations; every lane gets the total.
+template <int SEG>
+__device__ __forceinline__ int seg_sum(int v)
+{
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
+    if constexpr (SEG >= 8)
+        v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);     // row_half_mirror
+    if constexpr (SEG >= 16)
+        v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);     // row_mirror
+    return v;
+}
+
+// Compact mode: the running lanes' groups (at most B) move to LDS, SEG lanes
+// per group iterate them with the same update as the fast loop (codes by
+// v_cvt_pk_u8_f32, sums by v_sad_u8, the lanes' partial sums added exactly),
+// and the owners take back zero, iteration, beta and frozen.
+template <int NB, int GS>
+__device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS> &wf, const float (&w)[GS],
+                                           const GroupInit &g, LaneRun &r)
+{
+    using K = Compact<GS>;
+    constexpr double INV_GS = 1.0 / GS;
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
+    const uint32_t lane = __lane_id();
+    const uint64_t run_m = __ballot(r.run);
+    const int nrun = __popcll(run_m);
+    const int mine = __popcll(run_m & ((1ull << lane) - 1ull));
+    if (r.run) {
+#pragma unroll
+        for (int j = 0; j < GS / 8; ++j) {
+            uint32_t hw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hw[i] = (uint32_t)float_to_half_bits(w[8 * j + 2 * i]) |
+                        ((uint32_t)float_to_half_bits(w[8 * j + 2 * i + 1]) << 16);
+            wf.cw[mine * K::SEG + j] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        }
+        wf.cg[mine] = CompactGroup{g.s, r.z, g.mn, g.mx, g.amag, r.beta, r.it, 0, g.sw};
+    }
+    wave_sync();
+    const int b = (int)lane / K::SEG;
+    const bool act = b < nrun;
+    const CompactGroup st = wf.cg[act ? b : 0];
+    float we[8];
+    {
+        const u32x4 v = wf.cw[(act ? b : 0) * K::SEG + (int)lane % K::SEG];
+        _Float16 h[8];
+        __builtin_memcpy(h, &v, 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            we[i] = (float)h[i];
+    }
+    const float s = st.s;
+    const float thr_s = a.thr * s;
+    const float lim = a.thr_m * s;
+    const double ssw = (double)s * st.sw;
+    float z = st.z, beta = st.beta;
+    int it = st.it;
+    bool run = act, frozen = false;
+    while (__any(run)) {
+        if (run) {
+            const float tmin = __builtin_fmaf(st.mn, s, z);
+            const float tmax = __builtin_fmaf(st.mx, s, z);
+            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+            const bool est_ok = __builtin_fmaf(st.amag, s, fabsf(z)) + QMAX <= lim;
+            if (!(est_ok && bound <= thr_s)) {
+                run = false;
+                frozen = true;
+            }
+        }
+        // every lane computes (the DPP sums read whole blocks of lanes)
+        uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[0], s, z), 0, 0u);
+        uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4], s, z), 0, 0u);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+            d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[j], s, z), j, d0);
+            d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 + j], s, z), j, d1);
+        }
+        const uint32_t c = __builtin_amdgcn_sad_u8(d1, 0u, __builtin_amdgcn_sad_u8(d0, 0u, 0u));
+        const uint32_t q = __builtin_amdgcn_sad_u8(d1, QB, __builtin_amdgcn_sad_u8(d0, QB, 0u));
+        const int tot = seg_sum<K::SEG>((int)c - (int)q);
+        const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
+        const float zn = (float)(((double)sq - ssw) * INV_GS);
+        if (run) {
+            it = zn == z ? a.iters : it + 1;
+            beta = beta * a.kappa;
+            z = zn;
+            if (it >= a.iters)
+                run = false;
+        }
+    }
+    wave_sync();
+    if (act && (int)lane % K::SEG == 0) {
+        wf.cg[b].z = z;
+        wf.cg[b].beta = beta;
+        wf.cg[b].it = it;
+        wf.cg[b].frozen = frozen ? 1 : 0;
+    }
+    wave_sync();
+    if (r.run) {
+        const CompactGroup o = wf.cg[mine];
+        r.z = o.z;
+        r.beta = o.beta;
+        r.it = o.it;
+        r.frozen = o.frozen != 0;
+        r.run = false;
+    }
+    wave_sync();
+}
+
 // Fast iterations of the lanes with r.run, up to iters: a lane freezes its
 // group at the first iteration whose certificate fails, and stops once its
-// zero is a fixed point (r.it = iters then).
+// zero is a fixed point (r.it = iters then).  With wf: compact mode once at
+// most Compact::B groups of the wave still iterate.
 template <int NB, int GS>
 __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[GS], const GroupInit &g,
-                                           LaneRun &r)
+                                           LaneRun &r, WaveFinish<GS> *wf = nullptr)
 {
     constexpr float QMAX = (float)((1 << NB) - 1);
     constexpr double INV_GS = 1.0 / GS;
@@ -404,6 +536,12 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
     if (a.iters == 0)
         r.run = false;
     while (__any(r.run)) {
+        if constexpr (Compact<GS>::ON) {
+            if (wf != nullptr && __popcll(__ballot(r.run)) <= Compact<GS>::B) {
+                compact_iters<NB, GS>(a, *wf, w, g, r);
+                break;
+            }
+        }
         if (r.run) {
             const float tmin = __builtin_fmaf(g.mn, s, r.z);
             const float tmax = __builtin_fmaf(g.mx, s, r.z);
@@ -484,7 +622,7 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
     // loop and their results are not stored.
     const GroupInit g = group_init<NB, GS>(w);
     LaneRun r{g.z, a.beta0, 0, valid, false};
-    fast_iters<NB, GS>(a, w, g, r);
+    fast_iters<NB, GS>(a, w, g, r, &wf);
     finish_group<NB, GS, G, AXIS>(a, T, wf, valid, line, eg, w, g, r, words);
     s_out = g.s;
     z_out = r.z;
