@@ -142,6 +142,7 @@ int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_si
             d.cols = t.cols;
             d.nblk = (L + lb - 1) / lb;
             d.n_items = d.nblk * (axis == 1 ? t.rows : t.cols);
+            d.rdiv = 1.0 / (double)(axis == 1 ? d.nblk : t.cols);
             items += d.n_items;
             ++a.n;
         }

@@ -19,6 +19,7 @@ struct SolveTensor {
     int64_t rows, cols;
     int64_t n_items;     // work items: one block of lcm(gs, C) elements of one line
     int64_t nblk;        // work items per line
+    double rdiv;         // 1 / (axis 1: nblk, axis 0: cols), for the item -> (line, block) split
 };
 
 // Up to this many same-format tensors share one launch (kernel-argument size).

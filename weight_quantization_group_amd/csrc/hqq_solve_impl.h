@@ -234,17 +234,38 @@ struct WaveFinish {
     CompactGroup cg[Compact<GS>::ON ? Compact<GS>::B : 1];
 };
 
-// Pack a group's final codes (small integers held in fp32) into the work item's words.
+// Pack a group's final codes into the work item's words.  4-bit groups that
+// start on a word: eight codes per word as bytes (v_cvt_pk_u8_f32 of the
+// clamped value: round half to even of clamp(t) equals clamp of the rounded
+// t), nibble pairs folded with a shift-or, and the four nibble-pair bytes
+// gathered with v_perm_b32.  Other formats: code by code.
 template <int NB, int GS, int G, int WPB>
 __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float z,
                                            uint32_t (&words)[WPB])
 {
     constexpr int C = codes_per_word(NB);
     constexpr float QMAX = (float)((1 << NB) - 1);
+    if constexpr (NB == 4 && (G * GS) % 8 == 0 && GS % 8 == 0) {
 #pragma unroll
-    for (int i = 0; i < GS; ++i) {
-        const int n = G * GS + i;
-        words[n / C] |= (uint32_t)quant(w[i], s, z, QMAX) << ((n % C) * NB);
+        for (int q = 0; q < GS / 8; ++q) {
+            uint32_t d0 = 0, d1 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d0 = __builtin_amdgcn_cvt_pk_u8_f32(
+                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[8 * q + j], s, z), 0.0f, QMAX), j, d0);
+                d1 = __builtin_amdgcn_cvt_pk_u8_f32(
+                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[8 * q + 4 + j], s, z), 0.0f, QMAX), j, d1);
+            }
+            const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
+            const uint32_t x1 = d1 | (d1 >> 4);
+            words[(G * GS) / 8 + q] |= __builtin_amdgcn_perm(x1, x0, 0x06040200u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < GS; ++i) {
+            const int n = G * GS + i;
+            words[n / C] |= (uint32_t)quant(w[i], s, z, QMAX) << ((n % C) * NB);
+        }
     }
 }
 
@@ -651,13 +672,26 @@ __device__ __forceinline__ ItemPos item_pos(const SolveTensor &T, int64_t item)
     const bool live = item < T.n_items;
     const int64_t it_c = live ? item : 0;
     ItemPos p;
+    // quotient by the tensor's divisor through its fp64 reciprocal: the
+    // product is within one of the quotient (item < 2^53), the remainder
+    // test corrects it; the quotient is a row or block index (< 2^31)
+    const int64_t dv = AXIS == 1 ? T.nblk : T.cols;
+    int64_t q = (int64_t)(uint32_t)((double)it_c * T.rdiv);
+    int64_t r = it_c - q * dv;
+    if (r < 0) {
+        q -= 1;
+        r += dv;
+    } else if (r >= dv) {
+        q += 1;
+        r -= dv;
+    }
     int64_t blk;
     if constexpr (AXIS == 1) {
-        p.line = it_c / T.nblk;
-        blk = it_c - p.line * T.nblk;
+        p.line = q;
+        blk = r;
     } else {
-        blk = it_c / T.cols;
-        p.line = it_c - blk * T.cols;
+        blk = q;
+        p.line = r;
     }
     const int64_t L = AXIS == 1 ? T.cols : T.rows;
     p.e0 = blk * I::LB;
