@@ -49,7 +49,7 @@ HBM_PEAK_GBS = 8000.0
 # 2.625 B / 8 TB/s = 0.33 ps.  The VALU figures actually issued, from the
 # committed counter summary, are reported beside the roofline.
 def hbm_bytes_per_weight(nbits: int, group_size: int) -> float:
-    C = {4: 8, 3: 10, 2: 16, 1: 32}[nbits]
+    C = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}[nbits]
     return 2.0 + 4.0 / C + 8.0 / group_size
 
 
@@ -241,7 +241,8 @@ def main():
 
     gbs = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "llama7b_stack32_4b_g64" else
+                  f"GB/s of fp16 weights quantized (HQQ {nb}b g{gs}, {args.iters} it), workload {args.workload}",
         "value": round(gbs, 3),
         "unit": "GB/s",
         "n_gpus": 1,

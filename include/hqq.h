@@ -35,8 +35,8 @@
  *             (along in_features, contiguous); scale/zero are [rows, cols/gs].
  *   axis = 0: a group is group_size consecutive rows of one column
  *             (along out_features, strided); scale/zero are [rows/gs, cols].
- * Codes are packed along the group axis: C = 8 (4-bit), 10 (3-bit),
- * 16 (2-bit) or 32 (1-bit) codes per uint32; word k of a line holds the
+ * Codes are packed along the group axis: C = 4 (8-bit), 8 (4-bit),
+ * 10 (3-bit), 16 (2-bit) or 32 (1-bit) codes per uint32; word k of a line holds the
  * line's codes k*C .. k*C+C-1, code j in bits [j*b, j*b+b) (LSB first); the
  * unused fields of a line's last word, and bits 30-31 of 3-bit words, are 0.
  *   axis = 1: packed is [rows, ceil(cols/C)];  axis = 0: [ceil(rows/C), cols].
@@ -53,7 +53,8 @@
  *     nothing is enqueued and a negative HQQ_E* status is returned.
  *     HQQ_EHIP reports a failed kernel launch.  Contents of W that are NaN or
  *     Inf are a precondition violation and are not checked.
- *   - Supported: nbits in {1,2,3,4}; group_size in {8,16,32,64,128,256},
+ *   - Supported: nbits in {1,2,3,4,8} (lnwmold.com HQQ guide, section 2.2
+ *     lists 8/4/3/2/1 bits); group_size in {8,16,32,64,128,256},
  *     dividing the line length (cols for axis 1, rows for axis 0).
  */
 #ifndef HQQ_H
@@ -70,7 +71,7 @@ extern "C" {
 #endif
 
 #define HQQ_OK 0
-#define HQQ_EINVAL_NBITS (-1) /* nbits not in {1,2,3,4}                              */
+#define HQQ_EINVAL_NBITS (-1) /* nbits not in {1,2,3,4,8}                            */
 #define HQQ_EINVAL_AXIS (-2)  /* axis not in {0,1}                                   */
 #define HQQ_EINVAL_GROUP (-3) /* group_size unsupported or not dividing the line     */
 #define HQQ_EINVAL_SHAPE (-4) /* rows or cols < 1 or too large, or batch count < 0    */

@@ -28,7 +28,7 @@ BETA0_DEFAULT = 10.0
 KAPPA_DEFAULT = 1.01
 ITERS_DEFAULT = 20
 
-CODES_PER_WORD = {4: 8, 3: 10, 2: 16, 1: 32}
+CODES_PER_WORD = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}
 
 
 def build(force: bool = True) -> str:

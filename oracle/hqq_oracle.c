@@ -219,6 +219,7 @@ int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
 static int codes_per_word(int nbits)
 {
     switch (nbits) {
+    case 8: return 4;
     case 4: return 8;
     case 3: return 10;
     case 2: return 16;
@@ -231,7 +232,7 @@ static int check_shape(int64_t rows, int64_t cols, int nbits, int group_size, in
 {
     if (rows < 1 || cols < 1)
         return -4;
-    if (nbits < 1 || nbits > 4)
+    if (codes_per_word(nbits) < 0)
         return -1;
     if (axis != 0 && axis != 1)
         return -2;

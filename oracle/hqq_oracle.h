@@ -25,7 +25,8 @@
  * Conventions: W is fp16 bits, row-major [rows, cols] (rows = out_features,
  * cols = in_features).  axis=1: a group is gs consecutive elements of a row;
  * axis=0: gs consecutive rows of one column.  Codes are packed along the
- * group axis, LSB first, C = 8 (4b), 10 (3b), 16 (2b), 32 (1b) per uint32.
+ * group axis, LSB first, C = 4 (8b), 8 (4b), 10 (3b), 16 (2b), 32 (1b) per
+ * uint32.
  * All functions return 0 on success, a negative value on invalid arguments.
  */
 #ifndef HQQ_ORACLE_H

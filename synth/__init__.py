@@ -65,6 +65,7 @@ def workload(name: str):
     """List of tensors: dicts with layer, name, tensor_id, rows, cols, nbits,
     group_size, axis, seed.  Names: 'linear_4096x1024_4b_g64',
     'llama7b_layer_4b_g64', 'llama7b_layer_3b2b_axis0', 'llama7b_stack32_4b_g64',
+    'llama7b_stack32_8b_g128' (the same weights at 8 bits, group 128),
     'llama70b_stack80_mixed'."""
     out = []
     if name == "linear_4096x1024_4b_g64":
@@ -85,6 +86,11 @@ def workload(name: str):
             for n, r, c in _layer_7b():
                 out.append(dict(layer=layer, name=n, tensor_id=TENSOR_IDS[n], rows=r, cols=c,
                                 nbits=4, group_size=64, axis=1, seed=SEED_7B))
+    elif name == "llama7b_stack32_8b_g128":
+        for layer in range(32):
+            for n, r, c in _layer_7b():
+                out.append(dict(layer=layer, name=n, tensor_id=TENSOR_IDS[n], rows=r, cols=c,
+                                nbits=8, group_size=128, axis=1, seed=SEED_7B))
     elif name == "llama70b_stack80_mixed":
         for layer in range(80):
             for n, r, c in _layer_70b():
@@ -100,7 +106,7 @@ def workload(name: str):
 
 
 WORKLOADS = ["linear_4096x1024_4b_g64", "llama7b_layer_4b_g64", "llama7b_layer_3b2b_axis0",
-             "llama7b_stack32_4b_g64", "llama70b_stack80_mixed"]
+             "llama7b_stack32_4b_g64", "llama7b_stack32_8b_g128", "llama70b_stack80_mixed"]
 
 
 # ---------------------------------------------------------------------------

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_packed_words_matches_layout(lib, oracle_mod):
-    for nbits in (1, 2, 3, 4):
+    for nbits in (1, 2, 3, 4, 8):
         for axis in (0, 1):
             for rows, cols in ((1, 1), (7, 33), (4096, 4096), (11008, 4096), (320, 11008)):
                 assert lib.hqq_packed_words(rows, cols, nbits, axis) == \
@@ -81,7 +81,7 @@ def _q(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(nbits=0), "NBITS"), (dict(nbits=5), "NBITS"), (dict(nbits=8), "NBITS"),
+    (dict(nbits=0), "NBITS"), (dict(nbits=5), "NBITS"), (dict(nbits=7), "NBITS"), (dict(nbits=16), "NBITS"),
     (dict(axis=2), "AXIS"), (dict(axis=-1), "AXIS"),
     (dict(gs=48), "GROUP"), (dict(gs=512), "GROUP"), (dict(gs=4), "GROUP"),
     (dict(cols=96), "GROUP"), (dict(axis=0, rows=96), "GROUP"),

@@ -19,7 +19,7 @@ from helpers import random_f16, recon_mse
 
 pytestmark = pytest.mark.gpu
 
-QMAX = {1: 1, 2: 3, 3: 7, 4: 15}
+QMAX = {1: 1, 2: 3, 3: 7, 4: 15, 8: 255}
 C_OF = {4: 8, 3: 10, 2: 16, 1: 32}
 
 
@@ -88,7 +88,7 @@ def check_parity(oracle_mod, W16, nbits, gs, axis, g_packed, g_scale, g_zero, o=
 SHAPES = [(8, 8), (16, 24), (40, 96), (96, 40), (64, 320), (320, 64), (56, 1024), (1024, 48), (48, 56)]
 
 
-@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_pack_unpack_bitexact(hq, oracle_mod, nbits, axis):
     import torch
@@ -103,7 +103,7 @@ def test_pack_unpack_bitexact(hq, oracle_mod, nbits, axis):
         assert np.array_equal(back.cpu().numpy(), codes), (rows, cols)
 
 
-@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_dequantize_bitexact(hq, oracle_mod, nbits, axis):
     import torch
@@ -128,7 +128,7 @@ def test_dequantize_bitexact(hq, oracle_mod, nbits, axis):
 
 def _format_cases():
     out = []
-    for nbits in (1, 2, 3, 4):
+    for nbits in (1, 2, 3, 4, 8):
         for gs in (8, 16, 32, 64, 128, 256):
             for axis in (0, 1):
                 out.append((nbits, gs, axis))
@@ -330,7 +330,7 @@ def test_70b_stack_sampled(hq, oracle_mod):
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])
-@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1)])
+@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1), (8, 128, 1)])
 def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters):
     """Groups that stop before, at and after the point where the solve parks
     unfinished groups for later batches, and long runs, match the oracle."""

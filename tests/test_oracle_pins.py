@@ -21,7 +21,7 @@ import pytest
 
 from helpers import f16_bits_to_f32, fma_f32, random_f16
 
-QMAX = {1: 1, 2: 3, 3: 7, 4: 15}
+QMAX = {1: 1, 2: 3, 3: 7, 4: 15, 8: 255}
 
 
 # --------------------------------------------------------------------------
@@ -62,7 +62,7 @@ def test_f32_to_f16_rne(oracle_mod):
 # RTN at iters = 0
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 def test_iters0_is_minmax_rtn(oracle_mod, nbits):
     rng = np.random.RandomState(10 + nbits)
     qmax = QMAX[nbits]
@@ -253,7 +253,7 @@ def test_grid_weights_are_a_fixed_point(oracle_mod, nbits, gs):
         assert np.array_equal(back, W16)
 
 
-@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 def test_codes_in_range_and_axis_layout(oracle_mod, nbits):
     rng = np.random.RandomState(20 + nbits)
     W16 = random_f16(rng, (64, 48), std=0.05, outlier_frac=0.02)
@@ -353,6 +353,13 @@ def test_pack_hand_derived_words(oracle_mod):
     # 4-bit: codes 1..8 along a row -> nibbles LSB first
     codes = np.arange(1, 9, dtype=np.uint8).reshape(1, 8)
     assert oracle_mod.pack(codes, 4, 1)[0, 0] == 0x87654321
+    # 8-bit: four bytes per word, LSB first; a 6-wide row pads its 2nd word with zeros
+    codes = np.array([[0x11, 0xA2, 0x03, 0xFF, 0x7E, 0x80]], dtype=np.uint8)
+    words = oracle_mod.pack(codes, 8, 1)
+    assert words.shape == (1, 2) and words[0, 0] == 0xFF03A211 and words[0, 1] == 0x0000807E
+    # 8-bit along axis 0: word k of column c holds rows 4k..4k+3
+    colw = oracle_mod.pack(codes.reshape(6, 1), 8, 0)
+    assert colw.shape == (2, 1) and colw[0, 0] == 0xFF03A211 and colw[1, 0] == 0x0000807E
     # 3-bit: ten codes per word in bits 0..29, bits 30-31 zero; a 12-wide row pads its 2nd word
     codes = np.array([[7, 0, 1, 2, 3, 4, 5, 6, 7, 7, 5, 1]], dtype=np.uint8)
     words = oracle_mod.pack(codes, 3, 1)
@@ -375,7 +382,7 @@ def test_pack_hand_derived_words(oracle_mod):
     assert words[0, 0] == (1 | (1 << 5) | (1 << 31)) and words[0, 1] == 1
 
 
-@pytest.mark.parametrize("nbits", [1, 2, 3, 4])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_pack_unpack_roundtrip(oracle_mod, nbits, axis):
     C = oracle_mod.CODES_PER_WORD[nbits]

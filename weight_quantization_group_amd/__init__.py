@@ -23,7 +23,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhqq.so")
 
-CODES_PER_WORD = {4: 8, 3: 10, 2: 16, 1: 32}
+CODES_PER_WORD = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}
 P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order

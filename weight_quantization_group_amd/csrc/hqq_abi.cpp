@@ -14,7 +14,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 int check_common(int64_t rows, int64_t cols, int nbits, int group_size, int axis)
 {
-    if (nbits < 1 || nbits > 4)
+    if (!hqq::valid_nbits(nbits))
         return HQQ_EINVAL_NBITS;
     if (axis != 0 && axis != 1)
         return HQQ_EINVAL_AXIS;
@@ -71,7 +71,7 @@ extern "C" {
 
 int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis)
 {
-    if (nbits < 1 || nbits > 4)
+    if (!hqq::valid_nbits(nbits))
         return HQQ_EINVAL_NBITS;
     if (axis != 0 && axis != 1)
         return HQQ_EINVAL_AXIS;
@@ -85,7 +85,7 @@ const char *hqq_strerror(int status)
 {
     switch (status) {
     case HQQ_OK: return "ok";
-    case HQQ_EINVAL_NBITS: return "nbits must be 1, 2, 3 or 4";
+    case HQQ_EINVAL_NBITS: return "nbits must be 1, 2, 3, 4 or 8";
     case HQQ_EINVAL_AXIS: return "axis must be 0 or 1";
     case HQQ_EINVAL_GROUP: return "group_size must be 8, 16, 32, 64, 128 or 256 and divide the line length";
     case HQQ_EINVAL_SHAPE: return "rows and cols must be >= 1 (and rows, cols <= 2^31, rows*cols <= 2^40)";

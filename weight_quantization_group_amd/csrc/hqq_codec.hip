@@ -154,6 +154,8 @@ __global__ __launch_bounds__(256) void unpack_kernel(CodecArgs a)
         case 7: return NAME##_t<3, 1>(a, st);                                             \
         case 8: return NAME##_t<4, 0>(a, st);                                             \
         case 9: return NAME##_t<4, 1>(a, st);                                             \
+        case 16: return NAME##_t<8, 0>(a, st);                                            \
+        case 17: return NAME##_t<8, 1>(a, st);                                            \
         default: return hipErrorInvalidValue;                                             \
         }                                                                                 \
     }

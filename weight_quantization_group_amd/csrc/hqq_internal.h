@@ -6,7 +6,8 @@
 
 namespace hqq {
 
-constexpr int codes_per_word(int nb) { return nb == 4 ? 8 : nb == 3 ? 10 : nb == 2 ? 16 : 32; }
+constexpr int codes_per_word(int nb) { return nb == 8 ? 4 : nb == 4 ? 8 : nb == 3 ? 10 : nb == 2 ? 16 : 32; }
+constexpr bool valid_nbits(int nb) { return nb == 1 || nb == 2 || nb == 3 || nb == 4 || nb == 8; }
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 

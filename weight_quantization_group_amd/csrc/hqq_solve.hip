@@ -13,6 +13,7 @@ hipError_t launch_solve(int nbits, int group_size, int axis, const SolveArgs &a,
     case 2: return launch_solve_nb<2>(group_size, axis, a, st);
     case 3: return launch_solve_nb<3>(group_size, axis, a, st);
     case 4: return launch_solve_nb<4>(group_size, axis, a, st);
+    case 8: return launch_solve_nb<8>(group_size, axis, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -234,8 +234,9 @@ struct WaveFinish {
     CompactGroup cg[Compact<GS>::ON ? Compact<GS>::B : 1];
 };
 
-// Pack a group's final codes into the work item's words.  4-bit groups that
-// start on a word: eight codes per word as bytes (v_cvt_pk_u8_f32 of the
+// Pack a group's final codes into the work item's words.  8-bit: a word is
+// four clamped bytes.  4-bit groups that start on a word: eight codes per
+// word as bytes (v_cvt_pk_u8_f32 of the
 // clamped value: round half to even of clamp(t) equals clamp of the rounded
 // t), nibble pairs folded with a shift-or, and the four nibble-pair bytes
 // gathered with v_perm_b32.  Other formats: code by code.
@@ -259,6 +260,17 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
             const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
             const uint32_t x1 = d1 | (d1 >> 4);
             words[(G * GS) / 8 + q] |= __builtin_amdgcn_perm(x1, x0, 0x06040200u);
+        }
+    } else if constexpr (NB == 8) {
+        // four codes per word: the word is the four clamped bytes
+#pragma unroll
+        for (int q = 0; q < GS / 4; ++q) {
+            uint32_t d = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                d = __builtin_amdgcn_cvt_pk_u8_f32(
+                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[4 * q + j], s, z), 0.0f, QMAX), j, d);
+            words[(G * GS) / 4 + q] = d;
         }
     } else {
 #pragma unroll
@@ -383,6 +395,7 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
 constexpr int waves_per_simd(int nb, int gs)
 {
     return nb == 3   ? (gs == 8 ? 5 : gs <= 32 ? 4 : gs == 64 ? 3 : 1)
+           : nb == 8 ? (gs == 8 ? 6 : gs == 16 ? 5 : gs == 32 ? 4 : gs == 64 ? 3 : gs == 128 ? 2 : 1)
            : nb == 1 && gs == 8 ? 5
                               : (gs <= 16 ? 6 : gs == 32 ? 5 : gs == 64 ? 4 : gs == 128 ? 2 : 1);
 }
