@@ -63,6 +63,8 @@ def _bind(L):
     L.hqq_ref_unpack.restype = i32
     L.hqq_ref_dequantize.argtypes = [P, P, P, i64, i64, i32, i32, i32, P]
     L.hqq_ref_dequantize.restype = i32
+    L.hqq_ref_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
+    L.hqq_ref_linear.restype = i32
     return L
 
 
@@ -204,6 +206,22 @@ def dequantize(packed, scale, zero, rows, cols, nbits, group_size, axis) -> np.n
                                   nbits, group_size, axis, _ptr(out))
     _check(st, "dequantize")
     return out
+
+
+def linear(X16: np.ndarray, packed, scale, zero, N, nbits, group_size, with_abs=False):
+    """Y = X @ W_hat^T in fp64 (X fp16 bits [M, K]; axis = 1 weight [N, K]).
+    Returns Y [M, N] (and sum |x w| per output with with_abs)."""
+    X16 = np.ascontiguousarray(X16, dtype=np.uint16)
+    M, K = X16.shape
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    zero = np.ascontiguousarray(zero, dtype=np.float32)
+    Y = np.zeros((M, N), np.float64)
+    A = np.zeros((M, N), np.float64)
+    st = lib().hqq_ref_linear(_ptr(X16), M, K, _ptr(packed), _ptr(scale), _ptr(zero), N, nbits,
+                              group_size, _ptr(Y), _ptr(A))
+    _check(st, "linear")
+    return (Y, A) if with_abs else Y
 
 
 class Oracle:

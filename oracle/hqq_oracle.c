@@ -392,6 +392,40 @@ int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *
     return 0;
 }
 
+int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
+                   const uint32_t *packed, const float *scale, const float *zero,
+                   int64_t N, int nbits, int group_size, double *Y, double *absY)
+{
+    if (M < 1)
+        return -4;
+    int st = check_shape(N, K, nbits, group_size, 1);
+    if (st)
+        return st;
+    if (!X || !packed || !scale || !zero || !Y)
+        return -5;
+    uint16_t *W_hat = (uint16_t *)malloc((size_t)(N * K) * sizeof(uint16_t));
+    if (!W_hat)
+        return -2;
+    st = hqq_ref_dequantize(packed, scale, zero, N, K, nbits, group_size, 1, W_hat);
+    if (st == 0) {
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t n = 0; n < N; ++n) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    double prod = (double)hqq_ref_f16_to_f32(X[m * K + k]) *
+                                  (double)hqq_ref_f16_to_f32(W_hat[n * K + k]);
+                    acc += prod;
+                    mag += fabs(prod);
+                }
+                Y[m * N + n] = acc;
+                if (absY)
+                    absY[m * N + n] = mag;
+            }
+    }
+    free(W_hat);
+    return st;
+}
+
 int hqq_ref_quantize(const uint16_t *W, int64_t rows, int64_t cols,
                      int nbits, int group_size, int axis, int iters,
                      float p, float beta0, float kappa,

@@ -84,6 +84,17 @@ int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *
                        int64_t rows, int64_t cols, int nbits, int group_size, int axis,
                        uint16_t *W_hat);
 
+/* Linear layer on quantized weights (the consumer of the codes: HQQLinear's
+ * forward in the lnwmold.com HQQ guide, section 3.2, dequantizes W_q and
+ * multiplies in the compute dtype).  W_hat = hqq_ref_dequantize(...) of an
+ * axis = 1 weight [N, K]; X is fp16 bits [M, K].  Y[m, n] = sum_k X[m, k] *
+ * W_hat[n, k], summed in fp64 in order k = 0..K-1 (Y [M, N] doubles); absY
+ * [M, N] (optional) receives sum_k |X[m, k] * W_hat[n, k]| for error bounds.
+ * Returns 0 or a negative status as above. */
+int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
+                   const uint32_t *packed, const float *scale, const float *zero,
+                   int64_t N, int nbits, int group_size, double *Y, double *absY);
+
 #ifdef __cplusplus
 }
 #endif
