@@ -132,6 +132,28 @@ HQQ_API int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
 HQQ_API int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
                int nbits, int group_size, int axis, uint8_t *codes, void *stream);
 
+/* Linear layer on quantized weights: Y = X . W_hat^T, the quantized layer's
+ * forward pass (lnwmold.com HQQ guide section 3.2: the HQQLinear layer is
+ * called like the Linear it replaces, computing in compute_dtype = fp16;
+ * section 4.1: a backend fuses the dequantization and the matrix product
+ * into one kernel, which requires axis = 1).
+ *   X       fp16 bits [M, K] row-major, device, read only
+ *   packed  the axis = 1 packed codes of W [N, K] (hqq_packed_words(N, K,
+ *           nbits, 1) words, as written by hqq_quantize), read only
+ *   scale, zero  fp32 [N, K / group_size], read only
+ *   Y       fp16 bits [M, N] row-major, written (must not overlap the inputs)
+ * W_hat is exactly what hqq_dequantize writes; each output is the fp32 sum
+ * of the exact products X[m][k] * W_hat[n][k] (in an unspecified order)
+ * rounded to fp16, round-half-even.
+ * Supported: nbits in {1, 2, 4, 8} (a packed word holds whole 8-k runs);
+ * group_size in {8, ..., 256} dividing K; K a multiple of 32; M, N >= 1;
+ * X, the codes and the meta each below 2^31 bytes.
+ * All pointers 16-byte aligned.  Invalid arguments return HQQ_EINVAL_* before
+ * anything is enqueued (3-bit codes: HQQ_EINVAL_NBITS). */
+HQQ_API int hqq_linear(const uint16_t *X, int64_t M, int64_t K,
+                       const uint32_t *packed, const float *scale, const float *zero,
+                       int64_t N, int nbits, int group_size, uint16_t *Y, void *stream);
+
 /* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */
 HQQ_API int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);

@@ -39,7 +39,7 @@ def test_header_codes_match():
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack",
-                               "hqq_unpack", "hqq_packed_words", "hqq_strerror"])
+                               "hqq_unpack", "hqq_linear", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -103,6 +103,31 @@ def test_codec_rejects(lib):
     assert lib.hqq_pack(MIS, 64, 128, 4, 64, 1, A, None) == E["PTR"]
     assert lib.hqq_unpack(A, 0, 128, 4, 64, 1, A, None) == E["SHAPE"]
     assert lib.hqq_unpack(A, 64, 128, 4, 32, 0, None, None) == E["PTR"]
+
+
+def test_linear_rejects(lib):
+    # (X, M, K, packed, scale, zero, N, nbits, gs, Y, stream): invalid arguments
+    # return before anything is enqueued
+    ok = dict(M=4, K=128, N=32, nbits=4, gs=64)
+
+    def call(X=A, packed=A, scale=A, zero=A, Y=A, **kw):
+        a = {**ok, **kw}
+        return lib.hqq_linear(X, a["M"], a["K"], packed, scale, zero, a["N"], a["nbits"],
+                              a["gs"], Y, None)
+
+    assert call(nbits=3) == E["NBITS"]
+    assert call(nbits=5) == E["NBITS"]
+    assert call(M=0) == E["SHAPE"]
+    assert call(N=0) == E["SHAPE"]
+    assert call(K=0) == E["SHAPE"]
+    assert call(K=48) == E["SHAPE"]          # K must be a multiple of 32
+    assert call(K=96, gs=64) == E["GROUP"]   # gs must divide K
+    assert call(gs=48) == E["GROUP"]
+    assert call(gs=512, K=512) == E["GROUP"]
+    assert call(M=1 << 32) == E["SHAPE"]
+    assert call(X=None) == E["PTR"]
+    assert call(Y=MIS) == E["PTR"]
+    assert call(scale=MIS) == E["PTR"]
 
 
 def test_batch_rejects(lib):

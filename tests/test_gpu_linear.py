@@ -1,0 +1,207 @@
+"""GPU parity of the fused dequantize + matmul (hqq_linear, through the C ABI)
+against the oracle's linear layer (fp64 sums of X . W_hat^T, W_hat exactly
+dequantized).
+
+Bar.  W_hat inside the kernel is bit-exact (the identity-input tests see it
+directly).  Each product X[m][k] * W_hat[n][k] of two fp16 values is exact
+in fp32, so the kernel's fp32 result differs from the fp64 sum Yref only by
+fp32 accumulation, at most K * 2^-24 * A with A = sum_k |X[m][k] W_hat[n][k]|
+(the standard bound for any summation order), and the final rounding to fp16
+adds at most half an ulp of fp16, 2^-11 relative (2^-25 absolute in the
+subnormal range).  The test requires, per output,
+    |Y - Yref| <= 2^-11 |Yref| + 1.01 K 2^-24 A + 2^-24 .
+Inputs: seeded synthetic fp16 activations and weights; the weights are
+quantized by the oracle (or, for the large cases, given random codes and
+oracle-style min/max meta), so no input comes from the HIP path.
+"""
+import numpy as np
+import pytest
+
+from helpers import f16_bits_to_f32, random_f16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hq():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import weight_quantization_group_amd as w
+
+    w.load_library()
+    return w
+
+
+def _cuda(a: np.ndarray):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).cuda()
+
+
+def gpu_linear(hq, X16, packed, scale, zero, N, nbits, gs):
+    import torch
+
+    Y = hq.hqq_linear(_cuda(X16), _cuda(packed), _cuda(scale), _cuda(zero), N, nbits, gs)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=True):
+    """(packed, scale, zero) of an axis = 1 weight [N, K]: the oracle's solve
+    on a synthetic weight, or (solve=False) random codes with min/max meta of a
+    synthetic weight (cheap at large sizes)."""
+    if solve:
+        W16 = random_f16(rng, (N, K), std=0.02, outlier_frac=0.002)
+        return oracle_mod.quantize(W16, nbits, gs, 1, iters=4)
+    qmax = (1 << nbits) - 1
+    codes = rng.randint(0, qmax + 1, size=(N, K)).astype(np.uint8)
+    lo = -np.abs(rng.normal(0.03, 0.01, (N, K // gs)))
+    hi = np.abs(rng.normal(0.03, 0.01, (N, K // gs))) + 1e-3
+    scale = (qmax / (hi - lo)).astype(np.float32)
+    zero = (-lo * scale).astype(np.float32)
+    return oracle_mod.pack(codes, nbits, 1), scale, zero
+
+
+def check(Y16, Yref, A, K, tag=""):
+    Y = Y16.astype(np.float64)
+    assert Y.shape == Yref.shape, tag
+    assert np.all(np.isfinite(Y)), tag
+    err = np.abs(Y - Yref)
+    bound = 2.0 ** -11 * np.abs(Yref) + 1.01 * K * 2.0 ** -24 * A + 2.0 ** -24
+    worst = np.max(err / bound)
+    assert worst <= 1.0, f"{tag}: worst error / bound = {worst:.3g}"
+    return worst
+
+
+# (M, N, K, nbits, gs): one and several m tiles, ragged M and N, K not a
+# multiple of the 128-wide wave step, every supported width, small groups
+# (several groups per 32-k lane chunk), the smallest K
+CASES = [
+    (1, 64, 128, 4, 64),
+    (1, 40, 96, 4, 32),
+    (7, 100, 256, 4, 64),
+    (16, 48, 512, 4, 128),
+    (17, 33, 256, 4, 64),
+    (32, 64, 512, 4, 256),
+    (45, 70, 320, 4, 64),
+    (3, 50, 256, 2, 16),
+    (9, 24, 160, 2, 32),
+    (2, 36, 256, 1, 64),
+    (5, 20, 64, 1, 8),
+    (4, 30, 256, 8, 128),
+    (11, 18, 192, 8, 8),
+    (1, 16, 32, 4, 8),
+    (1, 1, 32, 4, 16),
+]
+
+
+@pytest.mark.parametrize("M,N,K,nbits,gs", CASES)
+def test_linear_parity(hq, oracle_mod, M, N, K, nbits, gs):
+    rng = np.random.RandomState(1000 + M * 7 + N + K + nbits * 13 + gs)
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs)
+    X16 = random_f16(rng, (M, K), std=1.0)
+    Y = gpu_linear(hq, X16, packed, scale, zero, N, nbits, gs)
+    Yref, A = oracle_mod.linear(X16, packed, scale, zero, N, nbits, gs, with_abs=True)
+    check(f16_bits_to_f32(Y.view(np.uint16)), Yref, A, K, f"{M}x{N}x{K} b{nbits} g{gs}")
+
+
+@pytest.mark.parametrize("nbits,gs", [(4, 64), (2, 16), (1, 32), (8, 128), (4, 8)])
+def test_identity_input_gives_dequantized_weights_exactly(hq, oracle_mod, nbits, gs):
+    """X = I: Y[m][n] = W_hat[n][m], bit-exact against the oracle's dequantize
+    (one nonzero product per output, so the kernel's W_hat is seen directly)."""
+    rng = np.random.RandomState(7 + nbits + gs)
+    K, N = 256, 40
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs)
+    X = np.zeros((K, K), np.float16)
+    np.fill_diagonal(X, 1.0)
+    Y = gpu_linear(hq, X.view(np.uint16), packed, scale, zero, N, nbits, gs)
+    W_hat = oracle_mod.dequantize(packed, scale, zero, N, K, nbits, gs, 1)
+    assert_same_weights(Y.view(np.uint16), W_hat.T)
+
+
+def test_identity_extreme_meta_exact(hq, oracle_mod):
+    """Scales over many binades and zeros far outside the code range: the
+    in-kernel quotient (one fp64 product) still matches the fp32 division,
+    down to fp16 subnormals.  (Scales stay >= 2^-7 so that no |W_hat| exceeds
+    the fp16 range: an infinite weight makes its whole output row NaN through
+    0 * inf, in any matmul.)"""
+    rng = np.random.RandomState(99)
+    K, N, gs, nbits = 128, 64, 32, 4
+    codes = rng.randint(0, 16, size=(N, K)).astype(np.uint8)
+    scale = (rng.uniform(1, 2, (N, K // gs)) * 2.0 ** rng.randint(-7, 31, (N, K // gs))).astype(np.float32)
+    zero = rng.uniform(-300, 300, (N, K // gs)).astype(np.float32)
+    packed = oracle_mod.pack(codes, nbits, 1)
+    X = np.zeros((K, K), np.float16)
+    np.fill_diagonal(X, 1.0)
+    Y = gpu_linear(hq, X.view(np.uint16), packed, scale, zero, N, nbits, gs)
+    W_hat = oracle_mod.dequantize(packed, scale, zero, N, K, nbits, gs, 1)
+    assert_same_weights(Y.view(np.uint16), W_hat.T)
+
+
+def assert_same_weights(Y_bits, W_bits):
+    """Bit-equal, except that a weight of -0 comes out as +0: the output adds
+    the +0 products of the zero inputs to it (IEEE: -0 + +0 = +0)."""
+    Yf, Wf = f16_bits_to_f32(Y_bits), f16_bits_to_f32(W_bits)
+    nz = Wf != 0
+    bad = np.argwhere((Y_bits != W_bits) & (nz | (Yf != 0)))
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}: {Y_bits[tuple(bad[0])]:#06x} vs {W_bits[tuple(bad[0])]:#06x}"
+
+
+def test_matches_gpu_dequantize_then_matmul_operand(hq, oracle_mod):
+    """The kernel's W_hat equals hqq_dequantize's output: X = e_k picks columns."""
+    import torch
+
+    rng = np.random.RandomState(5)
+    N, K, nbits, gs = 96, 512, 4, 64
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    Wd = hq.hqq_dequantize(_cuda(packed), _cuda(scale), _cuda(zero), N, K, nbits, gs, 1)
+    sel = rng.choice(K, 24, replace=False)
+    X = np.zeros((24, K), np.float16)
+    X[np.arange(24), sel] = 1.0
+    Y = gpu_linear(hq, X.view(np.uint16), packed, scale, zero, N, nbits, gs)
+    torch.cuda.synchronize()
+    W = Wd.cpu().numpy().view(np.uint16)
+    assert_same_weights(Y.view(np.uint16), W[:, sel].T)
+
+
+# the 7B decoder's linear shapes at one token (decode): q/k/v/o, gate/up, down
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008),
+                                   (8, 11008, 4096), (32, 4096, 4096)])
+def test_linear_full_size(hq, oracle_mod, M, N, K):
+    rng = np.random.RandomState(M + N // 7 + K // 5)
+    nbits, gs = 4, 64
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    X16 = random_f16(rng, (M, K), std=1.0)
+    Y = gpu_linear(hq, X16, packed, scale, zero, N, nbits, gs)
+    # the oracle on a sample of output columns (rows of W are independent)
+    cols = np.sort(rng.choice(N, min(N, 768), replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    Yref, A = oracle_mod.linear(X16, packed[cols], scale[cols], zero[cols], len(cols), nbits, gs,
+                                with_abs=True)
+    check(f16_bits_to_f32(Y.view(np.uint16))[:, cols], Yref, A, K, f"{M}x{N}x{K}")
+
+
+def test_linear_repeat_and_out_buffer(hq, oracle_mod):
+    """Two calls into one preallocated output give identical bits, and rows of
+    a previous larger result do not leak into a smaller call."""
+    import torch
+
+    rng = np.random.RandomState(11)
+    N, K, nbits, gs = 64, 256, 4, 64
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs)
+    X16 = random_f16(rng, (20, K), std=1.0)
+    args = (_cuda(packed), _cuda(scale), _cuda(zero), N, nbits, gs)
+    out = torch.empty((20, N), dtype=torch.float16, device="cuda")
+    y1 = hq.hqq_linear(_cuda(X16), *args, out=out).cpu().numpy().copy()
+    y2 = hq.hqq_linear(_cuda(X16), *args, out=out).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    small = hq.hqq_linear(_cuda(X16[:3]), *args).cpu().numpy()
+    assert np.array_equal(small.view(np.uint16), y1[:3].view(np.uint16))
+    Yref, A = oracle_mod.linear(X16[:3], packed, scale, zero, N, nbits, gs, with_abs=True)
+    check(f16_bits_to_f32(small.view(np.uint16)), Yref, A, K, "small after large")

@@ -1,7 +1,7 @@
 """Python binding of the MI355X HQQ library (``libhqq.so``, C ABI in include/hqq.h).
 
 Argument marshalling only: every step of quantize / dequantize / pack / unpack
-runs in the library's HIP kernels.  PyTorch supplies device memory and the
+/ linear runs in the library's HIP kernels.  PyTorch supplies device memory and the
 current stream.  There is no fallback: if the library is not built, or a
 tensor is not on the GPU, the call raises.
 
@@ -28,7 +28,7 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack", "hqq_unpack",
-           "hqq_packed_words", "hqq_strerror")
+           "hqq_linear", "hqq_packed_words", "hqq_strerror")
 
 # tensors per kernel launch of hqq_quantize_batch
 MAX_BATCH = 24
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_pack.restype = i32
     L.hqq_unpack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
     L.hqq_unpack.restype = i32
+    L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
+    L.hqq_linear.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
     L.hqq_packed_words.restype = i64
     L.hqq_strerror.argtypes = [i32]
@@ -215,4 +217,21 @@ def hqq_unpack(packed: torch.Tensor, rows: int, cols: int, nbits: int, group_siz
                       _dev_ptr(out, "out", (torch.uint8,)), _stream(packed.device))
     if st != 0:
         raise HQQError("hqq_unpack", st)
+    return out
+
+
+def hqq_linear(X: torch.Tensor, packed, scale, zero, N: int, nbits: int, group_size: int,
+               out=None) -> torch.Tensor:
+    """Y = X . W_hat^T (fp16 [M, N]) for X fp16 [M, K] and the axis = 1
+    quantized weight W [N, K] given by (packed, scale, zero)."""
+    L = load_library()
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    st = L.hqq_linear(_dev_ptr(X, "X", _F16), M, K, _dev_ptr(packed, "packed", _U32),
+                      _dev_ptr(scale, "scale", (torch.float32,)),
+                      _dev_ptr(zero, "zero", (torch.float32,)), N, nbits, group_size,
+                      _dev_ptr(out, "out", _F16), _stream(X.device))
+    if st != 0:
+        raise HQQError("hqq_linear", st)
     return out

@@ -236,4 +236,46 @@ int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols, int nbits, in
     return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
 }
 
+int hqq_linear(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
+               const float *scale, const float *zero, int64_t N, int nbits, int group_size,
+               uint16_t *Y, void *stream)
+{
+    if (!hqq::valid_nbits(nbits) || nbits == 3)
+        return HQQ_EINVAL_NBITS;
+    if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+        M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)
+        return HQQ_EINVAL_SHAPE;
+    // gridDim.x = ceil(N / 16) and gridDim.y = ceil(M / 32) must fit the launch
+    // limits, and the kernels address X, the codes and the meta with 32-bit
+    // byte offsets
+    const int64_t kMaxBytes = int64_t(1) << 31;
+    if ((N + 15) / 16 > 0x7fffffff || (M + 31) / 32 > 0xffff || M * K * 2 >= kMaxBytes ||
+        N * (K * nbits / 32) * 4 >= kMaxBytes || N * (K / 8) * 4 >= kMaxBytes)
+        return HQQ_EINVAL_SHAPE;
+    int gshift = -1;
+    for (int b = 3; b <= 8; ++b)
+        if (group_size == (1 << b))
+            gshift = b;
+    if (gshift < 0 || K % group_size != 0)
+        return HQQ_EINVAL_GROUP;
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(scale) || !aligned16(zero) ||
+        !aligned16(Y))
+        return HQQ_EINVAL_PTR;
+    hqq::LinearArgs a{};
+    a.X = X;
+    a.packed = packed;
+    a.scale = scale;
+    a.zero = zero;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.wpr = K * nbits / 32;
+    a.gpl = K / group_size;
+    a.gs = group_size;
+    a.gshift = gshift;
+    const hipError_t e = hqq::launch_linear(nbits, a, (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
 }  // extern "C"

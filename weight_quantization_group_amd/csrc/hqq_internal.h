@@ -63,10 +63,25 @@ struct CodecArgs {
     int64_t n_words;
 };
 
+// Arguments of the fused dequantize + matmul kernels: Y[M, N] = X[M, K] .
+// W_hat[N, K]^T with W in the axis = 1 packed layout.
+struct LinearArgs {
+    const uint16_t *X;       // fp16 bits [M, K]
+    const uint32_t *packed;  // [N, wpr] words
+    const float *scale;      // [N, gpl]
+    const float *zero;       // [N, gpl]
+    uint16_t *Y;             // fp16 bits [M, N]
+    int64_t M, N, K;
+    int64_t wpr;             // words per row of W: K * nbits / 32
+    int64_t gpl;             // groups per row of W: K / gs
+    int gs, gshift;          // group size and its log2
+};
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_solve(int nbits, int group_size, int axis, const SolveArgs &a, hipStream_t s);
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
+hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s);
 
 }  // namespace hqq

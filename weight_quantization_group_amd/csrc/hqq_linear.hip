@@ -1,0 +1,479 @@
+// hqq_linear.hip -- Y = X . W_hat^T with W_hat dequantized from packed codes
+// on the fly, on gfx950 matrix cores.
+//
+// This is the consumer of the codes: the HQQLinear forward of the lnwmold.com
+// HQQ guide (section 3.2: the quantized layer is called like the Linear it
+// replaces and computes in compute_dtype, fp16 here; section 4.1: a backend
+// fuses the dequantization and the matrix product into one kernel and needs
+// axis = 1; section 4.2: axis = 1 4-bit layers with optimized kernels).  W is
+// the axis = 1 layout, so a packed word holds C = 32 / nbits consecutive k of
+// one output row n, and the group of gs consecutive k shares (scale, zero).
+//
+// Exact dequantization.  W_hat[n][k] is the fp16 rounding of the fp32 quotient
+// (q - zero) / scale, both steps round-to-nearest-even, as the dequantize
+// kernel computes it.  Here the quotient comes from one fp64 product instead
+// of an fp32 division: with a = fl32(q - zero) and R = fl64(1 / scale),
+// fl32(a * R) equals fl32(a / scale).  The fp64 product is within 2^-52 of
+// a / scale (relative), while a quotient of two 24-bit significands is never
+// a rounding midpoint of fp32 and never closer to one than 2^-49 relative, so
+// both round to the same fp32 value.  Products of fp16 inputs are exact in
+// the fp32 accumulators, so the kernel differs from an exact dot product of
+// X with W_hat only by fp32 accumulation order and the final fp16 rounding.
+//
+// Code tables (4-bit codes, groups of 32 or more).  A group has only 16
+// distinct W_hat values, so a lane computes them once (16 exact quotients)
+// and keeps them as two 16-byte tables, the low and the high bytes, in 8
+// VGPRs.  A packed word then becomes 8 fp16 values with v_perm_b32 byte
+// lookups (two 8-entry halves joined on bit 3 of each code with v_bfi_b32):
+// about 3 VALU operations per weight instead of about 10 for the quotient.
+// The lookups give the 8 k of a word in the order 0,2,4,6,1,3,5,7; the X run
+// that meets it in the MFMA is permuted the same way (a dot product does not
+// depend on the k order inside an MFMA), and the other code widths produce
+// the same order.
+//
+// Skinny kernel (few rows of X: decode and small batches).  A workgroup owns
+// 16 output columns n (an MFMA 16x16x32 tile) and its 4, 8 or 16 waves split
+// K.  Lane
+// l works on row n = l % 16 and, in each 256-wide step of k, on the 64
+// consecutive k at 64 * (l / 16): one group (gs >= 64), the codes in 16 or 32
+// bytes, dequantized in registers to the eight 8-half B operands of eight
+// MFMAs.  When X fits (M * K * 2 bytes <= 64 KiB), the workgroup stages it in
+// LDS once, in operand order, and the A operands are single ds_read_b128s;
+// otherwise every lane reads its X runs from global memory (X is small and
+// stays in cache).  The waves add their partial sums through LDS at the end.
+#include "hqq_internal.h"
+
+namespace hqq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kLaneK = 64;                // consecutive k per lane per step
+constexpr int kStepK = 4 * kLaneK;        // k per wave step
+constexpr int kXldsMax = 64 * 1024;       // bytes of X staged in LDS, at most
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// an 8-k run of fp16 X (natural order) in operand order 0,2,4,6,1,3,5,7
+__device__ __forceinline__ uint4 run_order(uint4 x)
+{
+    return uint4{perm(x.y, x.x, 0x05040100u), perm(x.w, x.z, 0x05040100u),
+                 perm(x.y, x.x, 0x07060302u), perm(x.w, x.z, 0x07060302u)};
+}
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed fp16 pair, round-to-nearest-even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t f16x2(float lo, float hi)
+{
+    const half2v h = __builtin_convertvector(float2v{lo, hi}, half2v);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// the exact dequantized value of code c (fp32, before the fp16 rounding)
+__device__ __forceinline__ float wq(float c, float z, double R)
+{
+    return (float)((double)(c - z) * R);
+}
+
+// The 16 fp16 values of a 4-bit group as byte tables: L[q] holds the low
+// bytes of codes 4q .. 4q+3, H[q] the high bytes.
+struct Tab4 {
+    uint32_t L[4], H[4];
+};
+
+__device__ __forceinline__ Tab4 make_tab4(float s, float z)
+{
+    const double R = 1.0 / (double)s;
+    uint32_t P[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        P[i] = f16x2(wq((float)(2 * i), z, R), wq((float)(2 * i + 1), z, R));
+    Tab4 t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        t.L[q] = perm(P[2 * q + 1], P[2 * q], 0x06040200u);
+        t.H[q] = perm(P[2 * q + 1], P[2 * q], 0x07050301u);
+    }
+    return t;
+}
+
+// 8 codes of a 4-bit word -> 8 fp16 in operand order (0,2,4,6,1,3,5,7)
+__device__ __forceinline__ uint4 lookup4(const Tab4 &t, uint32_t w)
+{
+    // byte q of se / so: low 3 bits of the even / odd code of byte q; the
+    // masks are 0xff where bit 3 of that code is set (v_perm replicates the
+    // sign bit of a byte for selector values 8..11)
+    const uint32_t se = w & 0x07070707u, so = (w >> 4) & 0x07070707u;
+    const uint32_t me = perm(w << 12, w << 4, 0x090B080Au);
+    const uint32_t mo = perm(w << 8, w, 0x090B080Au);
+    auto pick = [](uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); };
+    const uint32_t lo_e = pick(me, perm(t.L[3], t.L[2], se), perm(t.L[1], t.L[0], se));
+    const uint32_t hi_e = pick(me, perm(t.H[3], t.H[2], se), perm(t.H[1], t.H[0], se));
+    const uint32_t lo_o = pick(mo, perm(t.L[3], t.L[2], so), perm(t.L[1], t.L[0], so));
+    const uint32_t hi_o = pick(mo, perm(t.H[3], t.H[2], so), perm(t.H[1], t.H[0], so));
+    return uint4{perm(hi_e, lo_e, 0x05010400u), perm(hi_e, lo_e, 0x07030602u),
+                 perm(hi_o, lo_o, 0x05010400u), perm(hi_o, lo_o, 0x07030602u)};
+}
+
+// Groups whose (scale, zero) a lane needs per step: 1 (gs >= 64), 2 (gs 32,
+// one per 32 k) or 8 (gs 8 or 16, one per 8-k run).
+constexpr int groups_per_chunk(int gs) { return gs >= 64 ? 1 : gs == 32 ? 2 : 8; }
+
+// One wave step's codes and meta for one lane (its 64-k chunk), and the X
+// runs of its m tiles when X is read from global memory.
+template <int NB, int GPC>
+struct StepBuf {
+    uint32_t w[2 * NB];
+    float s[GPC], z[GPC];
+};
+
+template <int MT>
+struct XRuns {
+    uint4 x[MT][8];
+};
+
+// Where a lane's chunk starts (k0) and where its second 32 k start (kh): k0
+// + 32, or k0 again where that is K or beyond (K % 64 == 32; those products
+// are masked to zero).  A chunk past K is moved to the last 32 k (in bounds;
+// masked to zero as well).  Offsets are 32-bit: the host keeps every array
+// below 2^31 bytes, so each load is a uniform base plus a lane offset.
+struct Chunk {
+    uint32_t k0, kh;
+};
+
+template <bool KT>
+__device__ __forceinline__ Chunk lane_chunk(uint32_t kbase, int grp, uint32_t K)
+{
+    uint32_t k0 = kbase + kLaneK * grp;
+    if constexpr (KT)
+        k0 = k0 < K ? k0 : K - 32;
+    const uint32_t kh = KT ? (k0 + 32 < K ? k0 + 32 : k0) : k0 + 32;
+    return Chunk{k0, kh};
+}
+
+template <typename T>
+__device__ __forceinline__ const T *at(const void *base, uint32_t byte_off)
+{
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+template <int NB, int GPC>
+__device__ __forceinline__ void load_step(StepBuf<NB, GPC> &b, const LinearArgs &a, Chunk c,
+                                          uint32_t nw, uint32_t ng)
+{
+    // nw: first word of the lane's row, ng: its first group
+    const uint32_t wa = 4 * (nw + c.k0 * NB / 32), wb = 4 * (nw + c.kh * NB / 32);
+    if constexpr (NB == 1) {
+        b.w[0] = *at<uint32_t>(a.packed, wa);
+        b.w[1] = *at<uint32_t>(a.packed, wb);
+    } else if constexpr (NB == 2) {
+        const uint2 u = *at<uint2>(a.packed, wa);
+        const uint2 v = *at<uint2>(a.packed, wb);
+        b.w[0] = u.x; b.w[1] = u.y; b.w[2] = v.x; b.w[3] = v.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int q = 0; q < NB / 4; ++q) {
+                const uint4 v = *at<uint4>(a.packed, (h ? wb : wa) + 16 * q);
+                b.w[NB * h + 4 * q + 0] = v.x; b.w[NB * h + 4 * q + 1] = v.y;
+                b.w[NB * h + 4 * q + 2] = v.z; b.w[NB * h + 4 * q + 3] = v.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < GPC; ++i) {
+        const uint32_t kk = GPC == 1 ? c.k0 : GPC == 2 ? (i ? c.kh : c.k0) : (i < 4 ? c.k0 : c.kh) + 8 * (i & 3);
+        const uint32_t g = 4 * (ng + (kk >> a.gshift));
+        b.s[i] = *at<float>(a.scale, g);
+        b.z[i] = *at<float>(a.zero, g);
+    }
+}
+
+// xr: element index of the first X element of each of the lane's rows
+template <int MT>
+__device__ __forceinline__ void load_x(XRuns<MT> &b, const LinearArgs &a, Chunk c,
+                                       const uint32_t (&xr)[MT])
+{
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b.x[u][j] = *at<uint4>(a.X, 2 * (xr[u] + c.k0) + 16 * j);
+            b.x[u][4 + j] = *at<uint4>(a.X, 2 * (xr[u] + c.kh) + 16 * j);
+        }
+    }
+}
+
+// B operand j (8-k run j of the chunk) by direct quotients, operand order
+template <int NB, int GPC>
+__device__ __forceinline__ uint4 dequant_run(const uint32_t *w, int j, const float *s,
+                                             const float *z)
+{
+    constexpr uint32_t MASK = (1u << NB) - 1u;
+    constexpr int ord[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    const int gi = GPC == 1 ? 0 : GPC == 2 ? (j >> 2) : j;
+    const double R = 1.0 / (double)s[gi];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int bit = (8 * j + ord[i]) * NB;
+        v[i] = wq((float)((w[bit / 32] >> (bit % 32)) & MASK), z[gi], R);
+    }
+    return uint4{f16x2(v[0], v[1]), f16x2(v[2], v[3]), f16x2(v[4], v[5]), f16x2(v[6], v[7])};
+}
+
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m)
+{
+    return uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+}
+
+__device__ __forceinline__ float4v mfma(uint4 A, uint4 B, float4v c)
+{
+    half8 a, b;
+    __builtin_memcpy(&a, &A, 16);
+    __builtin_memcpy(&b, &B, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// X staged in LDS: row m of the workgroup's X rows at xs + m * xrow (uint4
+// units), runs in operand order; the row pitch is K / 8 + 1 runs so that the
+// 16 rows of an operand fall in different banks.
+template <bool KT, int NB, int MT, int GPC, bool XL>
+__device__ __forceinline__ void compute_step(const StepBuf<NB, GPC> &b, const XRuns<XL ? 1 : MT> &xg,
+                                             uint32_t km0, uint32_t km1, const uint4 *xs,
+                                             const uint32_t (&xm)[MT], Chunk c,
+                                             float4v (&acc)[MT])
+{
+    uint4 B[8];
+    if constexpr (NB == 4 && GPC == 1) {
+        const Tab4 t = make_tab4(b.s[0], b.z[0]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            B[j] = lookup4(t, b.w[j]);
+    } else if constexpr (NB == 4 && GPC == 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Tab4 t = make_tab4(b.s[h], b.z[h]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                B[4 * h + j] = lookup4(t, b.w[4 * h + j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            B[j] = dequant_run<NB, GPC>(b.w, j, b.s, b.z);
+    }
+    // K % 256 != 0: a lane whose chunk (or its second half) lies past K adds
+    // zeros; the operands are cleared with integer masks (a select would
+    // become a branch that waits for every load in flight)
+    if constexpr (KT) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            B[j] = and4(B[j], j < 4 ? km0 : km1);
+    }
+    const uint32_t r0 = c.k0 >> 3, r1 = c.kh >> 3;
+#pragma unroll
+    for (int u = 0; u < MT; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint4 A;
+            if constexpr (XL)
+                A = xs[xm[u] + (j < 4 ? r0 + j : r1 + j - 4)];
+            else
+                A = run_order(xg.x[u][j]);
+            if constexpr (KT)
+                A = and4(A, j < 4 ? km0 : km1);
+            acc[u] = mfma(A, B[j], acc[u]);
+        }
+}
+
+// One K step in flight per wave: the next step's codes load while the
+// current one is computed and other waves run in the meantime.  A second
+// register buffer per wave costs more occupancy than it gains.
+// resident waves per SIMD the register allocation must allow
+constexpr int lin_waves_per_simd(int nb, int mt, int gpc, bool xl)
+{
+    return !xl ? (mt > 1 ? 3 : 4) : nb == 8 || mt > 1 || gpc == 8 ? 4 : 6;
+}
+
+template <bool KT, int NB, int MT, int GPC, bool XL, int WPB>
+__global__ __launch_bounds__(WPB * 64)
+__attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void linear_skinny_kernel(LinearArgs a)
+{
+    extern __shared__ uint4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane16 = lane & 15, grp = lane >> 4;
+    const uint32_t K = (uint32_t)a.K;
+    const int64_t n_raw = (int64_t)blockIdx.x * 16 + lane16;
+    const uint32_t n = (uint32_t)(n_raw < a.N ? n_raw : a.N - 1);
+    const uint32_t nw = n * (uint32_t)a.wpr, ng = n * (uint32_t)a.gpl;
+    const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+    const int mrows = (int)(a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT);
+    // X rows of the lane's m tiles (rows past M repeat the last; their
+    // outputs are not stored): LDS run index, or element index of X
+    const uint32_t xrow = K / 8 + 1;
+    uint32_t xr[MT];
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+        const int r = 16 * u + lane16 < mrows ? 16 * u + lane16 : mrows - 1;
+        xr[u] = XL ? (uint32_t)r * xrow : (uint32_t)((m0 + r) * a.K);
+    }
+
+    // X rows of this workgroup into LDS, runs in operand order
+    if constexpr (XL) {
+        const uint32_t runs = K / 8;
+        const uint4 *xg = reinterpret_cast<const uint4 *>(a.X + m0 * a.K);
+        for (uint32_t c = threadIdx.x; c < (uint32_t)mrows * runs; c += WPB * 64) {
+            const uint32_t m = c / runs, r = c - m * runs;
+            lds[m * xrow + r] = run_order(xg[c]);
+        }
+        __syncthreads();
+    }
+
+    // this wave's K steps: wave, wave + WPB, ...
+    const int n_steps = (int)((K + kStepK - 1) / kStepK);
+    const int my = n_steps > wave ? (n_steps - wave + WPB - 1) / WPB : 0;
+    auto kbase = [&](int i) { return (uint32_t)(wave + i * WPB) * kStepK; };
+
+    float4v acc[MT];
+#pragma unroll
+    for (int u = 0; u < MT; ++u)
+        acc[u] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // X from global memory: the step's X runs load before the next step's
+    // codes, so that waiting for them does not wait for the codes
+    StepBuf<NB, GPC> buf;
+    XRuns<XL ? 1 : MT> xg;
+    if (my > 0)
+        load_step(buf, a, lane_chunk<KT>(kbase(0), grp, K), nw, ng);
+    for (int i = 0; i < my; ++i) {
+        const Chunk c = lane_chunk<KT>(kbase(i), grp, K);
+        const uint32_t k0 = kbase(i) + kLaneK * grp;
+        const uint32_t km0 = k0 < K ? 0xffffffffu : 0u;
+        const uint32_t km1 = k0 + 32 < K ? 0xffffffffu : 0u;
+        if constexpr (!XL)
+            load_x(xg, a, c, xr);
+        const StepBuf<NB, GPC> cur = buf;
+        if (i + 1 < my)
+            load_step(buf, a, lane_chunk<KT>(kbase(i + 1), grp, K), nw, ng);
+        compute_step<KT, NB, MT, GPC, XL>(cur, xg, km0, km1, lds, xr, c, acc);
+    }
+
+    // add the waves' partial sums: red[wave][u * 4 + r][lane]
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int u = 0; u < MT; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            red[(wave * MT * 4 + u * 4 + r) * 64 + lane] = acc[u][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += WPB * 64) {
+        const int v = idx >> 6, l = idx & 63;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPB; ++w)
+            s += red[(w * MT * 4 + v) * 64 + l];
+        // accumulator r of lane l is D[4 * (l / 16) + r][l % 16] of tile u
+        const int u = v >> 2, r = v & 3;
+        const int64_t m = m0 + 16 * u + 4 * (l >> 4) + r;
+        const int64_t nn = (int64_t)blockIdx.x * 16 + (l & 15);
+        if (m < a.M && nn < a.N) {
+            const _Float16 h = (_Float16)s;
+            __builtin_memcpy(&a.Y[m * a.N + nn], &h, 2);
+        }
+    }
+}
+
+// Waves per workgroup (they split K): enough workgroups x waves to give every
+// SIMD about four waves, but no more waves than K steps.
+inline int lin_waves(int64_t blocks, int64_t K)
+{
+    const int64_t steps = (K + kStepK - 1) / kStepK;
+    int w = blocks >= 1024 ? 4 : blocks >= 512 ? 8 : 16;
+    while (w > 4 && w > steps)
+        w /= 2;
+    return w;
+}
+
+template <int NB, int MT, int GPC, bool XL, int WPB>
+hipError_t launch_wpb(const LinearArgs &a, dim3 grid, hipStream_t s)
+{
+    size_t lds = (size_t)WPB * MT * 4 * 64 * sizeof(float);
+    if (XL) {
+        const int64_t rows = a.M < 16 * MT ? a.M : 16 * MT;
+        const size_t x = (size_t)rows * (size_t)(a.K / 8 + 1) * 16;
+        lds = x > lds ? x : lds;
+    }
+    if (a.K % kStepK != 0)
+        hipLaunchKernelGGL((linear_skinny_kernel<true, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
+                           lds, s, a);
+    else
+        hipLaunchKernelGGL((linear_skinny_kernel<false, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
+                           lds, s, a);
+    return hipGetLastError();
+}
+
+template <int NB, int MT, int GPC, bool XL>
+hipError_t launch_one(const LinearArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+    switch (lin_waves((int64_t)grid.x * grid.y, a.K)) {
+    case 4: return launch_wpb<NB, MT, GPC, XL, 4>(a, grid, s);
+    case 8: return launch_wpb<NB, MT, GPC, XL, 8>(a, grid, s);
+    default: return launch_wpb<NB, MT, GPC, XL, 16>(a, grid, s);
+    }
+}
+
+template <int NB, int MT, int GPC>
+hipError_t launch_xl(const LinearArgs &a, hipStream_t s)
+{
+    const int64_t rows = a.M < 16 * MT ? a.M : 16 * MT;
+    if (rows * (a.K / 8 + 1) * 16 <= kXldsMax)
+        return launch_one<NB, MT, GPC, true>(a, s);
+    return launch_one<NB, MT, GPC, false>(a, s);
+}
+
+template <int NB, int MT>
+hipError_t launch_gpc(const LinearArgs &a, hipStream_t s)
+{
+    switch (groups_per_chunk(a.gs)) {
+    case 1: return launch_xl<NB, MT, 1>(a, s);
+    case 2: return launch_xl<NB, MT, 2>(a, s);
+    default: return launch_xl<NB, MT, 8>(a, s);
+    }
+}
+
+template <int NB>
+hipError_t launch_nb(const LinearArgs &a, hipStream_t s)
+{
+    // M > 32 runs ceil(M / 32) row blocks of 32
+    if (a.M <= 16)
+        return launch_gpc<NB, 1>(a, s);
+    return launch_gpc<NB, 2>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s)
+{
+    switch (nbits) {
+    case 1: return launch_nb<1>(a, s);
+    case 2: return launch_nb<2>(a, s);
+    case 4: return launch_nb<4>(a, s);
+    case 8: return launch_nb<8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hqq
