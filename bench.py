@@ -2,6 +2,7 @@
 """Benchmark of the HQQ solve on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --op linear [--steps K] [--warmup W]
 
 A step quantizes every tensor of the workload once, with all fp16 inputs
 already resident in HBM: consecutive tensors of one format go to
@@ -16,6 +17,16 @@ Prints one JSON line: the metric (GB/s of fp16 weights quantized), the
 roofline of the solve kernel (measured with HIP events around each launch
 inside the timed region, on the launch stream), and the CPU oracle timed on
 this host on a bounded sample.
+
+--op linear measures the consumer of the codes instead: one decode token of
+the same 7B shape through the quantized layers (HQQ guide, sections 3.2 and
+4.1: the layer's forward dequantizes and multiplies in fp16), i.e. the 224
+linear layers of 32 decoder layers at batch 1, each an hqq_linear call on
+4-bit g64 axis=1 codes.  The 224 calls are captured in one HIP graph and
+replayed, so the timing is the GPU's; the same 224 products with fp16
+weights (torch.matmul, hipBLASLt) are timed the same way beside it.  Codes
+are seeded random, meta from a synthetic min/max distribution, activations
+N(0, 1).
 """
 from __future__ import annotations
 
@@ -128,6 +139,153 @@ def _cpu_job(job):
     return W.size, time.perf_counter() - t0
 
 
+LINEAR_METRIC = "tokens/s, 7B decode (batch 1) through all 224 HQQ 4b g64 linear layers"
+
+
+def linear_cpu_baseline(nbits: int, gs: int, seconds: float = 15.0):
+    """The oracle's linear layer (fp64, single thread) on 4096 x 4096 decode
+    products, repeated for about `seconds`; scaled to tokens/s of the 224-layer
+    7B step by weight count."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.RandomState(0)
+    N = K = 4096
+    qmax = (1 << nbits) - 1
+    codes = rng.randint(0, qmax + 1, size=(N, K)).astype(np.uint8)
+    packed = oracle.pack(codes, nbits, 1)
+    scale = np.full((N, K // gs), qmax / 0.06, np.float32)
+    zero = np.full((N, K // gs), qmax / 2, np.float32)
+    X = (rng.standard_normal((1, K)).astype(np.float16)).view(np.uint16)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        oracle.linear(X, packed, scale, zero, N, nbits, gs)
+        n += 1
+    dt = time.perf_counter() - t0
+    w_per_s = n * N * K / dt
+    return dict(value=round(w_per_s / LLAMA7B_WEIGHTS, 6), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n} oracle linear products of 1 x 4096 by a 4096 x 4096 4-bit g{gs} weight "
+                       f"({dt:.1f} s, one thread), scaled by weight count to the 224-layer step",
+                weights_per_s=round(w_per_s, 1))
+
+
+# the 7B decoder's linear shapes (N, K) per layer: q, k, v, o, gate, up, down
+LLAMA7B_LINEARS = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+LLAMA7B_LAYERS = 32
+LLAMA7B_WEIGHTS = LLAMA7B_LAYERS * sum(n * k for n, k in LLAMA7B_LINEARS)
+
+
+def bench_linear(args):
+    import torch
+
+    import weight_quantization_group_amd as hq
+
+    hq.load_library()
+    dev = torch.device("cuda:0")
+    nbits, gs = 4, 64
+    qmax = (1 << nbits) - 1
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    layers = []
+    for li in range(LLAMA7B_LAYERS):
+        for (N, K) in LLAMA7B_LINEARS:
+            packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (N, K * nbits // 32), dtype=torch.int32,
+                                   device=dev, generator=gen)
+            lo = -(0.03 + 0.01 * torch.rand((N, K // gs), device=dev, generator=gen)).abs()
+            hi = (0.03 + 0.01 * torch.rand((N, K // gs), device=dev, generator=gen)).abs() + 1e-3
+            scale = (qmax / (hi - lo)).float()
+            zero = (-lo * scale).float()
+            layers.append((N, K, packed, scale, zero))
+    X = {K: torch.randn((1, K), device=dev, generator=gen).half() for K in (4096, 11008)}
+    Y = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+    torch.cuda.synchronize()
+
+    def token():
+        for (N, K, p, s, z) in layers:
+            hq.hqq_linear(X[K], p, s, z, N, nbits, gs, out=Y[N])
+
+    def graph_of(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g, steps, warmup):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+    g = graph_of(token)
+    ms_ev, ms_wall = timed(g, args.steps, args.warmup)
+    del g
+
+    # the fp16 reference: the same 224 products with 224 distinct fp16 weights
+    # (12.95 GB) through torch.matmul (hipBLASLt)
+    Wf = []
+    for (N, K, _, _, _) in layers:
+        w = torch.empty((N, K), dtype=torch.float16, device=dev)
+        w.normal_(0.0, 0.02, generator=gen)
+        Wf.append((N, K, w.t()))
+    Yf = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+
+    def token_fp16():
+        for (N, K, wt) in Wf:
+            torch.matmul(X[K], wt, out=Yf[N])
+
+    gf = graph_of(token_fp16)
+    ms_fp16, _ = timed(gf, args.steps, args.warmup)
+    del gf, Wf
+
+    bytes_per_token = sum(N * K * nbits / 8 + N * (K // gs) * 8 + K * 2 + N * 2
+                          for (N, K) in LLAMA7B_LINEARS) * LLAMA7B_LAYERS
+    gbs = bytes_per_token / (ms_ev * 1e-3) / 1e9
+    out = {
+        "metric": LINEAR_METRIC,
+        "value": round(1e3 / ms_ev, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_ev, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode_b1_4b_g64", "linears": len(layers), "M": 1,
+                   "weights": LLAMA7B_WEIGHTS, "nbits": nbits, "group_size": gs, "axis": 1},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "linear_skinny_kernel (4-bit, g64)",
+                     "bytes_per_step": int(bytes_per_token),
+                     "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
+        "fp16_matmul": {"ms_per_step": round(ms_fp16, 4), "tokens_per_s": round(1e3 / ms_fp16, 3),
+                        "speedup": round(ms_fp16 / ms_ev, 3)},
+        "wall_ms_per_step": round(ms_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = linear_cpu_baseline(nbits, gs)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +296,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--op", choices=("solve", "linear"), default="solve",
+                    help="solve: quantize the 7B stack (default); linear: one decode token "
+                         "through the quantized layers")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,6 +315,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.op == "linear":
+        bench_linear(args)
+        return
     hq.load_library()
     dev = torch.device("cuda:0")
     tensors = synth.workload(args.workload)
