@@ -140,6 +140,26 @@ def _cpu_job(job):
 
 
 LINEAR_METRIC = "tokens/s, 7B decode (batch 1) through all 224 HQQ 4b g64 linear layers"
+# HBM traffic of the linear kernel per step, from the committed rocprofv3
+# summary; used only while the kernel's sources are the ones it was taken with
+LINEAR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_4b_g64_llama7b_decode.traffic.json")
+LINEAR_KERNEL_SOURCES = ["weight_quantization_group_amd/csrc/hqq_linear.hip",
+                         "weight_quantization_group_amd/csrc/hqq_internal.h"]
+
+
+def linear_counter_summary():
+    try:
+        with open(LINEAR_TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in LINEAR_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return t if t.get("kernel_source_sha256") == h.hexdigest() else None
 
 
 def linear_cpu_baseline(nbits: int, gs: int, seconds: float = 15.0):
@@ -233,7 +253,20 @@ def bench_linear(args):
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
-    g = graph_of(token)
+    if args.calib_copy:
+        a = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    class Eager:
+        def __init__(self, fn):
+            self.replay = fn
+
+    # --eager: plain launches (for profilers that count per dispatch); the
+    # timing then includes the host's launch cost
+    g = Eager(token) if args.eager else graph_of(token)
     ms_ev, ms_wall = timed(g, args.steps, args.warmup)
     del g
 
@@ -250,7 +283,7 @@ def bench_linear(args):
         for (N, K, wt) in Wf:
             torch.matmul(X[K], wt, out=Yf[N])
 
-    gf = graph_of(token_fp16)
+    gf = Eager(token_fp16) if args.eager else graph_of(token_fp16)
     ms_fp16, _ = timed(gf, args.steps, args.warmup)
     del gf, Wf
 
@@ -273,13 +306,15 @@ def bench_linear(args):
         "config": {"workload": "llama7b_decode_b1_4b_g64", "linears": len(layers), "M": 1,
                    "weights": LLAMA7B_WEIGHTS, "nbits": nbits, "group_size": gs, "axis": 1},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (lambda c: c["hbm_bytes_per_step"] if c else None)(linear_counter_summary()),
                      "kernel": "linear_skinny_kernel (4-bit, g64)",
                      "bytes_per_step": int(bytes_per_token),
                      "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
         "fp16_matmul": {"ms_per_step": round(ms_fp16, 4), "tokens_per_s": round(1e3 / ms_fp16, 3),
                         "speedup": round(ms_fp16 / ms_ev, 3)},
         "wall_ms_per_step": round(ms_wall, 4),
+        "launch": "eager" if args.eager else "hip graph of the 224 calls",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = linear_cpu_baseline(nbits, gs)
@@ -296,6 +331,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="--op linear: plain launches instead of a captured HIP graph")
     ap.add_argument("--op", choices=("solve", "linear"), default="solve",
                     help="solve: quantize the 7B stack (default); linear: one decode token "
                          "through the quantized layers")
