@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --op linear [--steps K] [--warmup W]
+    python bench.py --op streamed [--steps K] [--warmup W]
 
 A step quantizes every tensor of the workload once, with all fp16 inputs
 already resident in HBM: consecutive tensors of one format go to
@@ -27,6 +28,12 @@ replayed, so the timing is the GPU's; the same 224 products with fp16
 weights (torch.matmul, hipBLASLt) are timed the same way beside it.  Codes
 are seeded random, meta from a synthetic min/max distribution, activations
 N(0, 1).
+
+--op streamed measures the solve over weights held in host memory (models
+larger than HBM): the 7B stack in pinned host memory, hqq_quantize_streamed
+copying double-buffered chunks of 512 MiB over PCIe while the solve runs.
+Its bound is the host-to-device link, reported beside a plain pinned copy
+of the same bytes.
 """
 from __future__ import annotations
 
@@ -321,6 +328,86 @@ def bench_linear(args):
     print(json.dumps(out), flush=True)
 
 
+# PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+PCIE_PEAK_GBS = 63.0
+
+
+def bench_streamed(args):
+    import torch
+
+    import synth
+    import weight_quantization_group_amd as hq
+
+    hq.load_library()
+    dev = torch.device("cuda:0")
+    tensors = synth.workload(args.workload)
+    nb, gs, ax = tensors[0]["nbits"], tensors[0]["group_size"], tensors[0]["axis"]
+    assert all((t["nbits"], t["group_size"], t["axis"]) == (nb, gs, ax) for t in tensors)
+    n_weights = sum(t["rows"] * t["cols"] for t in tensors)
+    host = torch.empty(n_weights, dtype=torch.int16, pin_memory=True)
+    items, off = [], 0
+    for t in tensors:
+        W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
+        synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+        h = host[off:off + W.numel()].view(t["rows"], t["cols"])
+        h.copy_(W.view(torch.int16))
+        off += W.numel()
+        del W
+        items.append((h, torch.empty(hq.packed_shape(t["rows"], t["cols"], nb, ax), dtype=torch.int32, device=dev),
+                      torch.empty(hq.meta_shape(t["rows"], t["cols"], gs, ax), dtype=torch.float32, device=dev),
+                      torch.empty(hq.meta_shape(t["rows"], t["cols"], gs, ax), dtype=torch.float32, device=dev)))
+    staging = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cs, ks = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step():
+        hq.hqq_quantize_streamed(items, nb, gs, ax, staging, copy_stream=cs, compute_stream=ks,
+                                 iters=args.iters)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the link alone: the same bytes, pinned host -> device, in 512 MiB pieces
+    dst = staging.view(torch.int16)
+    half = dst.numel() // 2
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(0, host.numel(), half):
+        dst[:min(half, host.numel() - i)].copy_(host[i:i + half], non_blocking=True)
+    torch.cuda.synchronize()
+    copy_ms = (time.perf_counter() - t0) * 1e3
+    gbs = 2.0 * n_weights / (ms * 1e-3) / 1e9
+    copy_gbs = 2.0 * n_weights / (copy_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"GB/s of fp16 weights quantized from pinned host memory (HQQ {nb}b g{gs}, {args.iters} it), "
+                  f"workload {args.workload}",
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
+                   "staging_bytes": staging.numel(), "nbits": nb, "group_size": gs, "axis": ax,
+                   "iters": args.iters},
+        "roofline": {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "pinned_copy_GBs": round(copy_gbs, 2), "frac_of_copy": round(gbs / copy_gbs, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,9 +420,9 @@ def main():
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--eager", action="store_true",
                     help="--op linear: plain launches instead of a captured HIP graph")
-    ap.add_argument("--op", choices=("solve", "linear"), default="solve",
+    ap.add_argument("--op", choices=("solve", "linear", "streamed"), default="solve",
                     help="solve: quantize the 7B stack (default); linear: one decode token "
-                         "through the quantized layers")
+                         "through the quantized layers; streamed: the solve from pinned host memory")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -354,6 +441,9 @@ def main():
         sys.exit(2)
     if args.op == "linear":
         bench_linear(args)
+        return
+    if args.op == "streamed":
+        bench_streamed(args)
         return
     hq.load_library()
     dev = torch.device("cuda:0")

@@ -113,6 +113,42 @@ HQQ_API int hqq_quantize_batch(const hqq_tensor *tensors, int n,
                                int nbits, int group_size, int axis,
                                int iters, float p, float beta0, float kappa, void *stream);
 
+/* One tensor of a streamed quantize call: W in HOST memory, outputs on the
+ * device (16-byte aligned; layouts as for hqq_quantize). */
+typedef struct hqq_host_tensor {
+    const uint16_t *W;   /* fp16 bits [rows, cols], host memory (page-locked for
+                          * the copies to overlap the solve), read only */
+    int64_t rows, cols;
+    uint32_t *packed;    /* device, hqq_packed_words(rows, cols, nbits, axis) words, written */
+    float *scale;        /* device, rows*cols/group_size values, written */
+    float *zero;         /* device, rows*cols/group_size values, written */
+} hqq_host_tensor;
+
+/* Quantize weights that live in host memory (lnwmold.com HQQ guide section
+ * 6.3: models too large for the device are quantized a batch of layers at a
+ * time), with results identical to hqq_quantize on device copies of them.
+ * The weights cross PCIe once, in chunks of whole row blocks (whole groups
+ * and packed words) that fit half of the caller's device staging buffer:
+ * chunk c is copied into half c % 2 on copy_stream while the solve of chunk
+ * c - 1 runs on compute_stream.  Everything is enqueued asynchronously; the
+ * results are complete when compute_stream has finished, and the host
+ * weights and the staging buffer must stay untouched until then.
+ *   tensors        HOST array of n descriptors (read during the call only)
+ *   staging        device buffer, 16-byte aligned, staging_bytes long; each
+ *                  half must hold at least one block unit of every tensor
+ *                  (lcm(group_size, codes per word) rows for axis 0, up to
+ *                  16 rows for axis 1, times cols * 2 bytes), else
+ *                  HQQ_EINVAL_SHAPE
+ *   copy_stream, compute_stream  HIP streams (may be the same stream)
+ * Every descriptor is validated before anything is enqueued.  n = 0 is a
+ * no-op.  The call creates four HIP events and releases them before it
+ * returns (pending ones when they complete); it allocates no memory. */
+HQQ_API int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n,
+                                  int nbits, int group_size, int axis,
+                                  int iters, float p, float beta0, float kappa,
+                                  void *staging, int64_t staging_bytes,
+                                  void *copy_stream, void *compute_stream);
+
 /* Dequantize: W_hat = fp16_round_half_even((W_q - zero) / scale) with an
  * IEEE fp32 subtraction and division (lnwmold.com HQQ guide section 3.2,
  * HQQLinear.dequantize()).  W_hat is fp16 bits [rows, cols], written. */

@@ -38,8 +38,9 @@ def test_header_codes_match():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
-    assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack",
-                               "hqq_unpack", "hqq_linear", "hqq_packed_words", "hqq_strerror"])
+    assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_streamed",
+                               "hqq_dequantize", "hqq_pack", "hqq_unpack", "hqq_linear",
+                               "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -128,6 +129,33 @@ def test_linear_rejects(lib):
     assert call(X=None) == E["PTR"]
     assert call(Y=MIS) == E["PTR"]
     assert call(scale=MIS) == E["PTR"]
+
+
+def test_streamed_rejects(lib):
+    import weight_quantization_group_amd as w
+
+    def call(tensors, n=None, staging=A, staging_bytes=1 << 20, nbits=4, gs=64, axis=1, iters=20):
+        arr = (w.HqqHostTensor * max(len(tensors), 1))(*tensors)
+        return lib.hqq_quantize_streamed(ctypes.cast(arr, ctypes.c_void_p),
+                                         len(tensors) if n is None else n, nbits, gs, axis, iters,
+                                         0.7, 10.0, 1.01, staging, staging_bytes, None, None)
+
+    host = 0x7000  # host W is only checked for NULL before anything is enqueued
+    ok = w.HqqHostTensor(host, 64, 128, 0x1000, 0x2000, 0x3000)
+    assert call([ok], n=-1) == E["SHAPE"]
+    assert call([], n=0) == E["OK"]
+    assert call([ok], iters=-1) == E["PARAM"]
+    assert call([ok], staging=None) == E["PTR"]
+    assert call([ok], staging=MIS) == E["PTR"]
+    assert call([w.HqqHostTensor(0, 64, 128, 0x1000, 0x2000, 0x3000)]) == E["PTR"]
+    assert call([w.HqqHostTensor(host, 64, 128, 0x1004, 0x2000, 0x3000)]) == E["PTR"]
+    assert call([ok], nbits=5) == E["NBITS"]
+    assert call([w.HqqHostTensor(host, 64, 100, 0x1000, 0x2000, 0x3000)]) == E["GROUP"]
+    # a half must hold one block unit: 1 row of 128 fp16 (axis 1) ...
+    assert call([ok], staging_bytes=256) == E["SHAPE"]
+    # ... or lcm(gs, codes per word) rows (axis 0, 3-bit g64: 320 rows of 256 B)
+    big = w.HqqHostTensor(host, 640, 128, 0x1000, 0x2000, 0x3000)
+    assert call([big], nbits=3, axis=0, staging_bytes=2 * 320 * 256 - 512) == E["SHAPE"]
 
 
 def test_batch_rejects(lib):

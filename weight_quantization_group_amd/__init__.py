@@ -27,8 +27,8 @@ CODES_PER_WORD = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}
 P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
-EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_dequantize", "hqq_pack", "hqq_unpack",
-           "hqq_linear", "hqq_packed_words", "hqq_strerror")
+EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_streamed", "hqq_dequantize",
+           "hqq_pack", "hqq_unpack", "hqq_linear", "hqq_packed_words", "hqq_strerror")
 
 # tensors per kernel launch of hqq_quantize_batch
 MAX_BATCH = 24
@@ -38,6 +38,12 @@ class HqqTensor(ctypes.Structure):
     """struct hqq_tensor of include/hqq.h"""
     _fields_ = [("W", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p)]
+
+
+class HqqHostTensor(ctypes.Structure):
+    """struct hqq_host_tensor of include/hqq.h (W in host memory)"""
+    _fields_ = HqqTensor._fields_
+
 
 _lib = None
 
@@ -67,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_pack.restype = i32
     L.hqq_unpack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
     L.hqq_unpack.restype = i32
+    L.hqq_quantize_streamed.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P, i64, P, P]
+    L.hqq_quantize_streamed.restype = i32
     L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_linear.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
@@ -235,3 +243,35 @@ def hqq_linear(X: torch.Tensor, packed, scale, zero, N: int, nbits: int, group_s
     if st != 0:
         raise HQQError("hqq_linear", st)
     return out
+
+
+def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging: torch.Tensor,
+                          copy_stream=None, compute_stream=None, iters: int = ITERS_DEFAULT,
+                          p: float = P_DEFAULT, beta0: float = BETA0_DEFAULT,
+                          kappa: float = KAPPA_DEFAULT):
+    """Quantize weights held in host memory.  items: list of (W, packed, scale,
+    zero) with W a CPU fp16 tensor (pinned for the copies to overlap) and the
+    outputs CUDA tensors; staging: a CUDA buffer (any dtype) split in two
+    halves.  Everything is enqueued on the two streams (default: the current
+    stream for both); the results are complete when compute_stream is."""
+    L = load_library()
+    n = len(items)
+    arr = (HqqHostTensor * max(n, 1))()
+    for i, (W, pk, sc, ze) in enumerate(items):
+        if not isinstance(W, torch.Tensor) or W.is_cuda or W.dtype not in _F16 or not W.is_contiguous():
+            raise TypeError("W must be a contiguous CPU fp16 tensor")
+        rows, cols = W.shape
+        arr[i] = HqqHostTensor(W.data_ptr(), rows, cols, _dev_ptr(pk, "packed", _U32).value,
+                               _dev_ptr(sc, "scale", (torch.float32,)).value,
+                               _dev_ptr(ze, "zero", (torch.float32,)).value)
+    if not isinstance(staging, torch.Tensor) or not staging.is_cuda or not staging.is_contiguous():
+        raise TypeError("staging must be a contiguous CUDA tensor")
+    dev = staging.device
+    cs = copy_stream if copy_stream is not None else torch.cuda.current_stream(dev)
+    ks = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+    st = L.hqq_quantize_streamed(ctypes.cast(arr, ctypes.c_void_p), n, nbits, group_size, axis, iters,
+                                 p, beta0, kappa, ctypes.c_void_p(staging.data_ptr()),
+                                 staging.numel() * staging.element_size(),
+                                 ctypes.c_void_p(cs.cuda_stream), ctypes.c_void_p(ks.cuda_stream))
+    if st != 0:
+        raise HQQError("hqq_quantize_streamed", st)

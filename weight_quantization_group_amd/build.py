@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhqq.so")
 
-SOURCES = ["hqq_abi.cpp", "hqq_solve.hip", "hqq_solve_b1.hip", "hqq_solve_b2.hip",
+SOURCES = ["hqq_abi.cpp", "hqq_stream.cpp", "hqq_solve.hip", "hqq_solve_b1.hip", "hqq_solve_b2.hip",
            "hqq_solve_b3.hip", "hqq_solve_b4.hip", "hqq_solve_b8.hip", "hqq_codec.hip",
            "hqq_linear.hip"]
 

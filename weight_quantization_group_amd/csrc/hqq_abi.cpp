@@ -67,6 +67,27 @@ void certificate(int iters, float pm1, float beta0, float kappa, float *thr, flo
 
 }  // namespace
 
+namespace hqq {
+
+int check_params(int iters, float p, float beta0, float kappa)
+{
+    if (iters < 0 || iters > kMaxIters || !finite_pos(p) || !finite_pos(beta0) || !finite_pos(kappa))
+        return HQQ_EINVAL_PARAM;
+    return HQQ_OK;
+}
+
+int check_tensor(const hqq_tensor &t, int nbits, int group_size, int axis)
+{
+    const int st = check_common(t.rows, t.cols, nbits, group_size, axis);
+    if (st)
+        return st;
+    if (!aligned16(t.W) || !aligned16(t.packed) || !aligned16(t.scale) || !aligned16(t.zero))
+        return HQQ_EINVAL_PTR;
+    return HQQ_OK;
+}
+
+}  // namespace hqq
+
 extern "C" {
 
 int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis)
@@ -103,16 +124,11 @@ int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_si
         return HQQ_EINVAL_SHAPE;
     if (n > 0 && !tensors)
         return HQQ_EINVAL_PTR;
-    if (iters < 0 || iters > kMaxIters || !finite_pos(p) || !finite_pos(beta0) || !finite_pos(kappa))
-        return HQQ_EINVAL_PARAM;
-    for (int i = 0; i < n; ++i) {
-        const hqq_tensor &t = tensors[i];
-        int st = check_common(t.rows, t.cols, nbits, group_size, axis);
-        if (st)
+    if (const int st = hqq::check_params(iters, p, beta0, kappa))
+        return st;
+    for (int i = 0; i < n; ++i)
+        if (const int st = hqq::check_tensor(tensors[i], nbits, group_size, axis))
             return st;
-        if (!aligned16(t.W) || !aligned16(t.packed) || !aligned16(t.scale) || !aligned16(t.zero))
-            return HQQ_EINVAL_PTR;
-    }
     if (n == 0)
         return HQQ_OK;
 

@@ -1,6 +1,8 @@
 // hqq_internal.h -- declarations shared by the library's own translation units.
 #pragma once
 
+#include "hqq.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,6 +78,10 @@ struct LinearArgs {
     int64_t gpl;             // groups per row of W: K / gs
     int gs, gshift;          // group size and its log2
 };
+
+// host-side argument checks shared by the entry points (HQQ_* status)
+int check_params(int iters, float p, float beta0, float kappa);
+int check_tensor(const ::hqq_tensor &t, int nbits, int group_size, int axis);
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_solve(int nbits, int group_size, int axis, const SolveArgs &a, hipStream_t s);
