@@ -30,6 +30,9 @@ ITERS_DEFAULT = 20
 
 CODES_PER_WORD = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}
 
+# element types of 16-bit weights and dequantized outputs
+DTYPES = {"f16": 0, "bf16": 1}
+
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc into ``oracle/libhqq_oracle.so``."""
@@ -47,6 +50,16 @@ def _bind(L):
     L.hqq_ref_f16_to_f32.restype = f32
     L.hqq_ref_f32_to_f16.argtypes = [f32]
     L.hqq_ref_f32_to_f16.restype = ctypes.c_uint16
+    L.hqq_ref_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.hqq_ref_bf16_to_f32.restype = f32
+    L.hqq_ref_f32_to_bf16.argtypes = [f32]
+    L.hqq_ref_f32_to_bf16.restype = ctypes.c_uint16
+    L.hqq_ref_quantize_dt.argtypes = [P, i32, i64, i64, i32, i32, i32, i32, f32, f32, f32, P, P, P]
+    L.hqq_ref_quantize_dt.restype = i32
+    L.hqq_ref_quantize_codes_dt.argtypes = [P, i32, i64, i64, i32, i32, i32, i32, f32, f32, f32, P, P, P]
+    L.hqq_ref_quantize_codes_dt.restype = i32
+    L.hqq_ref_dequantize_dt.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, P]
+    L.hqq_ref_dequantize_dt.restype = i32
     L.hqq_ref_shrink.argtypes = [f32, f32, f32]
     L.hqq_ref_shrink.restype = f32
     L.hqq_ref_solve_group.argtypes = [P, i32, i32, i32, f32, f32, f32, P, P, P, P, P, P, P, P]
@@ -106,6 +119,18 @@ def f32_to_f16(x: np.ndarray) -> np.ndarray:
     return np.array([L.hqq_ref_f32_to_f16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(x))
 
 
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    L = lib()
+    flat = np.ascontiguousarray(h, dtype=np.uint16).ravel()
+    return np.array([L.hqq_ref_bf16_to_f32(int(v)) for v in flat], dtype=np.float32).reshape(np.shape(h))
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    L = lib()
+    flat = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    return np.array([L.hqq_ref_f32_to_bf16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(x))
+
+
 def shrink(x: float, p: float, beta: float) -> float:
     return float(lib().hqq_ref_shrink(x, p, beta))
 
@@ -143,16 +168,18 @@ def meta_shape(rows, cols, group_size, axis):
 
 
 def quantize_codes(W16: np.ndarray, nbits, group_size, axis, iters=ITERS_DEFAULT,
-                   p=P_DEFAULT, beta0=BETA0_DEFAULT, kappa=KAPPA_DEFAULT):
-    """W16: uint16 (fp16 bits) [rows, cols].  Returns (codes uint8, scale, zero)."""
+                   p=P_DEFAULT, beta0=BETA0_DEFAULT, kappa=KAPPA_DEFAULT, dtype="f16"):
+    """W16: uint16 (fp16 or, dtype="bf16", bf16 bits) [rows, cols].
+    Returns (codes uint8, scale, zero)."""
     W16 = np.ascontiguousarray(W16, dtype=np.uint16)
     rows, cols = W16.shape
     codes = np.zeros((rows, cols), np.uint8)
     ms = meta_shape(rows, cols, group_size, axis)
     scale = np.zeros(ms, np.float32)
     zero = np.zeros(ms, np.float32)
-    st = lib().hqq_ref_quantize_codes(_ptr(W16), rows, cols, nbits, group_size, axis, iters,
-                                      p, beta0, kappa, _ptr(codes), _ptr(scale), _ptr(zero))
+    st = lib().hqq_ref_quantize_codes_dt(_ptr(W16), DTYPES[dtype], rows, cols, nbits, group_size,
+                                         axis, iters, p, beta0, kappa, _ptr(codes), _ptr(scale),
+                                         _ptr(zero))
     _check(st, "quantize_codes")
     return codes, scale, zero
 
@@ -163,16 +190,16 @@ def packed_shape(rows, cols, nbits, axis):
 
 
 def quantize(W16: np.ndarray, nbits, group_size, axis, iters=ITERS_DEFAULT,
-             p=P_DEFAULT, beta0=BETA0_DEFAULT, kappa=KAPPA_DEFAULT):
-    """Returns (packed uint32, scale, zero)."""
+             p=P_DEFAULT, beta0=BETA0_DEFAULT, kappa=KAPPA_DEFAULT, dtype="f16"):
+    """W16: fp16 (or dtype="bf16": bf16) bits.  Returns (packed uint32, scale, zero)."""
     W16 = np.ascontiguousarray(W16, dtype=np.uint16)
     rows, cols = W16.shape
     packed = np.zeros(packed_shape(rows, cols, nbits, axis), np.uint32)
     ms = meta_shape(rows, cols, group_size, axis)
     scale = np.zeros(ms, np.float32)
     zero = np.zeros(ms, np.float32)
-    st = lib().hqq_ref_quantize(_ptr(W16), rows, cols, nbits, group_size, axis, iters,
-                                p, beta0, kappa, _ptr(packed), _ptr(scale), _ptr(zero))
+    st = lib().hqq_ref_quantize_dt(_ptr(W16), DTYPES[dtype], rows, cols, nbits, group_size, axis,
+                                   iters, p, beta0, kappa, _ptr(packed), _ptr(scale), _ptr(zero))
     _check(st, "quantize")
     return packed, scale, zero
 
@@ -196,14 +223,14 @@ def unpack(packed: np.ndarray, rows, cols, nbits, axis) -> np.ndarray:
     return codes
 
 
-def dequantize(packed, scale, zero, rows, cols, nbits, group_size, axis) -> np.ndarray:
-    """Returns W_hat as uint16 fp16 bits [rows, cols]."""
+def dequantize(packed, scale, zero, rows, cols, nbits, group_size, axis, dtype="f16") -> np.ndarray:
+    """Returns W_hat as uint16 fp16 (or dtype="bf16": bf16) bits [rows, cols]."""
     packed = np.ascontiguousarray(packed, dtype=np.uint32)
     scale = np.ascontiguousarray(scale, dtype=np.float32)
     zero = np.ascontiguousarray(zero, dtype=np.float32)
     out = np.zeros((rows, cols), np.uint16)
-    st = lib().hqq_ref_dequantize(_ptr(packed), _ptr(scale), _ptr(zero), rows, cols,
-                                  nbits, group_size, axis, _ptr(out))
+    st = lib().hqq_ref_dequantize_dt(_ptr(packed), _ptr(scale), _ptr(zero), rows, cols,
+                                     nbits, group_size, axis, DTYPES[dtype], _ptr(out))
     _check(st, "dequantize")
     return out
 

@@ -102,6 +102,56 @@ uint16_t hqq_ref_f32_to_f16(float f)
     return (uint16_t)(sign | (uint16_t)(biased << 10) | (uint16_t)((int)m - 1024));
 }
 
+/* bfloat16 (1 sign, 8 exponent, 7 fraction bits; the top half of an IEEE
+ * binary32), from its field layout: the models the pages quantize are often
+ * loaded in bf16 (devpress.csdn.net tutorial, section 5). */
+float hqq_ref_bf16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 7) & 0xff;
+    int man = h & 0x7f;
+    float mag;
+    if (ex == 0)
+        mag = ldexpf((float)man, -133);              /* subnormal: man * 2^-133 */
+    else if (ex == 255)
+        mag = man ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(man | 0x80), ex - 134); /* (128 + man) * 2^(ex-134) */
+    return sign ? -mag : mag;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even */
+uint16_t hqq_ref_f32_to_bf16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    float a = fabsf(f);
+    if (isnan(a))
+        return (uint16_t)(sign | 0x7fc0u);
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7f80u);
+    if (a < ldexpf(1.0f, -126)) {
+        /* subnormal range, quantum 2^-133; 128 quanta becomes the smallest normal */
+        double m = nearbyint(ldexp((double)a, 133));
+        return (uint16_t)(sign | (uint16_t)m);
+    }
+    int e;
+    frexpf(a, &e);                                  /* a in [2^(e-1), 2^e) */
+    double m = nearbyint(ldexp((double)a, 8 - e));  /* 8-bit significand in [128, 256] */
+    int biased = e - 1 + 127;
+    if (m == 256.0) {
+        m = 128.0;
+        biased += 1;
+    }
+    if (biased >= 255)
+        return (uint16_t)(sign | 0x7f80u);
+    return (uint16_t)(sign | (uint16_t)(biased << 7) | (uint16_t)((int)m - 128));
+}
+
+static float widen16(uint16_t h, int dtype)
+{
+    return dtype == HQQ_REF_BF16 ? hqq_ref_bf16_to_f32(h) : hqq_ref_f16_to_f32(h);
+}
+
 /* ------------------------------------------------------------------------ */
 /* the solve                                                                */
 /* ------------------------------------------------------------------------ */
@@ -247,6 +297,17 @@ int hqq_ref_quantize_codes(const uint16_t *W, int64_t rows, int64_t cols,
                            float p, float beta0, float kappa,
                            uint8_t *codes, float *scale, float *zero)
 {
+    return hqq_ref_quantize_codes_dt(W, HQQ_REF_F16, rows, cols, nbits, group_size, axis, iters,
+                                     p, beta0, kappa, codes, scale, zero);
+}
+
+int hqq_ref_quantize_codes_dt(const uint16_t *W, int dtype, int64_t rows, int64_t cols,
+                              int nbits, int group_size, int axis, int iters,
+                              float p, float beta0, float kappa,
+                              uint8_t *codes, float *scale, float *zero)
+{
+    if (dtype != HQQ_REF_F16 && dtype != HQQ_REF_BF16)
+        return -8;
     int st = check_shape(rows, cols, nbits, group_size, axis);
     if (st)
         return st;
@@ -267,7 +328,7 @@ int hqq_ref_quantize_codes(const uint16_t *W, int64_t rows, int64_t cols,
         for (int64_t r = 0; r < rows; ++r)
             for (int64_t g = 0; g < ng; ++g) {
                 for (int j = 0; j < gs; ++j)
-                    w[j] = hqq_ref_f16_to_f32(W[r * cols + g * gs + j]);
+                    w[j] = widen16(W[r * cols + g * gs + j], dtype);
                 float s, z;
                 hqq_ref_solve_group(w, gs, nbits, iters, p, beta0, kappa, c, &s, &z,
                                     NULL, NULL, NULL, NULL, NULL);
@@ -281,7 +342,7 @@ int hqq_ref_quantize_codes(const uint16_t *W, int64_t rows, int64_t cols,
         for (int64_t g = 0; g < ng; ++g)
             for (int64_t col = 0; col < cols; ++col) {
                 for (int j = 0; j < gs; ++j)
-                    w[j] = hqq_ref_f16_to_f32(W[(g * gs + j) * cols + col]);
+                    w[j] = widen16(W[(g * gs + j) * cols + col], dtype);
                 float s, z;
                 hqq_ref_solve_group(w, gs, nbits, iters, p, beta0, kappa, c, &s, &z,
                                     NULL, NULL, NULL, NULL, NULL);
@@ -371,6 +432,16 @@ int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *
                        int64_t rows, int64_t cols, int nbits, int group_size, int axis,
                        uint16_t *W_hat)
 {
+    return hqq_ref_dequantize_dt(packed, scale, zero, rows, cols, nbits, group_size, axis,
+                                 HQQ_REF_F16, W_hat);
+}
+
+int hqq_ref_dequantize_dt(const uint32_t *packed, const float *scale, const float *zero,
+                          int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                          int dtype, uint16_t *W_hat)
+{
+    if (dtype != HQQ_REF_F16 && dtype != HQQ_REF_BF16)
+        return -8;
     int st = check_shape(rows, cols, nbits, group_size, axis);
     if (st)
         return st;
@@ -386,7 +457,8 @@ int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *
                                    : (r / group_size) * cols + col;
             float q = (float)codes[r * cols + col];
             float wr = (q - zero[gi]) / scale[gi];
-            W_hat[r * cols + col] = hqq_ref_f32_to_f16(wr);
+            W_hat[r * cols + col] = dtype == HQQ_REF_BF16 ? hqq_ref_f32_to_bf16(wr)
+                                                          : hqq_ref_f32_to_f16(wr);
         }
     free(codes);
     return 0;
@@ -431,13 +503,22 @@ int hqq_ref_quantize(const uint16_t *W, int64_t rows, int64_t cols,
                      float p, float beta0, float kappa,
                      uint32_t *packed, float *scale, float *zero)
 {
+    return hqq_ref_quantize_dt(W, HQQ_REF_F16, rows, cols, nbits, group_size, axis, iters,
+                               p, beta0, kappa, packed, scale, zero);
+}
+
+int hqq_ref_quantize_dt(const uint16_t *W, int dtype, int64_t rows, int64_t cols,
+                        int nbits, int group_size, int axis, int iters,
+                        float p, float beta0, float kappa,
+                        uint32_t *packed, float *scale, float *zero)
+{
     if (!packed)
         return -5;
     uint8_t *codes = (uint8_t *)malloc((size_t)(rows > 0 && cols > 0 ? rows * cols : 1));
     if (!codes)
         return -2;
-    int st = hqq_ref_quantize_codes(W, rows, cols, nbits, group_size, axis, iters,
-                                    p, beta0, kappa, codes, scale, zero);
+    int st = hqq_ref_quantize_codes_dt(W, dtype, rows, cols, nbits, group_size, axis, iters,
+                                       p, beta0, kappa, codes, scale, zero);
     if (st == 0)
         st = hqq_ref_pack(codes, rows, cols, nbits, axis, packed);
     free(codes);

@@ -40,6 +40,13 @@ extern "C" {
 
 /* exact fp16 -> fp32 widening, computed from the fields' values */
 float hqq_ref_f16_to_f32(uint16_t h);
+/* bfloat16 <-> fp32 (round to nearest even), from the bf16 field layout */
+float hqq_ref_bf16_to_f32(uint16_t h);
+uint16_t hqq_ref_f32_to_bf16(float f);
+
+/* element types of 16-bit weights / dequantized outputs */
+#define HQQ_REF_F16 0
+#define HQQ_REF_BF16 1
 /* fp32 -> fp16, round to nearest even, subnormals and overflow handled */
 uint16_t hqq_ref_f32_to_f16(float f);
 
@@ -60,6 +67,21 @@ int hqq_ref_solve_group(const float *w, int gs, int nbits, int iters,
 
 /* Whole-tensor solve: codes (uint8 [rows, cols], W's layout), scale and zero
  * (axis=1: [rows, cols/gs]; axis=0: [rows/gs, cols]). */
+/* W of element type dtype (HQQ_REF_F16 / HQQ_REF_BF16; -8 otherwise), widened
+ * exactly to fp32; everything after that is the same solve.  The group sum
+ * of the mean is formed in fp64 in index order. */
+int hqq_ref_quantize_codes_dt(const uint16_t *W, int dtype, int64_t rows, int64_t cols,
+                              int nbits, int group_size, int axis, int iters,
+                              float p, float beta0, float kappa,
+                              uint8_t *codes, float *scale, float *zero);
+int hqq_ref_quantize_dt(const uint16_t *W, int dtype, int64_t rows, int64_t cols,
+                        int nbits, int group_size, int axis, int iters,
+                        float p, float beta0, float kappa,
+                        uint32_t *packed, float *scale, float *zero);
+/* dequantize into dtype (fp16 or bf16, round half to even from the fp32 quotient) */
+int hqq_ref_dequantize_dt(const uint32_t *packed, const float *scale, const float *zero,
+                          int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                          int dtype, uint16_t *W_hat);
 int hqq_ref_quantize_codes(const uint16_t *W, int64_t rows, int64_t cols,
                            int nbits, int group_size, int axis, int iters,
                            float p, float beta0, float kappa,
