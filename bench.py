@@ -418,6 +418,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--wdtype", choices=("f16", "bf16"), default="f16",
+                    help="solve: element type of the weights (bf16: the synthetic fp16 weights rounded to bf16)")
     ap.add_argument("--eager", action="store_true",
                     help="--op linear: plain launches instead of a captured HIP graph")
     ap.add_argument("--op", choices=("solve", "linear", "streamed"), default="solve",
@@ -454,6 +456,8 @@ def main():
     for t in tensors:
         W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
         synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+        if args.wdtype == "bf16":
+            W = W.to(torch.bfloat16)
         ins.append(W)
         outs.append((torch.empty(hq.packed_shape(t["rows"], t["cols"], t["nbits"], t["axis"]),
                                  dtype=torch.int32, device=dev),
@@ -532,8 +536,9 @@ def main():
 
     gbs = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     out = {
-        "metric": METRIC if args.workload == "llama7b_stack32_4b_g64" else
-                  f"GB/s of fp16 weights quantized (HQQ {nb}b g{gs}, {args.iters} it), workload {args.workload}",
+        "metric": METRIC if args.workload == "llama7b_stack32_4b_g64" and args.wdtype == "f16" else
+                  f"GB/s of {'fp16' if args.wdtype == 'f16' else 'bf16'} weights quantized "
+                  f"(HQQ {nb}b g{gs}, {args.iters} it), workload {args.workload}",
         "value": round(gbs, 3),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -78,6 +78,13 @@ extern "C" {
 #define HQQ_EINVAL_PTR (-5)   /* NULL or misaligned pointer                          */
 #define HQQ_EINVAL_PARAM (-6) /* iters < 0, or p, beta0, kappa not finite and > 0    */
 #define HQQ_EHIP (-7)         /* a HIP launch failed                                  */
+#define HQQ_EINVAL_DTYPE (-8) /* dtype not HQQ_DTYPE_FP16 or HQQ_DTYPE_BF16           */
+
+/* Element types of 16-bit weight / dequantized tensors (the pages load models
+ * in fp16 or bf16 and set compute_dtype to either: devpress.csdn.net tutorial
+ * section 5, lnwmold.com HQQ guide sections 3.2 and 6.1). */
+#define HQQ_DTYPE_FP16 0
+#define HQQ_DTYPE_BF16 1
 
 /* Quantize W with the HQQ solve above (lnwmold.com HQQ guide sections 2.1-2.2;
  * devpress.csdn.net tutorial section 2).
@@ -112,6 +119,16 @@ typedef struct hqq_tensor {
 HQQ_API int hqq_quantize_batch(const hqq_tensor *tensors, int n,
                                int nbits, int group_size, int axis,
                                int iters, float p, float beta0, float kappa, void *stream);
+
+/* hqq_quantize_batch for weights of element type wdtype: HQQ_DTYPE_FP16 (the
+ * same call) or HQQ_DTYPE_BF16 (W holds bf16 bits; the devpress.csdn.net
+ * tutorial's section 5 quantizes a model loaded in bf16).  bf16 widens to
+ * fp32 exactly, so every later step is the fp16 path's; the group sum of the
+ * mean is formed in fp64 in index order (exact for fp16 in any order, not
+ * always for bf16's wider range).  Other wdtype: HQQ_EINVAL_DTYPE. */
+HQQ_API int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype,
+                                  int nbits, int group_size, int axis,
+                                  int iters, float p, float beta0, float kappa, void *stream);
 
 /* One tensor of a streamed quantize call: W in HOST memory, outputs on the
  * device (16-byte aligned; layouts as for hqq_quantize). */
@@ -155,6 +172,14 @@ HQQ_API int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n,
 HQQ_API int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero,
                    int64_t rows, int64_t cols, int nbits, int group_size, int axis,
                    uint16_t *W_hat, void *stream);
+
+/* hqq_dequantize into compute_dtype out_dtype (lnwmold.com HQQ guide section
+ * 3.2: dequantize() returns the compute_dtype, fp16 or bf16): W_hat is the
+ * same fp32 quotient rounded half to even to fp16 (HQQ_DTYPE_FP16, the same
+ * call) or bf16 (HQQ_DTYPE_BF16).  Other out_dtype: HQQ_EINVAL_DTYPE. */
+HQQ_API int hqq_dequantize_ex(const uint32_t *packed, const float *scale, const float *zero,
+                              int64_t rows, int64_t cols, int nbits, int group_size, int axis,
+                              int out_dtype, uint16_t *W_hat, void *stream);
 
 /* Pack uint8 codes [rows, cols] (W's layout; only the low nbits of each byte
  * are used) into the packed layout above (lnwmold.com HQQ guide section 3.2:

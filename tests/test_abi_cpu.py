@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hqq.h")
 LIB = os.path.join(ROOT, "weight_quantization_group_amd", "libhqq.so")
 
-E = dict(OK=0, NBITS=-1, AXIS=-2, GROUP=-3, SHAPE=-4, PTR=-5, PARAM=-6, HIP=-7)
+E = dict(OK=0, NBITS=-1, AXIS=-2, GROUP=-3, SHAPE=-4, PTR=-5, PARAM=-6, HIP=-7, DTYPE=-8)
 
 
 def _declared():
@@ -38,9 +38,10 @@ def test_header_codes_match():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
-    assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_streamed",
-                               "hqq_dequantize", "hqq_pack", "hqq_unpack", "hqq_linear",
-                               "hqq_packed_words", "hqq_strerror"])
+    assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
+                               "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
+                               "hqq_pack", "hqq_unpack", "hqq_linear", "hqq_packed_words",
+                               "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -156,6 +157,19 @@ def test_streamed_rejects(lib):
     # ... or lcm(gs, codes per word) rows (axis 0, 3-bit g64: 320 rows of 256 B)
     big = w.HqqHostTensor(host, 640, 128, 0x1000, 0x2000, 0x3000)
     assert call([big], nbits=3, axis=0, staging_bytes=2 * 320 * 256 - 512) == E["SHAPE"]
+
+
+def test_dtype_rejects(lib):
+    import weight_quantization_group_amd as w
+
+    t = (w.HqqTensor * 1)(w.HqqTensor(0x1000, 64, 128, 0x2000, 0x3000, 0x4000))
+    args = (ctypes.cast(t, ctypes.c_void_p), 1)
+    assert lib.hqq_quantize_batch_ex(*args, 2, 4, 64, 1, 20, 0.7, 10.0, 1.01, None) == E["DTYPE"]
+    assert lib.hqq_quantize_batch_ex(*args, -1, 4, 64, 1, 20, 0.7, 10.0, 1.01, None) == E["DTYPE"]
+    assert lib.hqq_quantize_batch_ex(*args, 1, 5, 64, 1, 20, 0.7, 10.0, 1.01, None) == E["NBITS"]
+    assert lib.hqq_dequantize_ex(A, A, A, 64, 128, 4, 64, 1, 7, A, None) == E["DTYPE"]
+    assert lib.hqq_dequantize_ex(A, A, A, 64, 100, 4, 64, 1, 1, A, None) == E["GROUP"]
+    assert lib.hqq_strerror(E["DTYPE"]) != b"unknown status"
 
 
 def test_batch_rejects(lib):

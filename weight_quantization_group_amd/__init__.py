@@ -27,8 +27,12 @@ CODES_PER_WORD = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}
 P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
-EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_streamed", "hqq_dequantize",
-           "hqq_pack", "hqq_unpack", "hqq_linear", "hqq_packed_words", "hqq_strerror")
+EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
+           "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_linear",
+           "hqq_packed_words", "hqq_strerror")
+
+# element types of include/hqq.h
+DTYPE_FP16, DTYPE_BF16 = 0, 1
 
 # tensors per kernel launch of hqq_quantize_batch
 MAX_BATCH = 24
@@ -67,6 +71,10 @@ def load_library(path: str = LIB_PATH):
     L.hqq_quantize.restype = i32
     L.hqq_quantize_batch.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P]
     L.hqq_quantize_batch.restype = i32
+    L.hqq_quantize_batch_ex.argtypes = [P, i32, i32, i32, i32, i32, i32, f32, f32, f32, P]
+    L.hqq_quantize_batch_ex.restype = i32
+    L.hqq_dequantize_ex.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, P, P]
+    L.hqq_dequantize_ex.restype = i32
     L.hqq_dequantize.argtypes = [P, P, P, i64, i64, i32, i32, i32, P, P]
     L.hqq_dequantize.restype = i32
     L.hqq_pack.argtypes = [P, i64, i64, i32, i32, i32, P, P]
@@ -130,8 +138,21 @@ _U32 = (torch.int32,) + ((torch.uint32,) if hasattr(torch, "uint32") else ())
 def hqq_quantize(W: torch.Tensor, nbits: int, group_size: int, axis: int,
                  iters: int = ITERS_DEFAULT, p: float = P_DEFAULT, beta0: float = BETA0_DEFAULT,
                  kappa: float = KAPPA_DEFAULT, packed=None, scale=None, zero=None):
-    """HQQ-quantize W [rows, cols] (fp16).  Returns (packed, scale, zero)."""
+    """HQQ-quantize W [rows, cols] (fp16, or bf16).  Returns (packed, scale, zero)."""
     L = load_library()
+    if isinstance(W, torch.Tensor) and W.dtype == torch.bfloat16:
+        rows, cols = W.shape
+        dev = W.device
+        if packed is None:
+            packed = torch.empty(packed_shape(rows, cols, nbits, axis), dtype=torch.int32, device=dev)
+        line = cols if axis == 1 else rows
+        ms = meta_shape(rows, cols, group_size, axis) if group_size > 0 and line % group_size == 0 else (1,)
+        if scale is None:
+            scale = torch.empty(ms, dtype=torch.float32, device=dev)
+        if zero is None:
+            zero = torch.empty(ms, dtype=torch.float32, device=dev)
+        QuantizeBatch([(W, packed, scale, zero)], nbits, group_size, axis, iters, p, beta0, kappa).run()
+        return packed, scale, zero
     rows, cols = W.shape
     dev = W.device
     if packed is None:
@@ -164,10 +185,15 @@ class QuantizeBatch:
         self._lib = load_library()
         self._items = [tuple(it) for it in items]
         n = len(self._items)
+        # the weights' element type: bf16 tensors, else fp16 bits
+        bf = [it[0].dtype == torch.bfloat16 for it in self._items]
+        if any(bf) and not all(bf):
+            raise TypeError("a batch holds fp16 or bf16 weights, not both")
+        self._wdtype = DTYPE_BF16 if n and bf[0] else DTYPE_FP16
         self._arr = (HqqTensor * max(n, 1))()
         for i, (W, pk, sc, ze) in enumerate(self._items):
             rows, cols = W.shape
-            self._arr[i] = HqqTensor(_dev_ptr(W, "W", _F16).value, rows, cols,
+            self._arr[i] = HqqTensor(_dev_ptr(W, "W", _F16 + (torch.bfloat16,)).value, rows, cols,
                                      _dev_ptr(pk, "packed", _U32).value,
                                      _dev_ptr(sc, "scale", (torch.float32,)).value,
                                      _dev_ptr(ze, "zero", (torch.float32,)).value)
@@ -177,9 +203,10 @@ class QuantizeBatch:
         self._args = (nbits, group_size, axis, iters, p, beta0, kappa)
 
     def run(self):
-        st = self._lib.hqq_quantize_batch(self._ptr, self._n, *self._args, _stream(self._dev))
+        st = self._lib.hqq_quantize_batch_ex(self._ptr, self._n, self._wdtype, *self._args,
+                                             _stream(self._dev))
         if st != 0:
-            raise HQQError("hqq_quantize_batch", st)
+            raise HQQError("hqq_quantize_batch_ex", st)
 
 
 def hqq_quantize_batch(items, nbits: int, group_size: int, axis: int,
@@ -191,16 +218,19 @@ def hqq_quantize_batch(items, nbits: int, group_size: int, axis: int,
 
 
 def hqq_dequantize(packed, scale, zero, rows: int, cols: int, nbits: int, group_size: int,
-                   axis: int, out=None) -> torch.Tensor:
-    """W_hat = fp16((W_q - zero) / scale) as an fp16 tensor [rows, cols]."""
+                   axis: int, out=None, dtype=torch.float16) -> torch.Tensor:
+    """W_hat = round((W_q - zero) / scale) to dtype (torch.float16 or
+    torch.bfloat16; out's dtype when out is given) as a tensor [rows, cols]."""
     L = load_library()
     if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float16, device=packed.device)
-    st = L.hqq_dequantize(_dev_ptr(packed, "packed", _U32), _dev_ptr(scale, "scale", (torch.float32,)),
-                          _dev_ptr(zero, "zero", (torch.float32,)), rows, cols, nbits, group_size,
-                          axis, _dev_ptr(out, "out", _F16), _stream(packed.device))
+        out = torch.empty((rows, cols), dtype=dtype, device=packed.device)
+    odt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_FP16
+    st = L.hqq_dequantize_ex(_dev_ptr(packed, "packed", _U32), _dev_ptr(scale, "scale", (torch.float32,)),
+                             _dev_ptr(zero, "zero", (torch.float32,)), rows, cols, nbits, group_size,
+                             axis, odt, _dev_ptr(out, "out", _F16 + (torch.bfloat16,)),
+                             _stream(packed.device))
     if st != 0:
-        raise HQQError("hqq_dequantize", st)
+        raise HQQError("hqq_dequantize_ex", st)
     return out
 
 

@@ -23,7 +23,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhqq.so")
 
 SOURCES = ["hqq_abi.cpp", "hqq_stream.cpp", "hqq_solve.hip", "hqq_solve_b1.hip", "hqq_solve_b2.hip",
-           "hqq_solve_b3.hip", "hqq_solve_b4.hip", "hqq_solve_b8.hip", "hqq_codec.hip",
+           "hqq_solve_b3.hip", "hqq_solve_b4.hip", "hqq_solve_b8.hip",
+           "hqq_solve_b1_bf16.hip", "hqq_solve_b2_bf16.hip", "hqq_solve_b3_bf16.hip",
+           "hqq_solve_b4_bf16.hip", "hqq_solve_b8_bf16.hip", "hqq_codec.hip",
            "hqq_linear.hip"]
 
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-fvisibility=hidden",

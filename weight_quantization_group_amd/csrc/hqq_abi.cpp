@@ -113,6 +113,7 @@ const char *hqq_strerror(int status)
     case HQQ_EINVAL_PTR: return "a pointer is NULL or not 16-byte aligned";
     case HQQ_EINVAL_PARAM: return "iters must be in [0, 65536] and p, beta0, kappa finite and > 0";
     case HQQ_EHIP: return "a HIP kernel launch failed";
+    case HQQ_EINVAL_DTYPE: return "dtype must be HQQ_DTYPE_FP16 or HQQ_DTYPE_BF16";
     default: return "unknown status";
     }
 }
@@ -120,6 +121,15 @@ const char *hqq_strerror(int status)
 int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_size, int axis,
                        int iters, float p, float beta0, float kappa, void *stream)
 {
+    return hqq_quantize_batch_ex(tensors, n, HQQ_DTYPE_FP16, nbits, group_size, axis, iters, p, beta0,
+                                 kappa, stream);
+}
+
+int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbits, int group_size,
+                          int axis, int iters, float p, float beta0, float kappa, void *stream)
+{
+    if (wdtype != HQQ_DTYPE_FP16 && wdtype != HQQ_DTYPE_BF16)
+        return HQQ_EINVAL_DTYPE;
     if (n < 0)
         return HQQ_EINVAL_SHAPE;
     if (n > 0 && !tensors)
@@ -178,7 +188,8 @@ int hqq_quantize_batch(const hqq_tensor *tensors, int n, int nbits, int group_si
         }
         a.n = used;
         i += used;
-        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, a, (hipStream_t)stream);
+        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, a,
+                                               (hipStream_t)stream);
         if (e != hipSuccess)
             return HQQ_EHIP;
     }
@@ -196,6 +207,16 @@ int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int g
 int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero, int64_t rows,
                    int64_t cols, int nbits, int group_size, int axis, uint16_t *W_hat, void *stream)
 {
+    return hqq_dequantize_ex(packed, scale, zero, rows, cols, nbits, group_size, axis, HQQ_DTYPE_FP16,
+                             W_hat, stream);
+}
+
+int hqq_dequantize_ex(const uint32_t *packed, const float *scale, const float *zero, int64_t rows,
+                      int64_t cols, int nbits, int group_size, int axis, int out_dtype, uint16_t *W_hat,
+                      void *stream)
+{
+    if (out_dtype != HQQ_DTYPE_FP16 && out_dtype != HQQ_DTYPE_BF16)
+        return HQQ_EINVAL_DTYPE;
     int st = check_common(rows, cols, nbits, group_size, axis);
     if (st)
         return st;
@@ -206,6 +227,7 @@ int hqq_dequantize(const uint32_t *packed, const float *scale, const float *zero
     a.scale = scale;
     a.zero = zero;
     a.W_hat = W_hat;
+    a.out_bf16 = out_dtype == HQQ_DTYPE_BF16;
     a.rows = rows;
     a.cols = cols;
     a.group_size = group_size;

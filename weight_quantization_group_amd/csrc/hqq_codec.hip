@@ -1,4 +1,4 @@
-// hqq_codec.hip -- dequantize, pack and unpack on gfx950.
+// hqq_codec.hip -- dequantize (to fp16 or bf16), pack and unpack on gfx950.
 //
 // These are the HQQLinear state operations of the lnwmold.com HQQ guide,
 // section 3.2 (W_q is kept bit-packed; dequantize() rebuilds the fp16 matrix
@@ -31,8 +31,27 @@ __device__ __forceinline__ void word_coords(int64_t wid, int64_t rows, int64_t c
     }
 }
 
-template <int NB, int AXIS>
-__global__ __launch_bounds__(256) void dequant_kernel(CodecArgs a)
+// fp32 -> fp16 (OB = false) or bf16 (OB = true) bits, round half to even
+// (bf16: the low 16 bits rounded off with the carry; NaN stays a quiet NaN)
+template <bool OB>
+__device__ __forceinline__ uint16_t out16(float f)
+{
+    if constexpr (OB) {
+        uint32_t u = __float_as_uint(f);
+        if ((u & 0x7fffffffu) > 0x7f800000u)
+            return (uint16_t)((u >> 16) | 0x40u);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return (uint16_t)(u >> 16);
+    } else {
+        const _Float16 h = (_Float16)f;
+        uint16_t b;
+        __builtin_memcpy(&b, &h, 2);
+        return b;
+    }
+}
+
+template <int NB, int AXIS, bool OB>
+__device__ __forceinline__ void dequant_body(const CodecArgs &a)
 {
     constexpr int C = codes_per_word(NB);
     constexpr uint32_t MASK = (1u << NB) - 1u;
@@ -53,8 +72,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecArgs a)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float q = (float)((word >> (j * NB)) & MASK);
-                const _Float16 h = (_Float16)((q - z) / s);
-                __builtin_memcpy(&out[j], &h, 2);
+                out[j] = out16<OB>((q - z) / s);
             }
             uint4 v;
             __builtin_memcpy(&v, out, 16);
@@ -66,8 +84,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecArgs a)
                 if (c < a.cols) {
                     const int64_t gi = r0 * gpl + c / gs;
                     const float q = (float)((word >> (j * NB)) & MASK);
-                    const _Float16 h = (_Float16)((q - a.zero[gi]) / a.scale[gi]);
-                    __builtin_memcpy(&a.W_hat[r0 * a.cols + c], &h, 2);
+                    a.W_hat[r0 * a.cols + c] = out16<OB>((q - a.zero[gi]) / a.scale[gi]);
                 }
             }
         }
@@ -78,11 +95,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecArgs a)
             if (r < a.rows) {
                 const int64_t gi = (r / gs) * a.cols + c0;
                 const float q = (float)((word >> (j * NB)) & MASK);
-                const _Float16 h = (_Float16)((q - a.zero[gi]) / a.scale[gi]);
-                __builtin_memcpy(&a.W_hat[r * a.cols + c0], &h, 2);
+                a.W_hat[r * a.cols + c0] = out16<OB>((q - a.zero[gi]) / a.scale[gi]);
             }
         }
     }
+}
+
+template <int NB, int AXIS>
+__global__ __launch_bounds__(256) void dequant_kernel(CodecArgs a)
+{
+    dequant_body<NB, AXIS, false>(a);
+}
+
+template <int NB, int AXIS>
+__global__ __launch_bounds__(256) void dequant_bf16_kernel(CodecArgs a)
+{
+    dequant_body<NB, AXIS, true>(a);
 }
 
 template <int NB, int AXIS>
@@ -161,6 +189,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(CodecArgs a)
     }
 
 HQQ_DEFINE_LAUNCH(dequant, dequant_kernel)
+HQQ_DEFINE_LAUNCH(dequant_bf16, dequant_bf16_kernel)
 HQQ_DEFINE_LAUNCH(pack, pack_kernel)
 HQQ_DEFINE_LAUNCH(unpack, unpack_kernel)
 
@@ -168,7 +197,7 @@ HQQ_DEFINE_LAUNCH(unpack, unpack_kernel)
 
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t st)
 {
-    return dequant_any(nbits, axis, a, st);
+    return a.out_bf16 ? dequant_bf16_any(nbits, axis, a, st) : dequant_any(nbits, axis, a, st);
 }
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t st)
 {

@@ -59,10 +59,11 @@ struct CodecArgs {
     uint8_t *codes_out;
     const float *scale;
     const float *zero;
-    uint16_t *W_hat;
+    uint16_t *W_hat;     // fp16 or (out_bf16) bf16 bits
     int64_t rows, cols;
     int group_size;
     int64_t n_words;
+    int out_bf16;
 };
 
 // Arguments of the fused dequantize + matmul kernels: Y[M, N] = X[M, K] .
@@ -84,7 +85,7 @@ int check_params(int iters, float p, float beta0, float kappa);
 int check_tensor(const ::hqq_tensor &t, int nbits, int group_size, int axis);
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_solve(int nbits, int group_size, int axis, const SolveArgs &a, hipStream_t s);
+hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, const SolveArgs &a, hipStream_t s);
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);

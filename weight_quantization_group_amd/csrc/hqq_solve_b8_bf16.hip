@@ -1,0 +1,8 @@
+// hqq_solve_b8_bf16.hip -- the 8-bit HQQ solve kernels for bf16 weights
+// (every group size and axis), in a translation unit of their own so the
+// variants compile in parallel.
+#include "hqq_solve_impl.h"
+
+namespace hqq {
+template hipError_t launch_solve_nb<8, true>(int, int, const SolveArgs &, hipStream_t);
+}  // namespace hqq

@@ -85,16 +85,56 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f)   // exact for f
     return b;
 }
 
+// Input weights are fp16 (BF = false) or bf16 (BF = true) bits; both widen
+// to fp32 exactly, and an fp32 value that came from them narrows back
+// exactly (bf16: the top 16 bits).
+template <bool BF>
+__device__ __forceinline__ float widen(uint16_t b)
+{
+    if constexpr (BF)
+        return __uint_as_float((uint32_t)b << 16);
+    else
+        return half_bits_to_float(b);
+}
+
+template <bool BF>
+__device__ __forceinline__ uint16_t narrow(float f)
+{
+    if constexpr (BF)
+        return (uint16_t)(__float_as_uint(f) >> 16);
+    else
+        return float_to_half_bits(f);
+}
+
+// eight 16-bit values of a 16-byte vector, widened to fp32
+template <bool BF>
+__device__ __forceinline__ void widen8(u32x4 v, float *out)
+{
+    if constexpr (BF) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(v[i] << 16);
+            out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    } else {
+        _Float16 h[8];
+        __builtin_memcpy(h, &v, 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            out[i] = (float)h[i];
+    }
+}
+
 // Column line of rows eg..eg+gs-1, widened to fp32.  The pointer advances one
 // row per load (the empty asm keeps the compiler from holding gs addresses).
-template <int GS>
+template <int GS, bool BF>
 __device__ __forceinline__ void load_column(const uint16_t *__restrict__ W, int64_t cols, int64_t line,
                                             int64_t eg, float (&w)[GS])
 {
     const uint16_t *q = W + eg * cols + line;
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
-        w[i] = half_bits_to_float(__builtin_nontemporal_load(q));
+        w[i] = widen<BF>(__builtin_nontemporal_load(q));
         q += cols;
         asm volatile("" : "+v"(q));
     }
@@ -102,7 +142,7 @@ __device__ __forceinline__ void load_column(const uint16_t *__restrict__ W, int6
 
 // Load one group (gs fp16 values) directly from global memory and widen
 // exactly to fp32.
-template <int GS, int AXIS>
+template <int GS, int AXIS, bool BF>
 __device__ __forceinline__ void load_group(const uint16_t *__restrict__ W, int64_t cols,
                                            int64_t line, int64_t e0, float (&w)[GS])
 {
@@ -111,23 +151,28 @@ __device__ __forceinline__ void load_group(const uint16_t *__restrict__ W, int64
 #pragma unroll
         for (int j = 0; j < GS / 8; ++j) {
             u32x4 v = __builtin_nontemporal_load(src + j);
-            _Float16 h[8];
-            __builtin_memcpy(h, &v, 16);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[j * 8 + i] = (float)h[i];
+            widen8<BF>(v, &w[j * 8]);
         }
     } else {
-        load_column<GS>(W, cols, line, e0, w);
+        load_column<GS, BF>(W, cols, line, e0, w);
     }
 }
 
-// Exact sum of the group's weights: fp16 values are multiples of 2^-24 below
-// 2^16, so any partial sum of <= 256 of them is an integer multiple of 2^-24
-// below 2^24, exactly representable in fp64.
-template <int GS>
+// Sum of the group's weights in fp64.  fp16 values are multiples of 2^-24
+// below 2^16, so any partial sum of <= 256 of them is an integer multiple of
+// 2^-24 below 2^24, exactly representable in fp64: the order is free.  bf16
+// values span a far wider range, so their sum is formed in index order (the
+// order the method's mean states), rounding where it must.
+template <int GS, bool BF>
 __device__ __forceinline__ double exact_sum(const float (&w)[GS])
 {
+    if constexpr (BF) {
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < GS; ++i)
+            acc += (double)w[i];
+        return acc;
+    }
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < GS; ++i)
@@ -283,7 +328,7 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
 
 // Finish the frozen groups of the wave (every lane of the wave takes part).
 // frozen: this lane's group is frozen; on return its z is the final zero.
-template <int NB, int GS>
+template <int NB, int GS, bool BF>
 __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS> &wf, bool frozen,
                                               const float (&w)[GS], float s, float &z, float beta,
                                               float mn, float mx, float amag, int it_f, double sw)
@@ -309,7 +354,7 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
             const int slot = __popcll(take & below);
 #pragma unroll
             for (int i = 0; i < GS; ++i)
-                wf.w[slot * GS + i] = float_to_half_bits(w[i]);
+                wf.w[slot * GS + i] = narrow<BF>(w[i]);
             wf.g[slot] = FrozenGroup{s, z, beta, mn, mx, amag, it_f, 0, sw};
         }
         wave_sync();
@@ -322,7 +367,7 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
         float we[F::EPL];
 #pragma unroll
         for (int k = 0; k < F::EPL; ++k)
-            we[k] = half_bits_to_float(wf.w[(ok ? slot : 0) * GS + pos * F::EPL + k]);
+            we[k] = widen<BF>(wf.w[(ok ? slot : 0) * GS + pos * F::EPL + k]);
         const float gs_s = st.s;
         const float thr_s = a.thr * gs_s;
         const float lim = a.thr_m * gs_s;
@@ -406,7 +451,7 @@ struct GroupInit {
     double sw;
 };
 
-template <int NB, int GS>
+template <int NB, int GS, bool BF>
 __device__ __forceinline__ GroupInit group_init(const float (&w)[GS])
 {
     constexpr float QMAX = (float)((1 << NB) - 1);
@@ -426,7 +471,7 @@ __device__ __forceinline__ GroupInit group_init(const float (&w)[GS])
         g.s = QMAX / rng;
         g.z = -(g.mn * g.s);
     }
-    g.sw = exact_sum<GS>(w);
+    g.sw = exact_sum<GS, BF>(w);
     g.amag = fmaxf(fabsf(g.mn), fabsf(g.mx));
     return g;
 }
@@ -458,7 +503,7 @@ __device__ __forceinline__ int seg_sum(int v)
 // per group iterate them with the same update as the fast loop (codes by
 // v_cvt_pk_u8_f32, sums by v_sad_u8, the lanes' partial sums added exactly),
 // and the owners take back zero, iteration, beta and frozen.
-template <int NB, int GS>
+template <int NB, int GS, bool BF>
 __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS> &wf, const float (&w)[GS],
                                            const GroupInit &g, LaneRun &r)
 {
@@ -476,8 +521,8 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
             uint32_t hw[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hw[i] = (uint32_t)float_to_half_bits(w[8 * j + 2 * i]) |
-                        ((uint32_t)float_to_half_bits(w[8 * j + 2 * i + 1]) << 16);
+                hw[i] = (uint32_t)narrow<BF>(w[8 * j + 2 * i]) |
+                        ((uint32_t)narrow<BF>(w[8 * j + 2 * i + 1]) << 16);
             wf.cw[mine * K::SEG + j] = u32x4{hw[0], hw[1], hw[2], hw[3]};
         }
         wf.cg[mine] = CompactGroup{g.s, r.z, g.mn, g.mx, g.amag, r.beta, r.it, 0, g.sw};
@@ -489,11 +534,7 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
     float we[8];
     {
         const u32x4 v = wf.cw[(act ? b : 0) * K::SEG + (int)lane % K::SEG];
-        _Float16 h[8];
-        __builtin_memcpy(h, &v, 16);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            we[i] = (float)h[i];
+        widen8<BF>(v, we);
     }
     const float s = st.s;
     const float thr_s = a.thr * s;
@@ -557,7 +598,7 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
 // group at the first iteration whose certificate fails, and stops once its
 // zero is a fixed point (r.it = iters then).  With wf: compact mode once at
 // most Compact::B groups of the wave still iterate.
-template <int NB, int GS>
+template <int NB, int GS, bool BF>
 __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[GS], const GroupInit &g,
                                            LaneRun &r, WaveFinish<GS> *wf = nullptr)
 {
@@ -572,7 +613,7 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
     while (__any(r.run)) {
         if constexpr (Compact<GS>::ON) {
             if (wf != nullptr && __popcll(__ballot(r.run)) <= Compact<GS>::B) {
-                compact_iters<NB, GS>(a, *wf, w, g, r);
+                compact_iters<NB, GS, BF>(a, *wf, w, g, r);
                 break;
             }
         }
@@ -628,7 +669,7 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
 
 // Finish: frozen lanes complete their iterations together (one lane per
 // element); then every valid lane packs its final codes.
-template <int NB, int GS, int G, int AXIS, int WPB>
+template <int NB, int GS, int G, int AXIS, int WPB, bool BF>
 __device__ __forceinline__ void finish_group(const SolveArgs &a, const SolveTensor &T, WaveFinish<GS> &wf,
                                              bool valid, int64_t line, int64_t eg, const float (&w)[GS],
                                              const GroupInit &g, LaneRun &r, uint32_t (&words)[WPB])
@@ -636,16 +677,16 @@ __device__ __forceinline__ void finish_group(const SolveArgs &a, const SolveTens
     if (valid && !r.frozen)
         pack_codes<NB, GS, G>(w, g.s, r.z, words);
     if (__any(r.frozen)) {
-        finish_frozen<NB, GS>(a, wf, r.frozen, w, g.s, r.z, r.beta, g.mn, g.mx, g.amag, r.it, g.sw);
+        finish_frozen<NB, GS, BF>(a, wf, r.frozen, w, g.s, r.z, r.beta, g.mn, g.mx, g.amag, r.it, g.sw);
         if (r.frozen) {
             float w2[GS];
-            load_group<GS, AXIS>(T.W, T.cols, line, eg, w2);
+            load_group<GS, AXIS, BF>(T.W, T.cols, line, eg, w2);
             pack_codes<NB, GS, G>(w2, g.s, r.z, words);
         }
     }
 }
 
-template <int NB, int GS, int G, int AXIS, int WPB>
+template <int NB, int GS, int G, int AXIS, int WPB, bool BF>
 __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor &T,
                                           WaveFinish<GS> &wf, bool valid, int64_t line, int64_t eg,
                                           const float (&w)[GS], uint32_t (&words)[WPB],
@@ -654,10 +695,10 @@ __device__ __forceinline__ void solve_one(const SolveArgs &a, const SolveTensor 
     // Lanes without a valid group hold in-bounds weights (staged from the
     // item's first group) and run the set-up on them; they never enter the
     // loop and their results are not stored.
-    const GroupInit g = group_init<NB, GS>(w);
+    const GroupInit g = group_init<NB, GS, BF>(w);
     LaneRun r{g.z, a.beta0, 0, valid, false};
-    fast_iters<NB, GS>(a, w, g, r, &wf);
-    finish_group<NB, GS, G, AXIS>(a, T, wf, valid, line, eg, w, g, r, words);
+    fast_iters<NB, GS, BF>(a, w, g, r, &wf);
+    finish_group<NB, GS, G, AXIS, WPB, BF>(a, T, wf, valid, line, eg, w, g, r, words);
     s_out = g.s;
     z_out = r.z;
 }
@@ -754,7 +795,7 @@ __device__ __forceinline__ void stage_group(const SolveTensor &T, int64_t line, 
 
 // Read this lane's staged group (or, for axis = 0 shapes that are not
 // staged, load it) and widen it exactly to fp32.
-template <int GS, int AXIS>
+template <int GS, int AXIS, bool BF>
 __device__ __forceinline__ void read_group(const Stage<GS, AXIS> &st, const SolveTensor &T, int64_t line,
                                            int64_t eg, bool rows64, float (&w)[GS])
 {
@@ -763,20 +804,16 @@ __device__ __forceinline__ void read_group(const Stage<GS, AXIS> &st, const Solv
 #pragma unroll
         for (int j = 0; j < GS / 8; ++j) {
             const u32x4 v = st.v[j][lane];
-            _Float16 h[8];
-            __builtin_memcpy(h, &v, 16);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[8 * j + i] = (float)h[i];
+            widen8<BF>(v, &w[8 * j]);
         }
     } else {
         if (rows64) {
             const uint16_t(*rows)[64] = reinterpret_cast<const uint16_t(*)[64]>(&st.v[0][0]);
 #pragma unroll
             for (int i = 0; i < GS; ++i)
-                w[i] = half_bits_to_float(rows[i][lane]);
+                w[i] = widen<BF>(rows[i][lane]);
         } else {
-            load_column<GS>(T.W, T.cols, line, eg, w);
+            load_column<GS, BF>(T.W, T.cols, line, eg, w);
         }
     }
     // The group stays resident as fp32 only: without this the compiler keeps
@@ -848,7 +885,7 @@ __device__ __forceinline__ void static_for(F &&f)
 // in order.  Per group: wait for its DMA, read it into registers, start the
 // DMA of the lane's next group, solve the group; a finished item is stored.
 // The loads of a group thus overlap the solve of the one before.
-template <int NB, int GS, int AXIS>
+template <int NB, int GS, int AXIS, bool BF>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NB, GS))))
 void solve_kernel(SolveArgs a)
 {
@@ -895,37 +932,37 @@ void solve_kernel(SolveArgs a)
             constexpr int G = decltype(Gc)::value;
             float w[GS];
             __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            read_group<GS, AXIS>(st, T, p.line, group_e(p, G), rows64, w);
+            read_group<GS, AXIS, BF>(st, T, p.line, group_e(p, G), rows64, w);
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             if constexpr (G + 1 < GSEQ)
                 stage_of(p, G + 1);
             else if (more)
                 stage_of(item_pos<NB, GS, AXIS>(T, first + (int64_t)(m + 1) * kBlock), 0);
-            solve_one<NB, GS, G, AXIS>(a, T, wf, G < p.ng, p.line, p.e0 + (int64_t)G * GS, w, words,
+            solve_one<NB, GS, G, AXIS, I::WPB, BF>(a, T, wf, G < p.ng, p.line, p.e0 + (int64_t)G * GS, w, words,
                                        sv[G], zv[G]);
         });
         store_item<NB, GS, AXIS>(T, p, words, sv, zv);
     }
 }
 
-template <int NB, int GS, int AXIS>
+template <int NB, int GS, int AXIS, bool BF>
 void launch_one(dim3 grid, dim3 block, const SolveArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((solve_kernel<NB, GS, AXIS>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((solve_kernel<NB, GS, AXIS, BF>), grid, block, 0, st, a);
 }
 
-template <int NB, int AXIS>
+template <int NB, int AXIS, bool BF>
 hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 {
     const dim3 block(kBlock);
     const dim3 grid((unsigned)a.blocks);
     switch (group_size) {
-    case 8: launch_one<NB, 8, AXIS>(grid, block, a, st); break;
-    case 16: launch_one<NB, 16, AXIS>(grid, block, a, st); break;
-    case 32: launch_one<NB, 32, AXIS>(grid, block, a, st); break;
-    case 64: launch_one<NB, 64, AXIS>(grid, block, a, st); break;
-    case 128: launch_one<NB, 128, AXIS>(grid, block, a, st); break;
-    case 256: launch_one<NB, 256, AXIS>(grid, block, a, st); break;
+    case 8: launch_one<NB, 8, AXIS, BF>(grid, block, a, st); break;
+    case 16: launch_one<NB, 16, AXIS, BF>(grid, block, a, st); break;
+    case 32: launch_one<NB, 32, AXIS, BF>(grid, block, a, st); break;
+    case 64: launch_one<NB, 64, AXIS, BF>(grid, block, a, st); break;
+    case 128: launch_one<NB, 128, AXIS, BF>(grid, block, a, st); break;
+    case 256: launch_one<NB, 256, AXIS, BF>(grid, block, a, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -933,11 +970,12 @@ hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 
 }  // namespace
 
-// launcher of the NB-bit solve kernels (defined in hqq_solve_b<NB>.hip)
-template <int NB>
+// launcher of the NB-bit solve kernels for fp16 (BF = false) or bf16 inputs
+// (defined in hqq_solve_b<NB>.hip and hqq_solve_b<NB>_bf16.hip)
+template <int NB, bool BF>
 hipError_t launch_solve_nb(int group_size, int axis, const SolveArgs &a, hipStream_t st)
 {
-    return axis == 1 ? launch_gs<NB, 1>(group_size, a, st) : launch_gs<NB, 0>(group_size, a, st);
+    return axis == 1 ? launch_gs<NB, 1, BF>(group_size, a, st) : launch_gs<NB, 0, BF>(group_size, a, st);
 }
 
 }  // namespace hqq
