@@ -60,6 +60,10 @@ def _bind(L):
     L.hqq_ref_quantize_codes_dt.restype = i32
     L.hqq_ref_dequantize_dt.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, P]
     L.hqq_ref_dequantize_dt.restype = i32
+    L.hqq_ref_quantize_meta.argtypes = [P, i64, i32, P, P, P]
+    L.hqq_ref_quantize_meta.restype = i32
+    L.hqq_ref_dequantize_meta.argtypes = [P, P, P, i64, i32, P]
+    L.hqq_ref_dequantize_meta.restype = i32
     L.hqq_ref_shrink.argtypes = [f32, f32, f32]
     L.hqq_ref_shrink.restype = f32
     L.hqq_ref_solve_group.argtypes = [P, i32, i32, i32, f32, f32, f32, P, P, P, P, P, P, P, P]
@@ -288,3 +292,26 @@ def build_variant(src_text: str, out_path: str) -> str:
 def source() -> str:
     with open(_SRC) as f:
         return f.read()
+
+
+def quantize_meta(meta: np.ndarray, group_size: int = 128):
+    """8-bit RTN of a metadata array (flattened, groups of group_size).
+    Returns (codes uint8 [n], scale fp32 [ceil(n/gs)], zero fp32 [ceil(n/gs)])."""
+    m = np.ascontiguousarray(meta, dtype=np.float32).ravel()
+    ng = -(-m.size // group_size)
+    codes = np.zeros(m.size, np.uint8)
+    s = np.zeros(ng, np.float32)
+    z = np.zeros(ng, np.float32)
+    _check(lib().hqq_ref_quantize_meta(_ptr(m), m.size, group_size, _ptr(codes), _ptr(s), _ptr(z)),
+           "quantize_meta")
+    return codes, s, z
+
+
+def dequantize_meta(codes, mscale, mzero, group_size: int = 128) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+    mscale = np.ascontiguousarray(mscale, dtype=np.float32)
+    mzero = np.ascontiguousarray(mzero, dtype=np.float32)
+    out = np.zeros(codes.size, np.float32)
+    _check(lib().hqq_ref_dequantize_meta(_ptr(codes), _ptr(mscale), _ptr(mzero), codes.size,
+                                         group_size, _ptr(out)), "dequantize_meta")
+    return out

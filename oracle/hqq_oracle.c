@@ -464,6 +464,50 @@ int hqq_ref_dequantize_dt(const uint32_t *packed, const float *scale, const floa
     return 0;
 }
 
+/* Metadata quantization (quant_scale / quant_zero: devpress.csdn.net
+ * tutorial section 3.3 and its troubleshooting section: the scale and zero
+ * arrays are themselves quantized at a higher precision such as 8 bits, and
+ * kept in fp16 otherwise).  Reading: after the solve, a meta array of n fp32
+ * values is cut into groups of group_size consecutive values (the last one
+ * may be shorter) and each group is quantized by 8-bit min-max RTN -- the
+ * solve above at iters = 0 -- giving uint8 codes and an fp32 scale and zero
+ * per meta group.  Dequantization is (code - zero) / scale in fp32. */
+int hqq_ref_quantize_meta(const float *meta, int64_t n, int group_size,
+                          uint8_t *codes, float *mscale, float *mzero)
+{
+    if (n < 1 || group_size < 1 || group_size > 1024)
+        return -4;
+    if (!meta || !codes || !mscale || !mzero)
+        return -5;
+    const int64_t ng = (n + group_size - 1) / group_size;
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t e0 = g * group_size;
+        const int len = (int)(n - e0 < group_size ? n - e0 : group_size);
+        float s, z;
+        int st = hqq_ref_solve_group(meta + e0, len, 8, 0, 0.7f, 10.0f, 1.01f, codes + e0, &s, &z,
+                                     NULL, NULL, NULL, NULL, NULL);
+        if (st)
+            return st;
+        mscale[g] = s;
+        mzero[g] = z;
+    }
+    return 0;
+}
+
+int hqq_ref_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
+                            int64_t n, int group_size, float *meta)
+{
+    if (n < 1 || group_size < 1 || group_size > 1024)
+        return -4;
+    if (!codes || !mscale || !mzero || !meta)
+        return -5;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t g = i / group_size;
+        meta[i] = ((float)codes[i] - mzero[g]) / mscale[g];
+    }
+    return 0;
+}
+
 int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
                    const uint32_t *packed, const float *scale, const float *zero,
                    int64_t N, int nbits, int group_size, double *Y, double *absY)

@@ -106,6 +106,13 @@ int hqq_ref_dequantize(const uint32_t *packed, const float *scale, const float *
                        int64_t rows, int64_t cols, int nbits, int group_size, int axis,
                        uint16_t *W_hat);
 
+/* 8-bit min-max RTN of a metadata array in groups of group_size (last one
+ * shorter), and its dequantization (quant_scale / quant_zero). */
+int hqq_ref_quantize_meta(const float *meta, int64_t n, int group_size,
+                          uint8_t *codes, float *mscale, float *mzero);
+int hqq_ref_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
+                            int64_t n, int group_size, float *meta);
+
 /* Linear layer on quantized weights (the consumer of the codes: HQQLinear's
  * forward in the lnwmold.com HQQ guide, section 3.2, dequantizes W_q and
  * multiplies in the compute dtype).  W_hat = hqq_ref_dequantize(...) of an
