@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --op linear [--steps K] [--warmup W]
     python bench.py --op streamed [--steps K] [--warmup W]
+    python bench.py --op meta [--steps K] [--warmup W]
 
 A step quantizes every tensor of the workload once, with all fp16 inputs
 already resident in HBM: consecutive tensors of one format go to
@@ -34,6 +35,10 @@ larger than HBM): the 7B stack in pinned host memory, hqq_quantize_streamed
 copying double-buffered chunks of 512 MiB over PCIe while the solve runs.
 Its bound is the host-to-device link, reported beside a plain pinned copy
 of the same bytes.
+
+--op meta measures the 8-bit quantization of the metadata (quant_scale /
+quant_zero): the scale and zero arrays the solve produced for the 7B stack
+(2 x 101 M fp32 values), quantized in groups of 128 by hqq_quantize_meta.
 """
 from __future__ import annotations
 
@@ -328,6 +333,87 @@ def bench_linear(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_meta(args):
+    import torch
+
+    import synth
+    import weight_quantization_group_amd as hq
+
+    hq.load_library()
+    dev = torch.device("cuda:0")
+    tensors = synth.workload(args.workload)
+    metas = []
+    for t in tensors:
+        W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
+        synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+        p, sc, ze = hq.hqq_quantize(W, t["nbits"], t["group_size"], t["axis"], iters=args.iters)
+        del W, p
+        metas += [sc, ze]
+    gsm = 128
+    outs = [(torch.empty(m.numel(), dtype=torch.uint8, device=dev),
+             torch.empty(-(-m.numel() // gsm), dtype=torch.float32, device=dev),
+             torch.empty(-(-m.numel() // gsm), dtype=torch.float32, device=dev)) for m in metas]
+    L = hq.load_library()
+    import ctypes
+
+    calls = [(ctypes.c_void_p(m.data_ptr()), m.numel(), ctypes.c_void_p(c.data_ptr()),
+              ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(z.data_ptr())) for m, (c, s, z) in zip(metas, outs)]
+    n_vals = sum(m.numel() for m in metas)
+    torch.cuda.synchronize()
+    stream = None
+
+    def step():
+        for (mp, n, cp, sp, zp) in calls:
+            if L.hqq_quantize_meta(mp, n, gsm, cp, sp, zp, stream) != 0:
+                raise RuntimeError("hqq_quantize_meta failed")
+
+    # the 448 launches are captured in one HIP graph (each array is small:
+    # launched one by one from the host, their launch cost would dominate)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stream = ctypes.c_void_p(side.cuda_stream)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    bytes_per_val = 4 + 1 + 8.0 / gsm
+    gbs = bytes_per_val * n_vals / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "G meta values/s quantized to 8 bits (quant_scale / quant_zero), 7B stack's scale and zero",
+        "value": round(n_vals / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gvalues/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload + "_meta", "values": n_vals, "arrays": len(metas),
+                   "meta_group_size": gsm},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_value": bytes_per_val,
+                     "kernel": "meta_quant_kernel"},
+    }
+    print(json.dumps(out), flush=True)
+
+
 # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 PCIE_PEAK_GBS = 63.0
 
@@ -422,7 +508,7 @@ def main():
                     help="solve: element type of the weights (bf16: the synthetic fp16 weights rounded to bf16)")
     ap.add_argument("--eager", action="store_true",
                     help="--op linear: plain launches instead of a captured HIP graph")
-    ap.add_argument("--op", choices=("solve", "linear", "streamed"), default="solve",
+    ap.add_argument("--op", choices=("solve", "linear", "streamed", "meta"), default="solve",
                     help="solve: quantize the 7B stack (default); linear: one decode token "
                          "through the quantized layers; streamed: the solve from pinned host memory")
     args = ap.parse_args()
@@ -446,6 +532,9 @@ def main():
         return
     if args.op == "streamed":
         bench_streamed(args)
+        return
+    if args.op == "meta":
+        bench_meta(args)
         return
     hq.load_library()
     dev = torch.device("cuda:0")

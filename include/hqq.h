@@ -193,6 +193,29 @@ HQQ_API int hqq_pack(const uint8_t *codes, int64_t rows, int64_t cols,
 HQQ_API int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols,
                int nbits, int group_size, int axis, uint8_t *codes, void *stream);
 
+/* Metadata quantization (quant_scale / quant_zero: devpress.csdn.net
+ * tutorial section 3.3 and its troubleshooting section -- the scale and zero
+ * arrays themselves are quantized at a higher precision such as 8 bits).
+ * The n fp32 values of meta (a scale or zero array of hqq_quantize, in its
+ * layout, read flat) are cut into groups of group_size consecutive values
+ * (the last one may be shorter) and each group is quantized by 8-bit min-max
+ * round-to-nearest-even -- the solve at iters = 0:
+ *   s = 255 / (max - min) (range 0: s = 1, z = -min), z = -(min * s),
+ *   code = clamp(rint(fma(v, s, z)), 0, 255).
+ *   meta    fp32 [n], device, read only (4-byte aligned)
+ *   codes   uint8 [n], written
+ *   mscale, mzero  fp32 [ceil(n / group_size)], written (4-byte aligned)
+ * group_size in [1, 1024] (else HQQ_EINVAL_GROUP); n >= 1.  The weight codes
+ * are unchanged: a caller that stores quantized meta dequantizes it with
+ * hqq_dequantize_meta and passes the result to hqq_dequantize / hqq_linear. */
+HQQ_API int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint8_t *codes,
+                              float *mscale, float *mzero, void *stream);
+
+/* meta[i] = (codes[i] - mzero[g]) / mscale[g], g = i / group_size, IEEE fp32;
+ * arguments as for hqq_quantize_meta (meta written). */
+HQQ_API int hqq_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
+                                int64_t n, int group_size, float *meta, void *stream);
+
 /* Linear layer on quantized weights: Y = X . W_hat^T, the quantized layer's
  * forward pass (lnwmold.com HQQ guide section 3.2: the HQQLinear layer is
  * called like the Linear it replaces, computing in compute_dtype = fp16;

@@ -40,8 +40,8 @@ def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
                                "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
-                               "hqq_pack", "hqq_unpack", "hqq_linear", "hqq_packed_words",
-                               "hqq_strerror"])
+                               "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
+                               "hqq_linear", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -170,6 +170,17 @@ def test_dtype_rejects(lib):
     assert lib.hqq_dequantize_ex(A, A, A, 64, 128, 4, 64, 1, 7, A, None) == E["DTYPE"]
     assert lib.hqq_dequantize_ex(A, A, A, 64, 100, 4, 64, 1, 1, A, None) == E["GROUP"]
     assert lib.hqq_strerror(E["DTYPE"]) != b"unknown status"
+
+
+def test_meta_rejects(lib):
+    assert lib.hqq_quantize_meta(A, 0, 128, A, A, A, None) == E["SHAPE"]
+    assert lib.hqq_quantize_meta(A, 100, 0, A, A, A, None) == E["GROUP"]
+    assert lib.hqq_quantize_meta(A, 100, 2048, A, A, A, None) == E["GROUP"]
+    assert lib.hqq_quantize_meta(None, 100, 128, A, A, A, None) == E["PTR"]
+    assert lib.hqq_quantize_meta(ctypes.c_void_p(0x1001), 100, 128, A, A, A, None) == E["PTR"]
+    assert lib.hqq_dequantize_meta(A, A, A, -5, 128, A, None) == E["SHAPE"]
+    assert lib.hqq_dequantize_meta(A, A, A, 100, 1025, A, None) == E["GROUP"]
+    assert lib.hqq_dequantize_meta(A, A, None, 100, 128, A, None) == E["PTR"]
 
 
 def test_batch_rejects(lib):

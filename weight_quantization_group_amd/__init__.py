@@ -28,8 +28,8 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
-           "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_linear",
-           "hqq_packed_words", "hqq_strerror")
+           "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
+           "hqq_dequantize_meta", "hqq_linear", "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
 DTYPE_FP16, DTYPE_BF16 = 0, 1
@@ -83,6 +83,10 @@ def load_library(path: str = LIB_PATH):
     L.hqq_unpack.restype = i32
     L.hqq_quantize_streamed.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P, i64, P, P]
     L.hqq_quantize_streamed.restype = i32
+    L.hqq_quantize_meta.argtypes = [P, i64, i32, P, P, P, P]
+    L.hqq_quantize_meta.restype = i32
+    L.hqq_dequantize_meta.argtypes = [P, P, P, i64, i32, P, P]
+    L.hqq_dequantize_meta.restype = i32
     L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_linear.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
@@ -305,3 +309,35 @@ def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging
                                  ctypes.c_void_p(cs.cuda_stream), ctypes.c_void_p(ks.cuda_stream))
     if st != 0:
         raise HQQError("hqq_quantize_streamed", st)
+
+
+def hqq_quantize_meta(meta: torch.Tensor, group_size: int = 128):
+    """8-bit RTN of a scale or zero array (quant_scale / quant_zero), read flat
+    in groups of group_size.  Returns (codes uint8 [n], mscale, mzero)."""
+    L = load_library()
+    n = meta.numel()
+    ng = -(-n // group_size)
+    codes = torch.empty(n, dtype=torch.uint8, device=meta.device)
+    ms = torch.empty(ng, dtype=torch.float32, device=meta.device)
+    mz = torch.empty(ng, dtype=torch.float32, device=meta.device)
+    st = L.hqq_quantize_meta(_dev_ptr(meta, "meta", (torch.float32,)), n, group_size,
+                             _dev_ptr(codes, "codes", (torch.uint8,)), _dev_ptr(ms, "mscale", (torch.float32,)),
+                             _dev_ptr(mz, "mzero", (torch.float32,)), _stream(meta.device))
+    if st != 0:
+        raise HQQError("hqq_quantize_meta", st)
+    return codes, ms, mz
+
+
+def hqq_dequantize_meta(codes: torch.Tensor, mscale, mzero, group_size: int = 128, out=None):
+    """fp32 meta [n] from its 8-bit codes."""
+    L = load_library()
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    st = L.hqq_dequantize_meta(_dev_ptr(codes, "codes", (torch.uint8,)),
+                               _dev_ptr(mscale, "mscale", (torch.float32,)),
+                               _dev_ptr(mzero, "mzero", (torch.float32,)), n, group_size,
+                               _dev_ptr(out, "out", (torch.float32,)), _stream(codes.device))
+    if st != 0:
+        raise HQQError("hqq_dequantize_meta", st)
+    return out

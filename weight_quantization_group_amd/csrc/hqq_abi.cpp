@@ -316,4 +316,36 @@ int hqq_linear(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
     return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
 }
 
+int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint8_t *codes, float *mscale,
+                      float *mzero, void *stream)
+{
+    if (n < 1 || n > kMaxElems)
+        return HQQ_EINVAL_SHAPE;
+    if (group_size < 1 || group_size > 1024)
+        return HQQ_EINVAL_GROUP;
+    if ((n + group_size - 1) / group_size > (int64_t)0x7fffffff * 4)   // grid: 4 groups per workgroup
+        return HQQ_EINVAL_SHAPE;
+    if (!meta || !codes || !mscale || !mzero || ((uintptr_t)meta & 3u) || ((uintptr_t)mscale & 3u) ||
+        ((uintptr_t)mzero & 3u))
+        return HQQ_EINVAL_PTR;
+    const hipError_t e = hqq::launch_quantize_meta(meta, n, group_size, codes, mscale, mzero,
+                                                   (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
+int hqq_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero, int64_t n,
+                        int group_size, float *meta, void *stream)
+{
+    if (n < 1 || n > kMaxElems || (n + 255) / 256 > 0x7fffffff)
+        return HQQ_EINVAL_SHAPE;
+    if (group_size < 1 || group_size > 1024)
+        return HQQ_EINVAL_GROUP;
+    if (!meta || !codes || !mscale || !mzero || ((uintptr_t)meta & 3u) || ((uintptr_t)mscale & 3u) ||
+        ((uintptr_t)mzero & 3u))
+        return HQQ_EINVAL_PTR;
+    const hipError_t e = hqq::launch_dequantize_meta(codes, mscale, mzero, n, group_size, meta,
+                                                     (hipStream_t)stream);
+    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+}
+
 }  // extern "C"

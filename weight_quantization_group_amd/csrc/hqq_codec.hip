@@ -193,7 +193,73 @@ HQQ_DEFINE_LAUNCH(dequant_bf16, dequant_bf16_kernel)
 HQQ_DEFINE_LAUNCH(pack, pack_kernel)
 HQQ_DEFINE_LAUNCH(unpack, unpack_kernel)
 
+// Metadata quantization (quant_scale / quant_zero): 8-bit min-max RTN of a
+// flattened fp32 array in groups of gs consecutive values (the last group
+// may be shorter) -- the solve's set-up and final codes at iters = 0.  One
+// wave per meta group; each lane takes every 64th value of the group.
+__global__ __launch_bounds__(256) void meta_quant_kernel(const float *meta, int64_t n, int gs,
+                                                         uint8_t *codes, float *mscale, float *mzero,
+                                                         int64_t groups)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= groups)
+        return;
+    const int64_t e0 = g * gs;
+    const int len = (int)(n - e0 < gs ? n - e0 : gs);
+    float mn = meta[e0], mx = meta[e0];
+    for (int i = lane; i < len; i += 64) {
+        mn = fminf(mn, meta[e0 + i]);
+        mx = fmaxf(mx, meta[e0 + i]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const float rng = mx - mn;
+    const float s = rng == 0.0f ? 1.0f : 255.0f / rng;
+    const float z = rng == 0.0f ? -mn : -(mn * s);
+    for (int i = lane; i < len; i += 64) {
+        const float t = __builtin_rintf(__builtin_fmaf(meta[e0 + i], s, z));
+        codes[e0 + i] = (uint8_t)__builtin_amdgcn_fmed3f(t, 0.0f, 255.0f);
+    }
+    if (lane == 0) {
+        mscale[g] = s;
+        mzero[g] = z;
+    }
+}
+
+// meta[i] = (code - zero) / scale of its meta group, IEEE fp32
+__global__ __launch_bounds__(256) void meta_dequant_kernel(const uint8_t *codes, const float *mscale,
+                                                           const float *mzero, int64_t n, int gs,
+                                                           float *meta)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int64_t g = i / gs;
+    meta[i] = ((float)codes[i] - mzero[g]) / mscale[g];
+}
+
 }  // namespace
+
+hipError_t launch_quantize_meta(const float *meta, int64_t n, int gs, uint8_t *codes, float *mscale,
+                                float *mzero, hipStream_t st)
+{
+    const int64_t groups = (n + gs - 1) / gs;
+    hipLaunchKernelGGL(meta_quant_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, st, meta, n,
+                       gs, codes, mscale, mzero, groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
+                                  int64_t n, int gs, float *meta, hipStream_t st)
+{
+    hipLaunchKernelGGL(meta_dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, codes,
+                       mscale, mzero, n, gs, meta);
+    return hipGetLastError();
+}
 
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t st)
 {

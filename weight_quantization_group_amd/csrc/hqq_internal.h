@@ -90,5 +90,9 @@ hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s);
+hipError_t launch_quantize_meta(const float *meta, int64_t n, int gs, uint8_t *codes, float *mscale,
+                                float *mzero, hipStream_t s);
+hipError_t launch_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
+                                  int64_t n, int gs, float *meta, hipStream_t s);
 
 }  // namespace hqq
