@@ -98,6 +98,24 @@ CASES = [
     (11, 18, 192, 8, 8),
     (1, 16, 32, 4, 8),
     (1, 1, 32, 4, 16),
+    # M >= 384 and K % 64 == 0: the tiled kernel (256 x 128 tiles, table and
+    # direct dequantization, ragged M and N); below: the row blocks
+    (64, 128, 256, 4, 64),
+    (100, 70, 320, 4, 64),
+    (130, 200, 192, 2, 16),
+    (77, 96, 128, 8, 32),
+    (64, 64, 64, 4, 8),
+    (96, 130, 512, 4, 32),
+    (200, 260, 256, 4, 128),
+    (65, 33, 128, 2, 64),
+    (128, 128, 512, 8, 256),
+    (300, 140, 256, 4, 64),
+    (257, 129, 128, 2, 32),
+    (512, 256, 320, 8, 64),
+    (384, 64, 192, 4, 16),
+    (400, 300, 256, 4, 64),
+    (513, 130, 128, 2, 32),
+    (640, 256, 320, 8, 64),
 ]
 
 
@@ -172,7 +190,8 @@ def test_matches_gpu_dequantize_then_matmul_operand(hq, oracle_mod):
 
 # the 7B decoder's linear shapes at one token (decode): q/k/v/o, gate/up, down
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008),
-                                   (8, 11008, 4096), (32, 4096, 4096)])
+                                   (8, 11008, 4096), (32, 4096, 4096), (512, 4096, 4096),
+                                   (256, 11008, 4096)])
 def test_linear_full_size(hq, oracle_mod, M, N, K):
     rng = np.random.RandomState(M + N // 7 + K // 5)
     nbits, gs = 4, 64
@@ -180,7 +199,7 @@ def test_linear_full_size(hq, oracle_mod, M, N, K):
     X16 = random_f16(rng, (M, K), std=1.0)
     Y = gpu_linear(hq, X16, packed, scale, zero, N, nbits, gs)
     # the oracle on a sample of output columns (rows of W are independent)
-    cols = np.sort(rng.choice(N, min(N, 768), replace=False))
+    cols = np.sort(rng.choice(N, min(N, 768 if M <= 32 else 80), replace=False))
     cols[0], cols[-1] = 0, N - 1
     Yref, A = oracle_mod.linear(X16, packed[cols], scale[cols], zero[cols], len(cols), nbits, gs,
                                 with_abs=True)

@@ -454,10 +454,233 @@ hipError_t launch_gpc(const LinearArgs &a, hipStream_t s)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled kernel (many rows of X: prefill).  A workgroup computes a 256 x 128
+// tile of Y with four waves (2 x 2, each 128 x 64 as 8 x 4 MFMA 16x16x32
+// tiles).  Per 64-wide step of K:
+//   * X's 256 x 64 tile is copied global -> LDS by DMA (global_load_lds, no
+//     registers), runs of 8 k XOR-swizzled by row so the MFMA reads of 16
+//     rows spread over the banks;
+//   * W's 128 x 64 tile is dequantized once by the workgroup (two threads
+//     per row, 32 k each; 4-bit codes through the group's code table) into
+//     LDS in natural k order;
+//   * the waves run their 64 MFMAs from LDS.
+// X goes through a ring of three LDS buffers, W through two, with one
+// barrier per step.  Within step s a wave first reads all of its MFMA
+// operands into registers, then dequantizes W for step s + 1 into the other
+// W buffer (its codes were loaded two steps earlier), then starts the DMA of
+// X for step s + 2, then runs its MFMAs and loads the codes of step s + 3.
+// Nothing touches LDS between the DMA and the barrier, so the wait the
+// compiler places for the DMA before the next LDS read comes after a full
+// step of matrix work.  The dequantization is shared by the 256 rows of X.
+
+constexpr int kTK = 64;              // k per step
+constexpr int kTBM = 256, kTBN = 128;
+constexpr int kWPitch = kTK / 8 + 1; // W tile row pitch in 8-k runs (uint4)
+
+// 8 codes of a 4-bit word -> 8 fp16 in natural k order
+__device__ __forceinline__ uint4 lookup4n(const Tab4 &t, uint32_t w)
+{
+    const uint4 q = lookup4(t, w);   // (c0,c2) (c4,c6) (c1,c3) (c5,c7)
+    return uint4{perm(q.z, q.x, 0x05040100u), perm(q.z, q.x, 0x07060302u),
+                 perm(q.w, q.y, 0x05040100u), perm(q.w, q.y, 0x07060302u)};
+}
+
+// A thread's share of a W step: RW = 4 runs of 8 k of one row (its codes,
+// and per run or per group the meta)
+template <int NB, bool G1>
+struct TileW {
+    uint32_t w[NB];                  // 32 k x NB bits = NB words
+    float s[G1 ? 1 : 4], z[G1 ? 1 : 4];
+};
+
+template <int NB, bool G1>
+__device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 (&out)[4])
+{
+    if constexpr (NB == 4 && G1) {
+        const Tab4 t = make_tab4(b.s[0], b.z[0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out[j] = lookup4n(t, b.w[j]);
+    } else {
+        constexpr uint32_t MASK = (1u << NB) - 1u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = G1 ? 0 : j;
+            const double R = 1.0 / (double)b.s[g];
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int bit = (8 * j + i) * NB;
+                v[i] = wq((float)((b.w[bit / 32] >> (bit % 32)) & MASK), b.z[g], R);
+            }
+            out[j] = uint4{f16x2(v[0], v[1]), f16x2(v[2], v[3]), f16x2(v[4], v[5]), f16x2(v[6], v[7])};
+        }
+    }
+}
+
+
+template <int NB, bool G1>
+__global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearArgs a)
+{
+    constexpr int TM = kTBM / 32, TN = kTBN / 32;   // MFMA tiles per wave (8 x 4)
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    __shared__ uint4 xs[3][kTBM * 8];
+    __shared__ uint4 ws[2][kTBN * kWPitch];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kTBM, n0 = (int64_t)blockIdx.x * kTBN;
+    const uint32_t K = (uint32_t)a.K;
+    const uint32_t steps = K / kTK;
+
+    // X DMA: wave w moves rows 64 w .. 64 w + 63, 8 rows (64 runs) per
+    // instruction; lane l fills slot (row 8 i + l / 8, column l % 8), which
+    // holds run (l % 8) ^ (row % 8) of that row
+    uint32_t xsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wave + 8 * i + (lane >> 3);
+        const int64_t m = m0 + r < a.M ? m0 + r : a.M - 1;
+        xsrc[i] = (uint32_t)(m * a.K) + 8 * ((lane & 7) ^ (r & 7));      // halves
+    }
+    auto dma_x = [&](uint32_t k0, int b) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(a.X + xsrc[i] + k0, (lds_ptr)&xs[b][(64 * wave + 8 * i) * 8], 16,
+                                             0, 0);
+    };
+
+    // W: thread t dequantizes row t / 2, runs 4 (t % 2) .. + 3
+    const int wr = tid >> 1, wr0 = (tid & 1) * 4;
+    const int64_t wn_ = n0 + wr < a.N ? n0 + wr : a.N - 1;
+    const uint32_t wbase = (uint32_t)(wn_ * a.wpr) + (8 * wr0 * NB) / 32;
+    const uint32_t gbase = (uint32_t)(wn_ * a.gpl);
+    auto load_w = [&](uint32_t k0, TileW<NB, G1> &w) {
+        const uint32_t wo = 4 * (wbase + (k0 * NB) / 32);
+        if constexpr (NB == 8) {
+            const uint4 u = *at<uint4>(a.packed, wo), v = *at<uint4>(a.packed, wo + 16);
+            w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
+            w.w[4] = v.x; w.w[5] = v.y; w.w[6] = v.z; w.w[7] = v.w;
+        } else if constexpr (NB == 4) {
+            const uint4 u = *at<uint4>(a.packed, wo);
+            w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
+        } else {
+            const uint2 u = *at<uint2>(a.packed, wo);
+            w.w[0] = u.x; w.w[1] = u.y;
+        }
+#pragma unroll
+        for (int j = 0; j < (G1 ? 1 : 4); ++j) {
+            const uint32_t g = 4 * (gbase + ((k0 + 8 * (wr0 + j)) >> a.gshift));
+            w.s[j] = *at<float>(a.scale, g);
+            w.z[j] = *at<float>(a.zero, g);
+        }
+    };
+    auto store_w = [&](const TileW<NB, G1> &w, int b) {
+        uint4 runs[4];
+        dequant_tile_runs<NB, G1>(w, runs);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            ws[b][wr * kWPitch + wr0 + j] = runs[j];
+    };
+
+    float4v acc[TM][TN];
+#pragma unroll
+    for (int u = 0; u < TM; ++u)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            acc[u][t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // Past the last step the loads repeat it (in bounds, never used).
+    // Prologue: X(0) and X(1) by DMA, W(0) in LDS, the codes of W(1) and
+    // W(2) in registers.
+    auto clampk = [&](uint32_t s_) { return (s_ < steps ? s_ : steps - 1) * kTK; };
+    TileW<NB, G1> wb0, wb1;
+    load_w(0, wb0);
+    store_w(wb0, 0);
+    load_w(clampk(1), wb1);
+    load_w(clampk(2), wb0);
+    dma_x(0, 0);
+    dma_x(clampk(1), 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): X(0) has landed
+    __syncthreads();
+
+    // step st: X in buffer st % 3, W in buffer st & 1; wn1 holds the codes
+    // of step st + 1
+    auto step = [&](uint32_t st, TileW<NB, G1> &wn1) {
+        const int bx = (int)(st % 3), bw = (int)(st & 1);
+        uint4 A[2][TM], B[2][TN];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int u = 0; u < TM; ++u) {
+                const int r = wm * (kTBM / 2) + 16 * u + (lane & 15);
+                A[ks][u] = xs[bx][r * 8 + ((4 * ks + (lane >> 4)) ^ (r & 7))];
+            }
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                B[ks][t] = ws[bw][(wn * (kTBN / 2) + 16 * t + (lane & 15)) * kWPitch + 4 * ks + (lane >> 4)];
+        }
+        store_w(wn1, bw ^ 1);
+        dma_x(clampk(st + 2), (int)((st + 2) % 3));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int u = 0; u < TM; ++u)
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    acc[u][t] = mfma(A[ks][u], B[ks][t], acc[u][t]);
+        load_w(clampk(st + 3), wn1);
+        __syncthreads();
+    };
+    // two steps per trip, so that the register buffers are named statically
+    for (uint32_t st = 0; st < steps; st += 2) {
+        step(st, wb1);
+        if (st + 1 < steps)
+            step(st + 1, wb0);
+    }
+
+    // accumulator r of lane l in tile (u, t) is Y[m][n] with
+    // m = 4 (l / 16) + r + 16 u, n = l % 16 + 16 t in the wave's quadrant
+#pragma unroll
+    for (int u = 0; u < TM; ++u)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * (kTBM / 2) + 16 * u + 4 * (lane >> 4) + r;
+                const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
+                if (m < a.M && n < a.N) {
+                    const _Float16 h = (_Float16)acc[u][t][r];
+                    __builtin_memcpy(&a.Y[m * a.N + n], &h, 2);
+                }
+            }
+}
+
+template <int NB>
+hipError_t launch_tiled(const LinearArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.N + kTBN - 1) / kTBN), (unsigned)((a.M + kTBM - 1) / kTBM));
+    if (a.gs >= 32)
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// rows of X from which the tiled kernel is used (K a multiple of 64; 2-, 4-
+// and 8-bit codes).  Below it the 256-row tiles leave most CUs idle and the
+// row blocks of the skinny kernel are faster (measured at N = 4096).
+constexpr int64_t kTiledMinRows = 384;
+
 template <int NB>
 hipError_t launch_nb(const LinearArgs &a, hipStream_t s)
 {
-    // M > 32 runs ceil(M / 32) row blocks of 32
+    if constexpr (NB >= 2) {
+        if (a.M >= kTiledMinRows && a.K % kTK == 0)
+            return launch_tiled<NB>(a, s);
+    }
+    // skinny: M > 32 runs ceil(M / 32) row blocks of 32
     if (a.M <= 16)
         return launch_gpc<NB, 1>(a, s);
     return launch_gpc<NB, 2>(a, s);
