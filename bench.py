@@ -353,33 +353,22 @@ def bench_meta(args):
     outs = [(torch.empty(m.numel(), dtype=torch.uint8, device=dev),
              torch.empty(-(-m.numel() // gsm), dtype=torch.float32, device=dev),
              torch.empty(-(-m.numel() // gsm), dtype=torch.float32, device=dev)) for m in metas]
-    L = hq.load_library()
-    import ctypes
-
-    calls = [(ctypes.c_void_p(m.data_ptr()), m.numel(), ctypes.c_void_p(c.data_ptr()),
-              ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(z.data_ptr())) for m, (c, s, z) in zip(metas, outs)]
+    batch = hq.MetaBatch([(m, *o) for m, o in zip(metas, outs)], gsm)
     n_vals = sum(m.numel() for m in metas)
     torch.cuda.synchronize()
-    stream = None
+    import ctypes
 
-    def step():
-        for (mp, n, cp, sp, zp) in calls:
-            if L.hqq_quantize_meta(mp, n, gsm, cp, sp, zp, stream) != 0:
-                raise RuntimeError("hqq_quantize_meta failed")
-
-    # the 448 launches are captured in one HIP graph (each array is small:
-    # launched one by one from the host, their launch cost would dominate)
+    # one C-ABI call quantizes all 448 arrays, 32 per kernel launch; the call
+    # is captured in a HIP graph so that the step is the kernels alone
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        stream = ctypes.c_void_p(side.cuda_stream)
-        step()
+        batch.quantize(ctypes.c_void_p(side.cuda_stream))
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-        step()
+        batch.quantize(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -406,7 +395,7 @@ def bench_meta(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload + "_meta", "values": n_vals, "arrays": len(metas),
-                   "meta_group_size": gsm},
+                   "meta_group_size": gsm, "launches": -(-len(metas) // hq.META_BATCH)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_value": bytes_per_val,
                      "kernel": "meta_quant_kernel"},

@@ -216,6 +216,35 @@ HQQ_API int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint
 HQQ_API int hqq_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
                                 int64_t n, int group_size, float *meta, void *stream);
 
+/* One meta array of a batched meta call: the n values of meta and their
+ * 8-bit codes and per-group mscale / mzero, as in hqq_quantize_meta (device
+ * pointers, 4-byte aligned; codes any alignment). */
+typedef struct hqq_meta_tensor {
+    float *meta;         /* fp32 [n]: read by the quantize call, written by the dequantize call */
+    int64_t n;
+    uint8_t *codes;      /* uint8 [n] */
+    float *mscale;       /* fp32 [ceil(n / group_size)] */
+    float *mzero;        /* fp32 [ceil(n / group_size)] */
+} hqq_meta_tensor;
+
+/* hqq_quantize_meta over count arrays that share group_size, with results
+ * identical to count single calls.  A model's scale and zero arrays are many
+ * and each is small (a 4096 x 4096 layer at group size 64 has 1 MB of each),
+ * so one launch per array is dominated by launch latency; here up to 64
+ * arrays share a launch (descriptors passed by value, nothing allocated).
+ *   items   host array of count descriptors, read during the call only
+ * Every descriptor is checked before anything is enqueued (n < 1 or above
+ * 2^40: HQQ_EINVAL_SHAPE; a null or misaligned pointer: HQQ_EINVAL_PTR);
+ * count = 0 is a no-op, count < 0 HQQ_EINVAL_SHAPE.  Outputs of different
+ * items must not overlap each other or any input. */
+HQQ_API int hqq_quantize_meta_batch(const hqq_meta_tensor *items, int count, int group_size,
+                                    void *stream);
+
+/* hqq_dequantize_meta over count arrays (meta written); arguments and checks
+ * as for hqq_quantize_meta_batch. */
+HQQ_API int hqq_dequantize_meta_batch(const hqq_meta_tensor *items, int count, int group_size,
+                                      void *stream);
+
 /* Linear layer on quantized weights: Y = X . W_hat^T, the quantized layer's
  * forward pass (lnwmold.com HQQ guide section 3.2: the HQQLinear layer is
  * called like the Linear it replaces, computing in compute_dtype = fp16;

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
                                "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
-                               "hqq_linear", "hqq_packed_words", "hqq_strerror"])
+                               "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -181,6 +181,33 @@ def test_meta_rejects(lib):
     assert lib.hqq_dequantize_meta(A, A, A, -5, 128, A, None) == E["SHAPE"]
     assert lib.hqq_dequantize_meta(A, A, A, 100, 1025, A, None) == E["GROUP"]
     assert lib.hqq_dequantize_meta(A, A, None, 100, 128, A, None) == E["PTR"]
+
+
+def test_meta_batch_rejects(lib):
+    """Every descriptor is checked before any launch: a bad item after a good
+    one is reported as such (a launch would fail with HQQ_EHIP without a GPU)."""
+    import weight_quantization_group_amd as w
+
+    def items(*specs):
+        arr = (w.HqqMetaTensor * max(1, len(specs)))()
+        for i, (meta, n, codes, ms, mz) in enumerate(specs):
+            arr[i] = w.HqqMetaTensor(meta, n, codes, ms, mz)
+        return arr
+
+    good = (0x1000, 300, 0x2001, 0x3000, 0x4000)    # codes need no alignment
+    for fn in (lib.hqq_quantize_meta_batch, lib.hqq_dequantize_meta_batch):
+        assert fn(items(good), 0, 128, None) == 0                 # no-op
+        assert fn(None, 0, 128, None) == 0
+        assert fn(items(good), -1, 128, None) == E["SHAPE"]
+        assert fn(None, 2, 128, None) == E["PTR"]
+        assert fn(items(good), 1, 0, None) == E["GROUP"]
+        assert fn(items(good), 1, 1025, None) == E["GROUP"]
+        assert fn(items(good, (0x1000, 0, 0x2000, 0x3000, 0x4000)), 2, 128, None) == E["SHAPE"]
+        assert fn(items(good, (0x1000, 1 << 41, 0x2000, 0x3000, 0x4000)), 2, 128, None) == E["SHAPE"]
+        assert fn(items(good, (0x1002, 300, 0x2000, 0x3000, 0x4000)), 2, 128, None) == E["PTR"]
+        assert fn(items(good, (0x1000, 300, 0x2000, 0x3000, 0x4001)), 2, 128, None) == E["PTR"]
+        assert fn(items(good, (0x1000, 300, None, 0x3000, 0x4000)), 2, 128, None) == E["PTR"]
+        assert fn(items(good, (0x1000, 300, 0x2000, None, 0x4000)), 2, 128, None) == E["PTR"]
 
 
 def test_batch_rejects(lib):

@@ -1,6 +1,6 @@
 """GPU parity of the metadata quantization (hqq_quantize_meta,
-hqq_dequantize_meta, through the C ABI) against the oracle, and the path
-W codes + quantized meta -> dequantize end to end."""
+hqq_dequantize_meta and their batched forms, through the C ABI) against the
+oracle, and the path W codes + quantized meta -> dequantize end to end."""
 import numpy as np
 import pytest
 
@@ -45,6 +45,76 @@ def test_meta_parity_random(hq, oracle_mod, n, gs):
     meta = rng.uniform(-400, 400, n).astype(np.float32)
     meta[: min(n, 3 * gs): 2] = 0.0          # zeros, and a constant stretch
     _check(hq, oracle_mod, meta, gs)
+
+
+def test_meta_batch_parity(hq, oracle_mod):
+    """140 arrays of ragged sizes in one call (three launches of up to 64
+    arrays), each checked against the oracle, quantize and dequantize."""
+    import torch
+
+    rng = np.random.RandomState(31)
+    sizes = [int(x) for x in rng.randint(1, 3000, size=135)] + [1, 127, 128, 129, 65536 + 5]
+    metas = [rng.uniform(-50, 50, n).astype(np.float32) for n in sizes]
+    metas[3][:] = 7.0                                 # a constant array
+    for gs in (128, 64):
+        dev = [torch.from_numpy(m).cuda() for m in metas]
+        q = hq.hqq_quantize_meta_batch(dev, gs)
+        back = hq.hqq_dequantize_meta_batch(q, gs)
+        torch.cuda.synchronize()
+        for m, (c, ms, mz), b in zip(metas, q, back):
+            oc, os_, oz = oracle_mod.quantize_meta(m, gs)
+            assert np.array_equal(c.cpu().numpy(), oc), (m.size, gs)
+            assert same_value(ms.cpu().numpy(), os_) and same_value(mz.cpu().numpy(), oz), (m.size, gs)
+            assert same_value(b.cpu().numpy(), oracle_mod.dequantize_meta(oc, os_, oz, gs)), (m.size, gs)
+
+
+@pytest.mark.parametrize("gs", [16, 32, 64, 256, 512, 1024, 100, 3])
+def test_meta_batch_group_sizes_and_alignment(hq, oracle_mod, gs):
+    """Every group size of the vector path and two others; arrays that start
+    4 bytes past a 16-byte boundary, codes at odd addresses (both take the
+    value-by-value path), sizes below one group and ragged last groups."""
+    import torch
+
+    rng = np.random.RandomState(40 + gs)
+    sizes = [1, gs - 1 if gs > 1 else 1, gs, gs + 1, 5 * gs + 7, 20000 + 3]
+    items, refs = [], []
+    for k, n in enumerate(sizes):
+        m = rng.uniform(-3, 3, n).astype(np.float32)
+        shift_m, shift_c = (k % 2, (k // 2) % 2)      # misaligned meta / codes
+        mbuf = torch.empty(n + 4, dtype=torch.float32, device="cuda")
+        md = mbuf[shift_m:shift_m + n]
+        md.copy_(torch.from_numpy(m))
+        cbuf = torch.empty(n + 4, dtype=torch.uint8, device="cuda")
+        ng = -(-n // gs)
+        items.append((md, cbuf[shift_c:shift_c + n], torch.empty(ng, dtype=torch.float32, device="cuda"),
+                      torch.empty(ng, dtype=torch.float32, device="cuda")))
+        refs.append(m)
+    mb = hq.MetaBatch(items, gs)
+    mb.quantize()
+    torch.cuda.synchronize()
+    for (md, c, ms, mz), m in zip(items, refs):
+        oc, os_, oz = oracle_mod.quantize_meta(m, gs)
+        assert np.array_equal(c.cpu().numpy(), oc), (m.size, gs)
+        assert same_value(ms.cpu().numpy(), os_) and same_value(mz.cpu().numpy(), oz), (m.size, gs)
+        md.fill_(float("nan"))
+    mb.dequantize()
+    torch.cuda.synchronize()
+    for (md, c, ms, mz), m in zip(items, refs):
+        oc, os_, oz = oracle_mod.quantize_meta(m, gs)
+        assert same_value(md.cpu().numpy(), oracle_mod.dequantize_meta(oc, os_, oz, gs)), (m.size, gs)
+
+
+def test_meta_batch_equals_single_calls(hq):
+    """The batch and the single-array entry points agree bit for bit."""
+    import torch
+
+    rng = np.random.RandomState(32)
+    dev = [torch.from_numpy(rng.uniform(-1, 1, n).astype(np.float32)).cuda() for n in (5000, 17, 40000, 1)]
+    batch = hq.hqq_quantize_meta_batch(dev, 128)
+    for m, (c, ms, mz) in zip(dev, batch):
+        c1, ms1, mz1 = hq.hqq_quantize_meta(m, 128)
+        assert torch.equal(c, c1) and torch.equal(ms.view(torch.int32), ms1.view(torch.int32))
+        assert torch.equal(mz.view(torch.int32), mz1.view(torch.int32))
 
 
 def test_meta_parity_solver_outputs(hq, oracle_mod):

@@ -29,19 +29,28 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
-           "hqq_dequantize_meta", "hqq_linear", "hqq_packed_words", "hqq_strerror")
+           "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
+           "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
 DTYPE_FP16, DTYPE_BF16 = 0, 1
 
 # tensors per kernel launch of hqq_quantize_batch
 MAX_BATCH = 24
+# meta arrays per kernel launch of hqq_quantize_meta_batch / hqq_dequantize_meta_batch
+META_BATCH = 64
 
 
 class HqqTensor(ctypes.Structure):
     """struct hqq_tensor of include/hqq.h"""
     _fields_ = [("W", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p)]
+
+
+class HqqMetaTensor(ctypes.Structure):
+    """struct hqq_meta_tensor of include/hqq.h"""
+    _fields_ = [("meta", ctypes.c_void_p), ("n", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("mscale", ctypes.c_void_p), ("mzero", ctypes.c_void_p)]
 
 
 class HqqHostTensor(ctypes.Structure):
@@ -87,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     L.hqq_quantize_meta.restype = i32
     L.hqq_dequantize_meta.argtypes = [P, P, P, i64, i32, P, P]
     L.hqq_dequantize_meta.restype = i32
+    L.hqq_quantize_meta_batch.argtypes = [P, i32, i32, P]
+    L.hqq_quantize_meta_batch.restype = i32
+    L.hqq_dequantize_meta_batch.argtypes = [P, i32, i32, P]
+    L.hqq_dequantize_meta_batch.restype = i32
     L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_linear.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
@@ -341,3 +354,66 @@ def hqq_dequantize_meta(codes: torch.Tensor, mscale, mzero, group_size: int = 12
     if st != 0:
         raise HQQError("hqq_dequantize_meta", st)
     return out
+
+
+class MetaBatch:
+    """Several meta arrays for hqq_quantize_meta_batch / hqq_dequantize_meta_batch,
+    marshalled into the C descriptor array once; quantize() and dequantize()
+    are then single C-ABI calls (one launch per 64 arrays) on the current
+    stream.  items: list of (meta fp32, codes uint8, mscale fp32, mzero fp32)
+    CUDA tensors, kept alive by the object."""
+
+    def __init__(self, items, group_size: int = 128):
+        self._lib = load_library()
+        self._items = [tuple(it) for it in items]
+        self.group_size = group_size
+        arr = (HqqMetaTensor * max(1, len(self._items)))()
+        for i, (m, c, ms, mz) in enumerate(self._items):
+            n = m.numel()
+            if c.numel() != n:
+                raise ValueError(f"item {i}: codes has {c.numel()} values for {n} meta values")
+            ng = -(-n // group_size)
+            if ms.numel() != ng or mz.numel() != ng:
+                raise ValueError(f"item {i}: mscale / mzero need {ng} values")
+            arr[i] = HqqMetaTensor(_dev_ptr(m, "meta", (torch.float32,)).value, n,
+                                   _dev_ptr(c, "codes", (torch.uint8,)).value,
+                                   _dev_ptr(ms, "mscale", (torch.float32,)).value,
+                                   _dev_ptr(mz, "mzero", (torch.float32,)).value)
+        self._arr = arr
+        self._device = self._items[0][0].device if self._items else None
+
+    def quantize(self, stream=None):
+        st = self._lib.hqq_quantize_meta_batch(self._arr, len(self._items), self.group_size,
+                                               stream if stream is not None else self._stream())
+        if st != 0:
+            raise HQQError("hqq_quantize_meta_batch", st)
+
+    def dequantize(self, stream=None):
+        st = self._lib.hqq_dequantize_meta_batch(self._arr, len(self._items), self.group_size,
+                                                 stream if stream is not None else self._stream())
+        if st != 0:
+            raise HQQError("hqq_dequantize_meta_batch", st)
+
+    def _stream(self):
+        return _stream(self._device) if self._device is not None else None
+
+
+def hqq_quantize_meta_batch(metas, group_size: int = 128):
+    """hqq_quantize_meta over a list of fp32 arrays in one call.  Returns a list
+    of (codes, mscale, mzero)."""
+    outs = []
+    for m in metas:
+        ng = -(-m.numel() // group_size)
+        outs.append((torch.empty(m.numel(), dtype=torch.uint8, device=m.device),
+                     torch.empty(ng, dtype=torch.float32, device=m.device),
+                     torch.empty(ng, dtype=torch.float32, device=m.device)))
+    MetaBatch([(m, *o) for m, o in zip(metas, outs)], group_size).quantize()
+    return outs
+
+
+def hqq_dequantize_meta_batch(quantized, group_size: int = 128):
+    """hqq_dequantize_meta over a list of (codes, mscale, mzero) in one call.
+    Returns the fp32 arrays."""
+    outs = [torch.empty(c.numel(), dtype=torch.float32, device=c.device) for c, _, _ in quantized]
+    MetaBatch([(o, c, ms, mz) for o, (c, ms, mz) in zip(outs, quantized)], group_size).dequantize()
+    return outs

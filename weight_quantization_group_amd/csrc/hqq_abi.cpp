@@ -88,6 +88,65 @@ int check_tensor(const hqq_tensor &t, int nbits, int group_size, int axis)
 
 }  // namespace hqq
 
+namespace {
+
+// Workgroups of one meta array in the quantize or the dequantize grid.
+int64_t meta_blocks(int64_t n, int gs, bool quant)
+{
+    if (quant) {
+        const int gpb = hqq::meta_groups_per_block(gs);
+        return ((n + gs - 1) / gs + gpb - 1) / gpb;
+    }
+    return (n + hqq::kMetaDequantBlock - 1) / hqq::kMetaDequantBlock;
+}
+
+// The meta calls: every descriptor checked, then launches of up to
+// kMetaBatch arrays whose grid stays below 2^31 workgroups.
+int meta_batch(const hqq_meta_tensor *items, int count, int gs, bool quant, void *stream)
+{
+    if (count < 0)
+        return HQQ_EINVAL_SHAPE;
+    if (count > 0 && !items)
+        return HQQ_EINVAL_PTR;
+    if (gs < 1 || gs > 1024)
+        return HQQ_EINVAL_GROUP;
+    const int64_t kMaxGrid = 0x7fffffff;
+    for (int i = 0; i < count; ++i) {
+        const hqq_meta_tensor &t = items[i];
+        if (t.n < 1 || t.n > kMaxElems || meta_blocks(t.n, gs, quant) > kMaxGrid)
+            return HQQ_EINVAL_SHAPE;
+        if (!t.meta || !t.codes || !t.mscale || !t.mzero || ((uintptr_t)t.meta & 3u) ||
+            ((uintptr_t)t.mscale & 3u) || ((uintptr_t)t.mzero & 3u))
+            return HQQ_EINVAL_PTR;
+    }
+    hqq::MetaBatch b{};
+    int64_t blocks = 0;
+    auto flush = [&]() {
+        const hipError_t e = quant ? hqq::launch_quantize_meta(b, gs, (hipStream_t)stream)
+                                   : hqq::launch_dequantize_meta(b, gs, (hipStream_t)stream);
+        b.count = 0;
+        blocks = 0;
+        return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+    };
+    for (int i = 0; i < count; ++i) {
+        const hqq_meta_tensor &t = items[i];
+        const int64_t nb = meta_blocks(t.n, gs, quant);
+        if (b.count == hqq::kMetaBatch || blocks + nb > kMaxGrid)
+            if (const int st = flush())
+                return st;
+        b.meta[b.count] = t.meta;
+        b.n[b.count] = t.n;
+        b.codes[b.count] = t.codes;
+        b.mscale[b.count] = t.mscale;
+        b.mzero[b.count] = t.mzero;
+        ++b.count;
+        blocks += nb;
+    }
+    return b.count ? flush() : HQQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis)
@@ -323,29 +382,30 @@ int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint8_t *cod
         return HQQ_EINVAL_SHAPE;
     if (group_size < 1 || group_size > 1024)
         return HQQ_EINVAL_GROUP;
-    if ((n + group_size - 1) / group_size > (int64_t)0x7fffffff * 4)   // grid: 4 groups per workgroup
-        return HQQ_EINVAL_SHAPE;
-    if (!meta || !codes || !mscale || !mzero || ((uintptr_t)meta & 3u) || ((uintptr_t)mscale & 3u) ||
-        ((uintptr_t)mzero & 3u))
-        return HQQ_EINVAL_PTR;
-    const hipError_t e = hqq::launch_quantize_meta(meta, n, group_size, codes, mscale, mzero,
-                                                   (hipStream_t)stream);
-    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+    const hqq_meta_tensor t{const_cast<float *>(meta), n, codes, mscale, mzero};
+    return meta_batch(&t, 1, group_size, true, stream);
 }
 
 int hqq_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero, int64_t n,
                         int group_size, float *meta, void *stream)
 {
-    if (n < 1 || n > kMaxElems || (n + 255) / 256 > 0x7fffffff)
+    if (n < 1 || n > kMaxElems)
         return HQQ_EINVAL_SHAPE;
     if (group_size < 1 || group_size > 1024)
         return HQQ_EINVAL_GROUP;
-    if (!meta || !codes || !mscale || !mzero || ((uintptr_t)meta & 3u) || ((uintptr_t)mscale & 3u) ||
-        ((uintptr_t)mzero & 3u))
-        return HQQ_EINVAL_PTR;
-    const hipError_t e = hqq::launch_dequantize_meta(codes, mscale, mzero, n, group_size, meta,
-                                                     (hipStream_t)stream);
-    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+    const hqq_meta_tensor t{meta, n, const_cast<uint8_t *>(codes), const_cast<float *>(mscale),
+                            const_cast<float *>(mzero)};
+    return meta_batch(&t, 1, group_size, false, stream);
+}
+
+int hqq_quantize_meta_batch(const hqq_meta_tensor *items, int count, int group_size, void *stream)
+{
+    return meta_batch(items, count, group_size, true, stream);
+}
+
+int hqq_dequantize_meta_batch(const hqq_meta_tensor *items, int count, int group_size, void *stream)
+{
+    return meta_batch(items, count, group_size, false, stream);
 }
 
 }  // extern "C"

@@ -193,71 +193,243 @@ HQQ_DEFINE_LAUNCH(dequant_bf16, dequant_bf16_kernel)
 HQQ_DEFINE_LAUNCH(pack, pack_kernel)
 HQQ_DEFINE_LAUNCH(unpack, unpack_kernel)
 
-// Metadata quantization (quant_scale / quant_zero): 8-bit min-max RTN of a
-// flattened fp32 array in groups of gs consecutive values (the last group
-// may be shorter) -- the solve's set-up and final codes at iters = 0.  One
-// wave per meta group; each lane takes every 64th value of the group.
-__global__ __launch_bounds__(256) void meta_quant_kernel(const float *meta, int64_t n, int gs,
-                                                         uint8_t *codes, float *mscale, float *mzero,
-                                                         int64_t groups)
+// Metadata quantization (quant_scale / quant_zero, devpress.csdn.net
+// tutorial section 3.3): 8-bit min-max RTN of a flattened fp32 array in groups
+// of gs consecutive values (the last group may be shorter) -- the solve's
+// set-up and final codes at iters = 0.  The kernels take up to kMetaBatch
+// arrays per launch: a model has two small meta arrays per layer, and one
+// launch per array would cost more in launch latency than in memory time.
+
+// Array of a meta batch that workgroup blk belongs to (uniform; count <= 64).
+__device__ inline int meta_item(const MetaBatch &b, int64_t blk)
+{
+    int j = 0;
+    for (int k = 1; k < b.count; ++k)
+        j = blk >= b.block0[k] ? k : j;
+    return j;
+}
+
+// Code of value v in a group with scale s and zero z.
+__device__ inline uint32_t meta_code(float v, float s, float z)
+{
+    return (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(__builtin_fmaf(v, s, z)), 0.0f, 255.0f);
+}
+
+// Scale and zero of a group from its minimum and maximum (range 0: s = 1).
+__device__ inline void meta_scale_zero(float mn, float mx, float &s, float &z)
+{
+    const float rng = mx - mn;
+    s = rng == 0.0f ? 1.0f : 255.0f / rng;
+    z = rng == 0.0f ? -mn : -(mn * s);
+}
+
+// Generic path (any gs, any 4-byte alignment): one wave per group, each lane
+// taking every 64th value; the wave walks its share of the block's groups.
+__device__ void meta_quant_generic(const MetaBatch &b, int j, int gs, int64_t g0, int groups)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (g >= groups)
-        return;
-    const int64_t e0 = g * gs;
-    const int len = (int)(n - e0 < gs ? n - e0 : gs);
-    float mn = meta[e0], mx = meta[e0];
-    for (int i = lane; i < len; i += 64) {
-        mn = fminf(mn, meta[e0 + i]);
-        mx = fmaxf(mx, meta[e0 + i]);
-    }
+    const int64_t n = b.n[j];
+    for (int k = threadIdx.x >> 6; k < groups; k += 4) {
+        const int64_t g = g0 + k;
+        const int64_t e0 = g * gs;
+        if (e0 >= n)
+            return;
+        const float *meta = b.meta[j] + e0;
+        uint8_t *codes = b.codes[j] + e0;
+        const int len = (int)(n - e0 < gs ? n - e0 : gs);
+        float mn = meta[0], mx = meta[0];
+        for (int i = lane; i < len; i += 64) {
+            mn = fminf(mn, meta[i]);
+            mx = fmaxf(mx, meta[i]);
+        }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
-    const float rng = mx - mn;
-    const float s = rng == 0.0f ? 1.0f : 255.0f / rng;
-    const float z = rng == 0.0f ? -mn : -(mn * s);
-    for (int i = lane; i < len; i += 64) {
-        const float t = __builtin_rintf(__builtin_fmaf(meta[e0 + i], s, z));
-        codes[e0 + i] = (uint8_t)__builtin_amdgcn_fmed3f(t, 0.0f, 255.0f);
-    }
-    if (lane == 0) {
-        mscale[g] = s;
-        mzero[g] = z;
+        for (int o = 32; o > 0; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        float s, z;
+        meta_scale_zero(mn, mx, s, z);
+        for (int i = lane; i < len; i += 64)
+            codes[i] = (uint8_t)meta_code(meta[i], s, z);
+        if (lane == 0) {
+            b.mscale[j][g] = s;
+            b.mzero[j][g] = z;
+        }
     }
 }
 
-// meta[i] = (code - zero) / scale of its meta group, IEEE fp32
-__global__ __launch_bounds__(256) void meta_dequant_kernel(const uint8_t *codes, const float *mscale,
-                                                           const float *mzero, int64_t n, int gs,
-                                                           float *meta)
+// Vector path (gs = 2^LG in [16, 1024], meta 16-byte and codes 4-byte
+// aligned): L = min(64, gs / 4) lanes share a group and each loads F =
+// max(1, gs / 256) float4 of it; a wave covers 64 / L groups per slot and its
+// four slots' loads are all issued before the first reduction, so 4 KB per
+// wave are in flight.  The group's last, shorter group is read value by value.
+template <int LG>
+__device__ void meta_quant_vec(const MetaBatch &b, int j, int64_t g0)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n)
+    constexpr int GS = 1 << LG;
+    constexpr int L = GS / 4 < 64 ? GS / 4 : 64;
+    constexpr int F = GS / 256 > 1 ? GS / 256 : 1;
+    constexpr int PER = 64 / L;   // groups per slot
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / L, r = lane % L;
+    const int64_t n = b.n[j];
+    const float *meta = b.meta[j];
+    const int64_t gw = g0 + (int64_t)(threadIdx.x >> 6) * 4 * PER;   // the wave's first group
+    float v[4][F][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e0 = (gw + u * PER + sub) * GS;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int64_t e = e0 + (int64_t)(f * L + r) * 4;
+            if (e0 + GS <= n) {
+                const float4 q = *reinterpret_cast<const float4 *>(meta + e);
+                v[u][f][0] = q.x, v[u][f][1] = q.y, v[u][f][2] = q.z, v[u][f][3] = q.w;
+            } else if (e0 < n) {
+                // the array's last group: values past n repeat its first value
+                const float first = meta[e0];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[u][f][c] = e + c < n ? meta[e + c] : first;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[u][f][c] = 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t g = gw + u * PER + sub;
+        const int64_t e0 = g * GS;
+        float mn = v[u][0][0], mx = v[u][0][0];
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                mn = fminf(mn, v[u][f][c]);
+                mx = fmaxf(mx, v[u][f][c]);
+            }
+#pragma unroll
+        for (int o = L / 2; o > 0; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        if (e0 >= n)
+            continue;
+        float s, z;
+        meta_scale_zero(mn, mx, s, z);
+        uint8_t *codes = b.codes[j];
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int64_t e = e0 + (int64_t)(f * L + r) * 4;
+            const uint32_t c0 = meta_code(v[u][f][0], s, z), c1 = meta_code(v[u][f][1], s, z);
+            const uint32_t c2 = meta_code(v[u][f][2], s, z), c3 = meta_code(v[u][f][3], s, z);
+            if (e0 + GS <= n) {
+                *reinterpret_cast<uint32_t *>(codes + e) = c0 | c1 << 8 | c2 << 16 | c3 << 24;
+            } else {
+                const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (e + c < n)
+                        codes[e + c] = (uint8_t)cs[c];
+            }
+        }
+        if (r == 0) {
+            b.mscale[j][g] = s;
+            b.mzero[j][g] = z;
+        }
+    }
+}
+
+// LG = log2(gs) for the vector path's group sizes, 0 for any other gs.
+template <int LG>
+__global__ __launch_bounds__(256) void meta_quant_kernel(const MetaBatch b, int gs)
+{
+    const int64_t blk = blockIdx.x;
+    const int j = meta_item(b, blk);
+    const int gpb = meta_groups_per_block(gs);
+    const int64_t g0 = (blk - b.block0[j]) * gpb;
+    if constexpr (LG != 0) {
+        if (((uintptr_t)b.meta[j] & 15u) == 0 && ((uintptr_t)b.codes[j] & 3u) == 0) {
+            meta_quant_vec<LG>(b, j, g0);
+            return;
+        }
+    }
+    meta_quant_generic(b, j, gs, g0, gpb);
+}
+
+// meta[i] = (code - zero) / scale of its meta group, IEEE fp32.  A workgroup
+// takes 1024 values of one array: four per lane (one uint32 of codes, one
+// float4 out) when meta is 16-byte and codes 4-byte aligned, else one value
+// at a time.
+__global__ __launch_bounds__(256) void meta_dequant_kernel(const MetaBatch b, int gs)
+{
+    const int64_t blk = blockIdx.x;
+    const int j = meta_item(b, blk);
+    const int64_t n = b.n[j];
+    const int64_t base = (blk - b.block0[j]) * kMetaDequantBlock;
+    const uint8_t *codes = b.codes[j];
+    const float *ms = b.mscale[j], *mz = b.mzero[j];
+    float *meta = b.meta[j];
+    if (((uintptr_t)meta & 15u) == 0 && ((uintptr_t)codes & 3u) == 0) {
+        const int64_t i = base + threadIdx.x * 4;
+        if (i + 4 <= n) {
+            const uint32_t c = *reinterpret_cast<const uint32_t *>(codes + i);
+            float o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t g = (i + k) / gs;
+                o[k] = ((float)((c >> (8 * k)) & 255u) - mz[g]) / ms[g];
+            }
+            *reinterpret_cast<float4 *>(meta + i) = make_float4(o[0], o[1], o[2], o[3]);
+            return;
+        }
+        for (int64_t e = i; e < n && e < i + 4; ++e)
+            meta[e] = ((float)codes[e] - mz[e / gs]) / ms[e / gs];
         return;
-    const int64_t g = i / gs;
-    meta[i] = ((float)codes[i] - mzero[g]) / mscale[g];
+    }
+    for (int k = 0; k < kMetaDequantBlock; k += 256) {
+        const int64_t e = base + k + threadIdx.x;
+        if (e < n)
+            meta[e] = ((float)codes[e] - mz[e / gs]) / ms[e / gs];
+    }
 }
 
 }  // namespace
 
-hipError_t launch_quantize_meta(const float *meta, int64_t n, int gs, uint8_t *codes, float *mscale,
-                                float *mzero, hipStream_t st)
+hipError_t launch_quantize_meta(MetaBatch &b, int gs, hipStream_t st)
 {
-    const int64_t groups = (n + gs - 1) / gs;
-    hipLaunchKernelGGL(meta_quant_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, st, meta, n,
-                       gs, codes, mscale, mzero, groups);
+    const int gpb = meta_groups_per_block(gs);
+    int64_t blocks = 0;
+    for (int j = 0; j < b.count; ++j) {
+        b.block0[j] = blocks;
+        blocks += ((b.n[j] + gs - 1) / gs + gpb - 1) / gpb;
+    }
+    b.block0[b.count] = blocks;
+    const dim3 grid((unsigned)blocks), block(256);
+    switch (gs) {
+    case 16: hipLaunchKernelGGL(meta_quant_kernel<4>, grid, block, 0, st, b, gs); break;
+    case 32: hipLaunchKernelGGL(meta_quant_kernel<5>, grid, block, 0, st, b, gs); break;
+    case 64: hipLaunchKernelGGL(meta_quant_kernel<6>, grid, block, 0, st, b, gs); break;
+    case 128: hipLaunchKernelGGL(meta_quant_kernel<7>, grid, block, 0, st, b, gs); break;
+    case 256: hipLaunchKernelGGL(meta_quant_kernel<8>, grid, block, 0, st, b, gs); break;
+    case 512: hipLaunchKernelGGL(meta_quant_kernel<9>, grid, block, 0, st, b, gs); break;
+    case 1024: hipLaunchKernelGGL(meta_quant_kernel<10>, grid, block, 0, st, b, gs); break;
+    default: hipLaunchKernelGGL(meta_quant_kernel<0>, grid, block, 0, st, b, gs); break;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
-                                  int64_t n, int gs, float *meta, hipStream_t st)
+hipError_t launch_dequantize_meta(MetaBatch &b, int gs, hipStream_t st)
 {
-    hipLaunchKernelGGL(meta_dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, codes,
-                       mscale, mzero, n, gs, meta);
+    int64_t blocks = 0;
+    for (int j = 0; j < b.count; ++j) {
+        b.block0[j] = blocks;
+        blocks += (b.n[j] + kMetaDequantBlock - 1) / kMetaDequantBlock;
+    }
+    b.block0[b.count] = blocks;
+    hipLaunchKernelGGL(meta_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, b, gs);
     return hipGetLastError();
 }
 

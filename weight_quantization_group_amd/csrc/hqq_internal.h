@@ -90,9 +90,30 @@ hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s);
-hipError_t launch_quantize_meta(const float *meta, int64_t n, int gs, uint8_t *codes, float *mscale,
-                                float *mzero, hipStream_t s);
-hipError_t launch_dequantize_meta(const uint8_t *codes, const float *mscale, const float *mzero,
-                                  int64_t n, int gs, float *meta, hipStream_t s);
+// meta arrays per launch of the meta kernels (descriptors by value)
+constexpr int kMetaBatch = 64;
+
+struct MetaBatch {
+    int count;
+    int64_t block0[kMetaBatch + 1];   // first workgroup of each array; block0[count] = grid size
+    float *meta[kMetaBatch];
+    int64_t n[kMetaBatch];
+    uint8_t *codes[kMetaBatch];
+    float *mscale[kMetaBatch];
+    float *mzero[kMetaBatch];
+};
+
+// Meta groups per workgroup of the quantize kernel: 16 slots of 64 lanes x 4
+// values (one group per slot when gs >= 256).
+constexpr int meta_groups_per_block(int gs)
+{
+    return gs >= 256 ? 16 : 16 * (256 / gs);
+}
+// Values per workgroup of the dequantize kernel.
+constexpr int kMetaDequantBlock = 1024;
+
+// up to kMetaBatch arrays per call; block0 is filled in here
+hipError_t launch_quantize_meta(MetaBatch &b, int gs, hipStream_t s);
+hipError_t launch_dequantize_meta(MetaBatch &b, int gs, hipStream_t s);
 
 }  // namespace hqq
