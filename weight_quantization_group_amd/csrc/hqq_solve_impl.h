@@ -285,22 +285,27 @@ struct WaveFinish {
 // clamped value: round half to even of clamp(t) equals clamp of the rounded
 // t), nibble pairs folded with a shift-or, and the four nibble-pair bytes
 // gathered with v_perm_b32.  Other formats: code by code.
-template <int NB, int GS, int G, int WPB>
+// TOP = false: the caller has shown that no t of the group rounds above qmax
+// and that t is never NaN; the conversion's saturation at 0 is then the whole
+// clamp.
+template <int NB, int GS, int G, int WPB, bool TOP = true>
 __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float z,
                                            uint32_t (&words)[WPB])
 {
     constexpr int C = codes_per_word(NB);
     constexpr float QMAX = (float)((1 << NB) - 1);
+    auto clamped = [&](float x) {
+        const float t = __builtin_fmaf(x, s, z);
+        return TOP ? __builtin_amdgcn_fmed3f(t, 0.0f, QMAX) : t;
+    };
     if constexpr (NB == 4 && (G * GS) % 8 == 0 && GS % 8 == 0) {
 #pragma unroll
         for (int q = 0; q < GS / 8; ++q) {
             uint32_t d0 = 0, d1 = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                d0 = __builtin_amdgcn_cvt_pk_u8_f32(
-                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[8 * q + j], s, z), 0.0f, QMAX), j, d0);
-                d1 = __builtin_amdgcn_cvt_pk_u8_f32(
-                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[8 * q + 4 + j], s, z), 0.0f, QMAX), j, d1);
+                d0 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + j]), j, d0);
+                d1 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + 4 + j]), j, d1);
             }
             const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
             const uint32_t x1 = d1 | (d1 >> 4);
@@ -313,8 +318,7 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
             uint32_t d = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                d = __builtin_amdgcn_cvt_pk_u8_f32(
-                    __builtin_amdgcn_fmed3f(__builtin_fmaf(w[4 * q + j], s, z), 0.0f, QMAX), j, d);
+                d = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[4 * q + j]), j, d);
             words[(G * GS) / 4 + q] = d;
         }
     } else {
@@ -594,6 +598,38 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
     wave_sync();
 }
 
+// sum W_q of one fast iteration.  v_cvt_pk_u8_f32 rounds half to even and
+// saturates to [0, 255] (the clamp at 0), four codes to a word; v_sad_u8
+// against 0 adds a word's four codes c.  TOP: also against qmax in every
+// byte, giving sum |c - qmax|, and min(c, qmax) = (c + qmax - |c - qmax|) / 2:
+// 2.5 VALU ops per weight, 2 without.
+template <int NB, int GS, bool TOP>
+__device__ __forceinline__ uint32_t code_sum(const float (&w)[GS], float s, float z)
+{
+    static_assert(GS % 8 == 0, "two byte-sum chains of whole words");
+    constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
+    uint32_t c0 = 0, c1 = 0, a0 = 0, a1 = 0;
+#pragma unroll
+    for (int k = 0; k < GS / 4; k += 2) {
+        uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 0], s, z), 0, 0u);
+        uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4], s, z), 0, 0u);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+            d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + j], s, z), j, d0);
+            d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4 + j], s, z), j, d1);
+        }
+        c0 = __builtin_amdgcn_sad_u8(d0, 0u, c0);
+        c1 = __builtin_amdgcn_sad_u8(d1, 0u, c1);
+        if constexpr (TOP) {
+            a0 = __builtin_amdgcn_sad_u8(d0, QB, a0);
+            a1 = __builtin_amdgcn_sad_u8(d1, QB, a1);
+        }
+    }
+    if constexpr (TOP)
+        return ((c0 + c1) + (uint32_t)(GS * ((1 << NB) - 1)) - (a0 + a1)) >> 1;
+    return c0 + c1;
+}
+
 // Fast iterations of the lanes with r.run, up to iters: a lane freezes its
 // group at the first iteration whose certificate fails, and stops once its
 // zero is a fixed point (r.it = iters then).  With wf: compact mode once at
@@ -617,9 +653,9 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
                 break;
             }
         }
+        const float tmax = __builtin_fmaf(g.mx, s, r.z);
         if (r.run) {
             const float tmin = __builtin_fmaf(g.mn, s, r.z);
-            const float tmax = __builtin_fmaf(g.mx, s, r.z);
             const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
             const bool est_ok = __builtin_fmaf(g.amag, s, fabsf(r.z)) + QMAX <= lim;
             if (!(est_ok && bound <= thr_s)) {
@@ -627,31 +663,22 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
                 r.frozen = true;
             }
         }
+        // The clamp at qmax can bind only where the largest weight's t
+        // rounds above qmax (the fma is monotone in w); when no running lane
+        // of the wave is there (uniform branch), the codes are summed
+        // without it.  8-bit codes never need it: the conversion saturates
+        // at 255.
+        const bool top = NB < 8 && __any(r.run && !(tmax < QMAX + 0.5f));
+        uint32_t sq = 0;
+        if (top) {
+            if (r.run)
+                sq = code_sum<NB, GS, true>(w, s, r.z);
+        } else {
+            if (r.run)
+                sq = code_sum<NB, GS, false>(w, s, r.z);
+        }
         if (r.run) {
-            // W_q and sum W_q.  v_cvt_pk_u8_f32 rounds half to even and
-            // saturates to [0, 255] (the clamp at 0), four codes to a word;
-            // v_sad_u8 against 0 adds a word's four codes c, against qmax in
-            // every byte their |c - qmax|, and min(c, qmax) is
-            // (c + qmax - |c - qmax|) / 2: 2.5 VALU ops per weight.
-            static_assert(GS % 8 == 0, "two byte-sum chains of whole words");
-            constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
             const float z = r.z;
-            uint32_t c0 = 0, c1 = 0, a0 = 0, a1 = 0;
-#pragma unroll
-            for (int k = 0; k < GS / 4; k += 2) {
-                uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 0], s, z), 0, 0u);
-                uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4], s, z), 0, 0u);
-#pragma unroll
-                for (int j = 1; j < 4; ++j) {
-                    d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + j], s, z), j, d0);
-                    d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(w[4 * k + 4 + j], s, z), j, d1);
-                }
-                c0 = __builtin_amdgcn_sad_u8(d0, 0u, c0);
-                c1 = __builtin_amdgcn_sad_u8(d1, 0u, c1);
-                a0 = __builtin_amdgcn_sad_u8(d0, QB, a0);
-                a1 = __builtin_amdgcn_sad_u8(d1, QB, a1);
-            }
-            const uint32_t sq = ((c0 + c1) + (uint32_t)(GS * ((1 << NB) - 1)) - (a0 + a1)) >> 1;
             const float zn = (float)(((double)sq - ssw) * INV_GS);
             // Fixed point: the next zero depends on the current one only
             // through the codes, which are equal for equal zeros (+0 and -0
@@ -674,8 +701,19 @@ __device__ __forceinline__ void finish_group(const SolveArgs &a, const SolveTens
                                              bool valid, int64_t line, int64_t eg, const float (&w)[GS],
                                              const GroupInit &g, LaneRun &r, uint32_t (&words)[WPB])
 {
-    if (valid && !r.frozen)
-        pack_codes<NB, GS, G>(w, g.s, r.z, words);
+    // uniform choice of the packing without the clamp at qmax: every packing
+    // lane's largest t rounds to at most qmax and its group holds no NaN
+    // (the exact sum would be NaN)
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    const bool packing = valid && !r.frozen;
+    const bool top = __any(packing && !(__builtin_fmaf(g.mx, g.s, r.z) < QMAX + 0.5f && g.sw == g.sw));
+    if (top) {
+        if (packing)
+            pack_codes<NB, GS, G, WPB, true>(w, g.s, r.z, words);
+    } else {
+        if (packing)
+            pack_codes<NB, GS, G, WPB, false>(w, g.s, r.z, words);
+    }
     if (__any(r.frozen)) {
         finish_frozen<NB, GS, BF>(a, wf, r.frozen, w, g.s, r.z, r.beta, g.mn, g.mx, g.amag, r.it, g.sw);
         if (r.frozen) {
