@@ -95,15 +95,18 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def counter_summary():
+def counter_summary(workload: str, wdtype: str):
     """Counter-measured figures of the dominant solve kernel (HBM bytes and
-    issued VALU lane-ops per weight), or None if stale or absent."""
+    issued VALU lane-ops per weight), or None if stale, absent, or taken on
+    another workload or weight type (they were taken on fp16 weights)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except OSError:
         return None
     if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    if t.get("workload") != workload or wdtype != "f16":
         return None
     return t
 
@@ -603,7 +606,7 @@ def main():
     avg_ms = dom["ms"] / dom["launches"]
     bpw = hbm_bytes_per_weight(nb, gs)
     hbm_gbs = bpw * w_per_launch / (avg_ms * 1e-3) / 1e9
-    cs = counter_summary()
+    cs = counter_summary(args.workload, args.wdtype)
     traffic = round(cs["hbm_bytes_per_weight"] * w_per_launch) if cs else None
     valu = {"peak_TOPs": round(VALU_PEAK_TOPS, 3)}
     if cs:
@@ -635,7 +638,7 @@ def main():
         "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"solve_kernel<{nb},{gs},{ax}>", "avg_launch_ms": round(avg_ms, 5),
+                     "kernel": f"solve_kernel<{nb},{gs},{ax},{'true' if args.wdtype == 'bf16' else 'false'}>", "avg_launch_ms": round(avg_ms, 5),
                      "weights_per_launch": round(w_per_launch), "bytes_per_weight": bpw,
                      "valu": valu},
         "context": {"pages_hqq_llama7b_quantize_minutes": 8.2, "hardware": "not stated on the pages"},
