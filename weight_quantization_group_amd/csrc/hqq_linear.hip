@@ -478,6 +478,28 @@ constexpr int kTK = 64;              // k per step
 constexpr int kTBM = 256, kTBN = 128;
 constexpr int kWPitch = kTK / 8 + 1; // W tile row pitch in 8-k runs (uint4)
 
+// End of a k step.  A plain __syncthreads() is a workgroup release fence,
+// which waits for every vector memory operation of the wave (vmcnt(0)): the
+// code loads and X DMA just issued for later steps, a full memory latency
+// per step.  What the next step needs is narrower: this wave's W stores in
+// LDS (lgkmcnt(0)) and its DMA of the X tile the next step reads, issued one
+// step earlier.  In program order that DMA is followed by this step's X DMA
+// (kDmaOps operations) and code and meta loads (at least 3), so waiting
+// until at most kStepVm operations are outstanding is enough.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+constexpr int kDmaOps = 8;                 // global_load_lds per thread per X tile
+constexpr int kStepVm = kDmaOps + 3;
+static_assert(kTBM * kTK * 2 / 16 / 256 == kDmaOps, "X tile DMA operations per thread");
+constexpr int kWaitStep = (kStepVm & 15) | ((kStepVm >> 4) << 14) | (7 << 4);   // vmcnt(11) lgkmcnt(0)
+
+__device__ __forceinline__ void step_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitStep);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // 8 codes of a 4-bit word -> 8 fp16 in natural k order
 __device__ __forceinline__ uint4 lookup4n(const Tab4 &t, uint32_t w)
 {
@@ -631,7 +653,7 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearArgs a)
                 for (int t = 0; t < TN; ++t)
                     acc[u][t] = mfma(A[ks][u], B[ks][t], acc[u][t]);
         load_w(clampk(st + 3), wn1);
-        __syncthreads();
+        step_barrier();
     };
     // two steps per trip, so that the register buffers are named statically
     for (uint32_t st = 0; st < steps; st += 2) {
