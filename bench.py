@@ -235,9 +235,24 @@ def bench_linear(args):
             layers.append((N, K, packed, scale, zero))
     X = {K: torch.randn((1, K), device=dev, generator=gen).half() for K in (4096, 11008)}
     Y = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+    # per layer, the projections that read the same activations share one
+    # hqq_linear_batch call: (q, k, v), (o), (gate, up), (down)
+    nl = len(LLAMA7B_LINEARS)
+    calls = []
+    for li in range(LLAMA7B_LAYERS):
+        ly = layers[li * nl:(li + 1) * nl]
+        for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+            K = ly[idx[0]][1]
+            items = [(ly[i][2], ly[i][3], ly[i][4], ly[i][0],
+                      torch.empty((1, ly[i][0]), dtype=torch.float16, device=dev)) for i in idx]
+            calls.append((K, hq.LinearBatch(items, nbits, gs)))
     torch.cuda.synchronize()
 
     def token():
+        for (K, b) in calls:
+            b.run(X[K])
+
+    def token_per_layer():
         for (N, K, p, s, z) in layers:
             hq.hqq_linear(X[K], p, s, z, N, nbits, gs, out=Y[N])
 
@@ -284,22 +299,40 @@ def bench_linear(args):
     g = Eager(token) if args.eager else graph_of(token)
     ms_ev, ms_wall = timed(g, args.steps, args.warmup)
     del g
+    g = Eager(token_per_layer) if args.eager else graph_of(token_per_layer)
+    ms_per_layer, _ = timed(g, args.steps, args.warmup)
+    del g
 
-    # the fp16 reference: the same 224 products with 224 distinct fp16 weights
-    # (12.95 GB) through torch.matmul (hipBLASLt)
+    # the fp16 reference: the same 224 products with distinct fp16 weights
+    # (12.95 GB) through torch.matmul (hipBLASLt), with the same sharing of
+    # the inputs: q, k, v and gate, up as concatenated weights
     Wf = []
-    for (N, K, _, _, _) in layers:
-        w = torch.empty((N, K), dtype=torch.float16, device=dev)
-        w.normal_(0.0, 0.02, generator=gen)
-        Wf.append((N, K, w.t()))
-    Yf = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+    for li in range(LLAMA7B_LAYERS):
+        for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+            N = sum(LLAMA7B_LINEARS[i][0] for i in idx)
+            K = LLAMA7B_LINEARS[idx[0]][1]
+            w = torch.empty((N, K), dtype=torch.float16, device=dev)
+            w.normal_(0.0, 0.02, generator=gen)
+            Wf.append((K, w, torch.empty((1, N), dtype=torch.float16, device=dev),
+                       [LLAMA7B_LINEARS[i][0] for i in idx]))
 
     def token_fp16():
-        for (N, K, wt) in Wf:
-            torch.matmul(X[K], wt, out=Yf[N])
+        for (K, w, y, _) in Wf:
+            torch.matmul(X[K], w.t(), out=y)
 
+    def token_fp16_per_layer():
+        for (K, w, _, Ns) in Wf:
+            n0 = 0
+            for N in Ns:
+                torch.matmul(X[K], w[n0:n0 + N].t(), out=Yf[N])
+                n0 += N
+
+    Yf = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
     gf = Eager(token_fp16) if args.eager else graph_of(token_fp16)
     ms_fp16, _ = timed(gf, args.steps, args.warmup)
+    del gf
+    gf = Eager(token_fp16_per_layer) if args.eager else graph_of(token_fp16_per_layer)
+    ms_fp16_per_layer, _ = timed(gf, args.steps, args.warmup)
     del gf, Wf
 
     bytes_per_token = sum(N * K * nbits / 8 + N * (K // gs) * 8 + K * 2 + N * 2
@@ -327,9 +360,13 @@ def bench_linear(args):
                      "bytes_per_step": int(bytes_per_token),
                      "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
         "fp16_matmul": {"ms_per_step": round(ms_fp16, 4), "tokens_per_s": round(1e3 / ms_fp16, 3),
-                        "speedup": round(ms_fp16 / ms_ev, 3)},
+                        "speedup": round(ms_fp16 / ms_ev, 3),
+                        "per_layer_calls_ms_per_step": round(ms_fp16_per_layer, 4)},
+        "per_layer_calls": {"ms_per_step": round(ms_per_layer, 4),
+                            "tokens_per_s": round(1e3 / ms_per_layer, 3)},
         "wall_ms_per_step": round(ms_wall, 4),
-        "launch": "eager" if args.eager else "hip graph of the 224 calls",
+        "launch": ("eager" if args.eager else "hip graph") +
+                  " of 128 calls: hqq_linear_batch of (q, k, v), (o), (gate, up), (down) per layer",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = linear_cpu_baseline(nbits, gs)

@@ -267,7 +267,31 @@ HQQ_API int hqq_linear(const uint16_t *X, int64_t M, int64_t K,
                        const uint32_t *packed, const float *scale, const float *zero,
                        int64_t N, int nbits, int group_size, uint16_t *Y, void *stream);
 
-/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
+/* One weight of hqq_linear_batch: its axis = 1 packed codes [N, K] and fp32
+ * scale, zero [N, K / group_size] (read only), and its output Y fp16 bits
+ * [M, N] (written).  All pointers device, 16-byte aligned. */
+typedef struct hqq_linear_weight {
+    const uint32_t *packed;
+    const float *scale;
+    const float *zero;
+    int64_t N;
+    uint16_t *Y;
+} hqq_linear_weight;
+
+/* hqq_linear for count weights that share the input X (the projections of
+ * one layer that read the same activations, such as q, k and v, or gate and
+ * up), with results identical to count hqq_linear calls: Y_i = X . W_hat_i^T.
+ * The weights share K, nbits and group_size; their N differ freely.  Up to 8
+ * weights share one kernel launch, so a decode step pays the launch and
+ * pipeline fill once per launch instead of once per weight.
+ * Checks as for hqq_linear, per weight, before anything is enqueued; count =
+ * 0 is a no-op, count < 0 HQQ_EINVAL_SHAPE, ws NULL with count > 0
+ * HQQ_EINVAL_PTR.  The Y of different weights must not overlap each other or
+ * any input. */
+HQQ_API int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
+                             int count, int nbits, int group_size, void *stream);
+
+/* Number of uint32 words of the packed layout; a negative HQQ_E* status for/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */
 HQQ_API int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
 

@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(lib):
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
                                "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
-                               "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_packed_words", "hqq_strerror"])
+                               "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
+                               "hqq_linear_batch", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -130,6 +131,37 @@ def test_linear_rejects(lib):
     assert call(X=None) == E["PTR"]
     assert call(Y=MIS) == E["PTR"]
     assert call(scale=MIS) == E["PTR"]
+
+
+def test_linear_batch_rejects(lib):
+    """Every weight is checked before any launch: a bad weight after a good
+    one is reported as such (a launch would fail with HQQ_EHIP without a GPU)."""
+    import weight_quantization_group_amd as w
+
+    def ws(*specs):
+        arr = (w.HqqLinearWeight * max(1, len(specs)))()
+        for i, (pk, sc, ze, N, Y) in enumerate(specs):
+            arr[i] = w.HqqLinearWeight(pk, sc, ze, N, Y)
+        return arr
+
+    good = (0x1000, 0x2000, 0x3000, 32, 0x4000)
+
+    def call(arr, count, M=4, K=128, nbits=4, gs=64, X=A):
+        return lib.hqq_linear_batch(X, M, K, arr, count, nbits, gs, None)
+
+    assert call(ws(good), 0) == 0                  # no-op
+    assert call(None, 0) == 0
+    assert call(ws(good), -1) == E["SHAPE"]
+    assert call(None, 1) == E["PTR"]
+    assert call(ws(good), 1, nbits=3) == E["NBITS"]
+    assert call(ws(good), 1, K=48) == E["SHAPE"]
+    assert call(ws(good), 1, gs=48) == E["GROUP"]
+    assert call(ws(good), 1, X=MIS) == E["PTR"]
+    assert call(ws(good, (0x1000, 0x2000, 0x3000, 0, 0x4000)), 2) == E["SHAPE"]
+    assert call(ws(good, (0x1000, 0x2000, 0x3000, 1 << 40, 0x4000)), 2) == E["SHAPE"]
+    assert call(ws(good, (0x1000, 0x2000, 0x3001, 32, 0x4000)), 2) == E["PTR"]
+    assert call(ws(good, (0x1000, 0x2000, 0x3000, 32, None)), 2) == E["PTR"]
+    assert call(ws(*([good] * 9), (None, 0x2000, 0x3000, 32, 0x4000)), 10) == E["PTR"]
 
 
 def test_streamed_rejects(lib):

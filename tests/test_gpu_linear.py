@@ -224,3 +224,35 @@ def test_linear_repeat_and_out_buffer(hq, oracle_mod):
     assert np.array_equal(small.view(np.uint16), y1[:3].view(np.uint16))
     Yref, A = oracle_mod.linear(X16[:3], packed, scale, zero, N, nbits, gs, with_abs=True)
     check(f16_bits_to_f32(small.view(np.uint16)), Yref, A, K, "small after large")
+
+
+BATCH_CASES = [  # (M, K, nbits, gs, [N of each weight])
+    (1, 256, 4, 64, [64, 40, 300]),
+    (5, 512, 2, 32, [16, 17, 48, 100]),
+    (16, 256, 8, 64, [32, 96]),
+    (33, 128, 1, 32, [50, 16, 70]),
+    (400, 256, 4, 64, [130, 256, 60]),          # tiled kernel: 128-column tiles
+    (1, 256, 4, 16, [16] * 5 + [48] * 6),       # 11 weights: two launches
+]
+
+
+@pytest.mark.parametrize("M,K,nbits,gs,Ns", BATCH_CASES)
+def test_linear_batch_equals_single_calls(hq, oracle_mod, M, K, nbits, gs, Ns):
+    """hqq_linear_batch gives each weight exactly what hqq_linear gives it
+    (bit for bit), and the first weight's output meets the oracle bound."""
+    import torch
+
+    rng = np.random.RandomState(M * 31 + K + nbits + len(Ns))
+    X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+    Xd = _cuda(X16)
+    ws = [random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False) for N in Ns]
+    dev = [(_cuda(p), _cuda(s), _cuda(z), N) for (p, s, z), N in zip(ws, Ns)]
+    outs = hq.hqq_linear_batch(Xd, dev, nbits, gs)
+    torch.cuda.synchronize()
+    for (pk, sc, ze, N), Y in zip(dev, outs):
+        Y1 = hq.hqq_linear(Xd, pk, sc, ze, N, nbits, gs)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16)), (M, N)
+    p0, s0, z0 = ws[0]
+    Yref, A = oracle_mod.linear(X16, p0, s0, z0, Ns[0], nbits, gs, with_abs=True)
+    check(outs[0].cpu().numpy(), Yref, A, K, "batch weight 0")

@@ -29,7 +29,7 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
-           "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
+           "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_batch",
            "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
@@ -37,6 +37,8 @@ DTYPE_FP16, DTYPE_BF16 = 0, 1
 
 # tensors per kernel launch of hqq_quantize_batch
 MAX_BATCH = 24
+# weights per kernel launch of hqq_linear_batch
+LINEAR_BATCH = 8
 # meta arrays per kernel launch of hqq_quantize_meta_batch / hqq_dequantize_meta_batch
 META_BATCH = 64
 
@@ -51,6 +53,12 @@ class HqqMetaTensor(ctypes.Structure):
     """struct hqq_meta_tensor of include/hqq.h"""
     _fields_ = [("meta", ctypes.c_void_p), ("n", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("mscale", ctypes.c_void_p), ("mzero", ctypes.c_void_p)]
+
+
+class HqqLinearWeight(ctypes.Structure):
+    """struct hqq_linear_weight of include/hqq.h"""
+    _fields_ = [("packed", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("Y", ctypes.c_void_p)]
 
 
 class HqqHostTensor(ctypes.Structure):
@@ -102,6 +110,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_dequantize_meta_batch.restype = i32
     L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_linear.restype = i32
+    L.hqq_linear_batch.argtypes = [P, i64, i64, P, i32, i32, i32, P]
+    L.hqq_linear_batch.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
     L.hqq_packed_words.restype = i64
     L.hqq_strerror.argtypes = [i32]
@@ -290,6 +300,46 @@ def hqq_linear(X: torch.Tensor, packed, scale, zero, N: int, nbits: int, group_s
     if st != 0:
         raise HQQError("hqq_linear", st)
     return out
+
+
+class LinearBatch:
+    """Weights that share the input X, for hqq_linear_batch, marshalled into
+    the C descriptor array once; run(X) is then a single C-ABI call (one
+    launch per 8 weights) on the current stream.  weights: list of (packed,
+    scale, zero, N, Y) with Y a preallocated fp16 [M, N] CUDA tensor; the
+    tensors are kept alive by the object."""
+
+    def __init__(self, weights, nbits: int, group_size: int):
+        self._lib = load_library()
+        self._items = [tuple(w) for w in weights]
+        self.nbits, self.group_size = nbits, group_size
+        arr = (HqqLinearWeight * max(1, len(self._items)))()
+        for i, (pk, sc, ze, N, Y) in enumerate(self._items):
+            arr[i] = HqqLinearWeight(_dev_ptr(pk, "packed", _U32).value,
+                                     _dev_ptr(sc, "scale", (torch.float32,)).value,
+                                     _dev_ptr(ze, "zero", (torch.float32,)).value, N,
+                                     _dev_ptr(Y, "Y", _F16).value)
+        self._arr = arr
+
+    def run(self, X: torch.Tensor):
+        M, K = X.shape
+        for (_, _, _, N, Y) in self._items:
+            if tuple(Y.shape) != (M, N):
+                raise ValueError(f"Y must be [{M}, {N}], got {tuple(Y.shape)}")
+        st = self._lib.hqq_linear_batch(_dev_ptr(X, "X", _F16), M, K, self._arr, len(self._items),
+                                        self.nbits, self.group_size, _stream(X.device))
+        if st != 0:
+            raise HQQError("hqq_linear_batch", st)
+        return [it[4] for it in self._items]
+
+
+def hqq_linear_batch(X: torch.Tensor, weights, nbits: int, group_size: int):
+    """[X . W_hat_i^T] for weights [(packed, scale, zero, N), ...] sharing X,
+    in one C-ABI call.  Returns the fp16 outputs."""
+    M = X.shape[0]
+    items = [(pk, sc, ze, N, torch.empty((M, N), dtype=torch.float16, device=X.device))
+             for (pk, sc, ze, N) in weights]
+    return LinearBatch(items, nbits, group_size).run(X)
 
 
 def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging: torch.Tensor,

@@ -333,46 +333,73 @@ int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols, int nbits, in
     return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
 }
 
-int hqq_linear(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
-               const float *scale, const float *zero, int64_t N, int nbits, int group_size,
-               uint16_t *Y, void *stream)
+int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws, int count,
+                     int nbits, int group_size, void *stream)
 {
     if (!hqq::valid_nbits(nbits) || nbits == 3)
         return HQQ_EINVAL_NBITS;
-    if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
-        M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)
+    if (count < 0)
         return HQQ_EINVAL_SHAPE;
-    // gridDim.x = ceil(N / 16) and gridDim.y = ceil(M / 32) must fit the launch
-    // limits, and the kernels address X, the codes and the meta with 32-bit
-    // byte offsets
+    if (count > 0 && !ws)
+        return HQQ_EINVAL_PTR;
+    if (M < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || K > kMaxDim || M * K > kMaxElems)
+        return HQQ_EINVAL_SHAPE;
+    // gridDim.y = ceil(M / 32) must fit the launch limits, and the kernels
+    // address X, the codes and the meta with 32-bit byte offsets
     const int64_t kMaxBytes = int64_t(1) << 31;
-    if ((N + 15) / 16 > 0x7fffffff || (M + 31) / 32 > 0xffff || M * K * 2 >= kMaxBytes ||
-        N * (K * nbits / 32) * 4 >= kMaxBytes || N * (K / 8) * 4 >= kMaxBytes)
+    if ((M + 31) / 32 > 0xffff || M * K * 2 >= kMaxBytes)
         return HQQ_EINVAL_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        const int64_t N = ws[i].N;
+        if (N < 1 || N > kMaxDim || N * K > kMaxElems || M * N > kMaxElems ||
+            N * (K * nbits / 32) * 4 >= kMaxBytes || N * (K / 8) * 4 >= kMaxBytes)
+            return HQQ_EINVAL_SHAPE;
+    }
     int gshift = -1;
     for (int b = 3; b <= 8; ++b)
         if (group_size == (1 << b))
             gshift = b;
     if (gshift < 0 || K % group_size != 0)
         return HQQ_EINVAL_GROUP;
-    if (!aligned16(X) || !aligned16(packed) || !aligned16(scale) || !aligned16(zero) ||
-        !aligned16(Y))
+    if (!aligned16(X))
         return HQQ_EINVAL_PTR;
-    hqq::LinearArgs a{};
-    a.X = X;
-    a.packed = packed;
-    a.scale = scale;
-    a.zero = zero;
-    a.Y = Y;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.wpr = K * nbits / 32;
-    a.gpl = K / group_size;
-    a.gs = group_size;
-    a.gshift = gshift;
-    const hipError_t e = hqq::launch_linear(nbits, a, (hipStream_t)stream);
-    return e == hipSuccess ? HQQ_OK : HQQ_EHIP;
+    for (int i = 0; i < count; ++i)
+        if (!aligned16(ws[i].packed) || !aligned16(ws[i].scale) || !aligned16(ws[i].zero) ||
+            !aligned16(ws[i].Y))
+            return HQQ_EINVAL_PTR;
+    hqq::LinearBatch b{};
+    b.a.X = X;
+    b.a.M = M;
+    b.a.K = K;
+    b.a.wpr = K * nbits / 32;
+    b.a.gpl = K / group_size;
+    b.a.gs = group_size;
+    b.a.gshift = gshift;
+    // up to kLinBatch weights per launch (at most 8 x 2^27 column tiles: the
+    // grid's x dimension stays below 2^31)
+    for (int i0 = 0; i0 < count; i0 += hqq::kLinBatch) {
+        b.count = count - i0 < hqq::kLinBatch ? count - i0 : hqq::kLinBatch;
+        for (int j = 0; j < b.count; ++j) {
+            const hqq_linear_weight &w = ws[i0 + j];
+            b.packed[j] = w.packed;
+            b.scale[j] = w.scale;
+            b.zero[j] = w.zero;
+            b.Y[j] = w.Y;
+            b.N[j] = w.N;
+        }
+        if (hqq::launch_linear(nbits, b, (hipStream_t)stream) != hipSuccess)
+            return HQQ_EHIP;
+    }
+    return HQQ_OK;
+}
+
+int hqq_linear(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
+               const float *scale, const float *zero, int64_t N, int nbits, int group_size,
+               uint16_t *Y, void *stream)
+{
+    // null or misaligned pointers are rejected by the batch's alignment check
+    const hqq_linear_weight w{packed, scale, zero, N, Y};
+    return hqq_linear_batch(X, M, K, &w, 1, nbits, group_size, stream);
 }
 
 int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint8_t *codes, float *mscale,

@@ -80,6 +80,20 @@ struct LinearArgs {
     int gs, gshift;          // group size and its log2
 };
 
+// Several weights that share X (and K and the code format) in one launch:
+// weight j's column tiles are grid columns tile0[j] .. tile0[j + 1] - 1.
+constexpr int kLinBatch = 8;
+struct LinearBatch {
+    LinearArgs a;    // X, M, K, wpr, gpl, gs, gshift (its per-weight fields unused)
+    int count;
+    uint32_t tile0[kLinBatch + 1];   // filled by the launcher
+    const uint32_t *packed[kLinBatch];
+    const float *scale[kLinBatch];
+    const float *zero[kLinBatch];
+    uint16_t *Y[kLinBatch];
+    int64_t N[kLinBatch];
+};
+
 // host-side argument checks shared by the entry points (HQQ_* status)
 int check_params(int iters, float p, float beta0, float kappa);
 int check_tensor(const ::hqq_tensor &t, int nbits, int group_size, int axis);
@@ -89,7 +103,7 @@ hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, const So
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
-hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s);
+hipError_t launch_linear(int nbits, LinearBatch &b, hipStream_t s);
 // meta arrays per launch of the meta kernels (descriptors by value)
 constexpr int kMetaBatch = 64;
 

@@ -159,6 +159,25 @@ __device__ __forceinline__ Chunk lane_chunk(uint32_t kbase, int grp, uint32_t K)
     return Chunk{k0, kh};
 }
 
+// The weight of a batch that grid column bx belongs to (uniform; count <=
+// kLinBatch): the shared arguments with that weight's pointers and N; bx
+// becomes the column tile within the weight.
+__device__ __forceinline__ LinearArgs batch_item(const LinearBatch &b, uint32_t &bx)
+{
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < kLinBatch; ++k)
+        j = k < b.count && bx >= b.tile0[k] ? k : j;
+    LinearArgs a = b.a;
+    a.packed = b.packed[j];
+    a.scale = b.scale[j];
+    a.zero = b.zero[j];
+    a.Y = b.Y[j];
+    a.N = b.N[j];
+    bx -= b.tile0[j];
+    return a;
+}
+
 template <typename T>
 __device__ __forceinline__ const T *at(const void *base, uint32_t byte_off)
 {
@@ -307,14 +326,16 @@ constexpr int lin_waves_per_simd(int nb, int mt, int gpc, bool xl)
 
 template <bool KT, int NB, int MT, int GPC, bool XL, int WPB>
 __global__ __launch_bounds__(WPB * 64)
-__attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void linear_skinny_kernel(LinearArgs a)
+__attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void linear_skinny_kernel(LinearBatch lb)
 {
+    uint32_t bx = blockIdx.x;
+    const LinearArgs a = batch_item(lb, bx);
     extern __shared__ uint4 lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane16 = lane & 15, grp = lane >> 4;
     const uint32_t K = (uint32_t)a.K;
-    const int64_t n_raw = (int64_t)blockIdx.x * 16 + lane16;
+    const int64_t n_raw = (int64_t)bx * 16 + lane16;
     const uint32_t n = (uint32_t)(n_raw < a.N ? n_raw : a.N - 1);
     const uint32_t nw = n * (uint32_t)a.wpr, ng = n * (uint32_t)a.gpl;
     const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
@@ -387,7 +408,7 @@ __attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void l
         // accumulator r of lane l is D[4 * (l / 16) + r][l % 16] of tile u
         const int u = v >> 2, r = v & 3;
         const int64_t m = m0 + 16 * u + 4 * (l >> 4) + r;
-        const int64_t nn = (int64_t)blockIdx.x * 16 + (l & 15);
+        const int64_t nn = (int64_t)bx * 16 + (l & 15);
         if (m < a.M && nn < a.N) {
             const _Float16 h = (_Float16)s;
             __builtin_memcpy(&a.Y[m * a.N + nn], &h, 2);
@@ -406,9 +427,22 @@ inline int lin_waves(int64_t blocks, int64_t K)
     return w;
 }
 
-template <int NB, int MT, int GPC, bool XL, int WPB>
-hipError_t launch_wpb(const LinearArgs &a, dim3 grid, hipStream_t s)
+// grid columns of the batch: tile0[j] = first column tile of weight j
+inline uint32_t fill_tiles(LinearBatch &b, int64_t cols_per_tile)
 {
+    uint32_t t = 0;
+    for (int j = 0; j < b.count; ++j) {
+        b.tile0[j] = t;
+        t += (uint32_t)((b.N[j] + cols_per_tile - 1) / cols_per_tile);
+    }
+    b.tile0[b.count] = t;
+    return t;
+}
+
+template <int NB, int MT, int GPC, bool XL, int WPB>
+hipError_t launch_wpb(const LinearBatch &b, dim3 grid, hipStream_t s)
+{
+    const LinearArgs &a = b.a;
     size_t lds = (size_t)WPB * MT * 4 * 64 * sizeof(float);
     if (XL) {
         const int64_t rows = a.M < 16 * MT ? a.M : 16 * MT;
@@ -417,40 +451,42 @@ hipError_t launch_wpb(const LinearArgs &a, dim3 grid, hipStream_t s)
     }
     if (a.K % kStepK != 0)
         hipLaunchKernelGGL((linear_skinny_kernel<true, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
-                           lds, s, a);
+                           lds, s, b);
     else
         hipLaunchKernelGGL((linear_skinny_kernel<false, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
-                           lds, s, a);
+                           lds, s, b);
     return hipGetLastError();
 }
 
 template <int NB, int MT, int GPC, bool XL>
-hipError_t launch_one(const LinearArgs &a, hipStream_t s)
+hipError_t launch_one(LinearBatch &b, hipStream_t s)
 {
-    const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
+    const LinearArgs &a = b.a;
+    const dim3 grid(fill_tiles(b, 16), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
     switch (lin_waves((int64_t)grid.x * grid.y, a.K)) {
-    case 4: return launch_wpb<NB, MT, GPC, XL, 4>(a, grid, s);
-    case 8: return launch_wpb<NB, MT, GPC, XL, 8>(a, grid, s);
-    default: return launch_wpb<NB, MT, GPC, XL, 16>(a, grid, s);
+    case 4: return launch_wpb<NB, MT, GPC, XL, 4>(b, grid, s);
+    case 8: return launch_wpb<NB, MT, GPC, XL, 8>(b, grid, s);
+    default: return launch_wpb<NB, MT, GPC, XL, 16>(b, grid, s);
     }
 }
 
 template <int NB, int MT, int GPC>
-hipError_t launch_xl(const LinearArgs &a, hipStream_t s)
+hipError_t launch_xl(LinearBatch &b, hipStream_t s)
 {
+    const LinearArgs &a = b.a;
     const int64_t rows = a.M < 16 * MT ? a.M : 16 * MT;
     if (rows * (a.K / 8 + 1) * 16 <= kXldsMax)
-        return launch_one<NB, MT, GPC, true>(a, s);
-    return launch_one<NB, MT, GPC, false>(a, s);
+        return launch_one<NB, MT, GPC, true>(b, s);
+    return launch_one<NB, MT, GPC, false>(b, s);
 }
 
 template <int NB, int MT>
-hipError_t launch_gpc(const LinearArgs &a, hipStream_t s)
+hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 {
-    switch (groups_per_chunk(a.gs)) {
-    case 1: return launch_xl<NB, MT, 1>(a, s);
-    case 2: return launch_xl<NB, MT, 2>(a, s);
-    default: return launch_xl<NB, MT, 8>(a, s);
+    switch (groups_per_chunk(b.a.gs)) {
+    case 1: return launch_xl<NB, MT, 1>(b, s);
+    case 2: return launch_xl<NB, MT, 2>(b, s);
+    default: return launch_xl<NB, MT, 8>(b, s);
     }
 }
 
@@ -543,8 +579,10 @@ __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 
 
 
 template <int NB, bool G1>
-__global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearArgs a)
+__global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
 {
+    uint32_t bx = blockIdx.x;
+    const LinearArgs a = batch_item(lb, bx);
     constexpr int TM = kTBM / 32, TN = kTBN / 32;   // MFMA tiles per wave (8 x 4)
     typedef __attribute__((address_space(3))) void *lds_ptr;
     __shared__ uint4 xs[3][kTBM * 8];
@@ -552,7 +590,7 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kTBM, n0 = (int64_t)blockIdx.x * kTBN;
+    const int64_t m0 = (int64_t)blockIdx.y * kTBM, n0 = (int64_t)bx * kTBN;
     const uint32_t K = (uint32_t)a.K;
     const uint32_t steps = K / kTK;
 
@@ -680,13 +718,13 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearArgs a)
 }
 
 template <int NB>
-hipError_t launch_tiled(const LinearArgs &a, hipStream_t s)
+hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
-    const dim3 grid((unsigned)((a.N + kTBN - 1) / kTBN), (unsigned)((a.M + kTBM - 1) / kTBM));
-    if (a.gs >= 32)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true>), grid, dim3(256), 0, s, a);
+    const dim3 grid(fill_tiles(b, kTBN), (unsigned)((b.a.M + kTBM - 1) / kTBM));
+    if (b.a.gs >= 32)
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true>), grid, dim3(256), 0, s, b);
     else
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, false>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
@@ -696,27 +734,27 @@ hipError_t launch_tiled(const LinearArgs &a, hipStream_t s)
 constexpr int64_t kTiledMinRows = 384;
 
 template <int NB>
-hipError_t launch_nb(const LinearArgs &a, hipStream_t s)
+hipError_t launch_nb(LinearBatch &b, hipStream_t s)
 {
     if constexpr (NB >= 2) {
-        if (a.M >= kTiledMinRows && a.K % kTK == 0)
-            return launch_tiled<NB>(a, s);
+        if (b.a.M >= kTiledMinRows && b.a.K % kTK == 0)
+            return launch_tiled<NB>(b, s);
     }
     // skinny: M > 32 runs ceil(M / 32) row blocks of 32
-    if (a.M <= 16)
-        return launch_gpc<NB, 1>(a, s);
-    return launch_gpc<NB, 2>(a, s);
+    if (b.a.M <= 16)
+        return launch_gpc<NB, 1>(b, s);
+    return launch_gpc<NB, 2>(b, s);
 }
 
 }  // namespace
 
-hipError_t launch_linear(int nbits, const LinearArgs &a, hipStream_t s)
+hipError_t launch_linear(int nbits, LinearBatch &b, hipStream_t s)
 {
     switch (nbits) {
-    case 1: return launch_nb<1>(a, s);
-    case 2: return launch_nb<2>(a, s);
-    case 4: return launch_nb<4>(a, s);
-    case 8: return launch_nb<8>(a, s);
+    case 1: return launch_nb<1>(b, s);
+    case 2: return launch_nb<2>(b, s);
+    case 4: return launch_nb<4>(b, s);
+    case 8: return launch_nb<8>(b, s);
     default: return hipErrorInvalidValue;
     }
 }
