@@ -299,9 +299,13 @@ def bench_linear(args):
     g = Eager(token) if args.eager else graph_of(token)
     ms_ev, ms_wall = timed(g, args.steps, args.warmup)
     del g
-    g = Eager(token_per_layer) if args.eager else graph_of(token_per_layer)
-    ms_per_layer, _ = timed(g, args.steps, args.warmup)
-    del g
+    # context: one call per product (skipped for profiler runs, whose
+    # per-dispatch counters must see the batched calls only)
+    ms_per_layer = None
+    if not args.no_per_layer:
+        g = Eager(token_per_layer) if args.eager else graph_of(token_per_layer)
+        ms_per_layer, _ = timed(g, args.steps, args.warmup)
+        del g
 
     # the fp16 reference: the same 224 products with distinct fp16 weights
     # (12.95 GB) through torch.matmul (hipBLASLt), with the same sharing of
@@ -331,9 +335,12 @@ def bench_linear(args):
     gf = Eager(token_fp16) if args.eager else graph_of(token_fp16)
     ms_fp16, _ = timed(gf, args.steps, args.warmup)
     del gf
-    gf = Eager(token_fp16_per_layer) if args.eager else graph_of(token_fp16_per_layer)
-    ms_fp16_per_layer, _ = timed(gf, args.steps, args.warmup)
-    del gf, Wf
+    ms_fp16_per_layer = None
+    if not args.no_per_layer:
+        gf = Eager(token_fp16_per_layer) if args.eager else graph_of(token_fp16_per_layer)
+        ms_fp16_per_layer, _ = timed(gf, args.steps, args.warmup)
+        del gf
+    del Wf
 
     bytes_per_token = sum(N * K * nbits / 8 + N * (K // gs) * 8 + K * 2 + N * 2
                           for (N, K) in LLAMA7B_LINEARS) * LLAMA7B_LAYERS
@@ -361,9 +368,10 @@ def bench_linear(args):
                      "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
         "fp16_matmul": {"ms_per_step": round(ms_fp16, 4), "tokens_per_s": round(1e3 / ms_fp16, 3),
                         "speedup": round(ms_fp16 / ms_ev, 3),
-                        "per_layer_calls_ms_per_step": round(ms_fp16_per_layer, 4)},
+                        "per_layer_calls_ms_per_step":
+                            round(ms_fp16_per_layer, 4) if ms_fp16_per_layer else None},
         "per_layer_calls": {"ms_per_step": round(ms_per_layer, 4),
-                            "tokens_per_s": round(1e3 / ms_per_layer, 3)},
+                            "tokens_per_s": round(1e3 / ms_per_layer, 3)} if ms_per_layer else None,
         "wall_ms_per_step": round(ms_wall, 4),
         "launch": ("eager" if args.eager else "hip graph") +
                   " of 128 calls: hqq_linear_batch of (q, k, v), (o), (gate, up), (down) per layer",
@@ -533,6 +541,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-per-layer", action="store_true",
+                    help="linear: skip the one-call-per-product context timings (profiler runs)")
     ap.add_argument("--wdtype", choices=("f16", "bf16"), default="f16",
                     help="solve: element type of the weights (bf16: the synthetic fp16 weights rounded to bf16)")
     ap.add_argument("--eager", action="store_true",
