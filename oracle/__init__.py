@@ -82,6 +82,8 @@ def _bind(L):
     L.hqq_ref_dequantize.restype = i32
     L.hqq_ref_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_ref_linear.restype = i32
+    L.hqq_ref_linear_dt.argtypes = [P, i32, i64, i64, P, P, P, i64, i32, i32, P, P]
+    L.hqq_ref_linear_dt.restype = i32
     return L
 
 
@@ -239,8 +241,9 @@ def dequantize(packed, scale, zero, rows, cols, nbits, group_size, axis, dtype="
     return out
 
 
-def linear(X16: np.ndarray, packed, scale, zero, N, nbits, group_size, with_abs=False):
-    """Y = X @ W_hat^T in fp64 (X fp16 bits [M, K]; axis = 1 weight [N, K]).
+def linear(X16: np.ndarray, packed, scale, zero, N, nbits, group_size, with_abs=False, dtype="f16"):
+    """Y = X @ W_hat^T in fp64 (X fp16 or, dtype="bf16", bf16 bits [M, K];
+    axis = 1 weight [N, K], W_hat dequantized into the same dtype).
     Returns Y [M, N] (and sum |x w| per output with with_abs)."""
     X16 = np.ascontiguousarray(X16, dtype=np.uint16)
     M, K = X16.shape
@@ -249,8 +252,8 @@ def linear(X16: np.ndarray, packed, scale, zero, N, nbits, group_size, with_abs=
     zero = np.ascontiguousarray(zero, dtype=np.float32)
     Y = np.zeros((M, N), np.float64)
     A = np.zeros((M, N), np.float64)
-    st = lib().hqq_ref_linear(_ptr(X16), M, K, _ptr(packed), _ptr(scale), _ptr(zero), N, nbits,
-                              group_size, _ptr(Y), _ptr(A))
+    st = lib().hqq_ref_linear_dt(_ptr(X16), DTYPES[dtype], M, K, _ptr(packed), _ptr(scale), _ptr(zero),
+                                 N, nbits, group_size, _ptr(Y), _ptr(A))
     _check(st, "linear")
     return (Y, A) if with_abs else Y
 

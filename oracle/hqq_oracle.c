@@ -512,6 +512,19 @@ int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
                    const uint32_t *packed, const float *scale, const float *zero,
                    int64_t N, int nbits, int group_size, double *Y, double *absY)
 {
+    return hqq_ref_linear_dt(X, HQQ_REF_F16, M, K, packed, scale, zero, N, nbits, group_size, Y, absY);
+}
+
+/* The quantized layer's forward in compute dtype fp16 or bf16: W_hat is the
+ * dequantization into that dtype (lnwmold.com HQQ guide section 3.2, the
+ * HQQLinear layer computes in compute_dtype), X is given in it, and each
+ * output is the exact (fp64) sum of the products of the widened values. */
+int hqq_ref_linear_dt(const uint16_t *X, int dtype, int64_t M, int64_t K,
+                      const uint32_t *packed, const float *scale, const float *zero,
+                      int64_t N, int nbits, int group_size, double *Y, double *absY)
+{
+    if (dtype != HQQ_REF_F16 && dtype != HQQ_REF_BF16)
+        return -8;
     if (M < 1)
         return -4;
     int st = check_shape(N, K, nbits, group_size, 1);
@@ -522,14 +535,14 @@ int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
     uint16_t *W_hat = (uint16_t *)malloc((size_t)(N * K) * sizeof(uint16_t));
     if (!W_hat)
         return -2;
-    st = hqq_ref_dequantize(packed, scale, zero, N, K, nbits, group_size, 1, W_hat);
+    st = hqq_ref_dequantize_dt(packed, scale, zero, N, K, nbits, group_size, 1, dtype, W_hat);
     if (st == 0) {
         for (int64_t m = 0; m < M; ++m)
             for (int64_t n = 0; n < N; ++n) {
                 double acc = 0.0, mag = 0.0;
                 for (int64_t k = 0; k < K; ++k) {
-                    double prod = (double)hqq_ref_f16_to_f32(X[m * K + k]) *
-                                  (double)hqq_ref_f16_to_f32(W_hat[n * K + k]);
+                    double prod = (double)widen16(X[m * K + k], dtype) *
+                                  (double)widen16(W_hat[n * K + k], dtype);
                     acc += prod;
                     mag += fabs(prod);
                 }

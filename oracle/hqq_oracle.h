@@ -124,6 +124,13 @@ int hqq_ref_linear(const uint16_t *X, int64_t M, int64_t K,
                    const uint32_t *packed, const float *scale, const float *zero,
                    int64_t N, int nbits, int group_size, double *Y, double *absY);
 
+/* The same in compute dtype fp16 or bf16 (HQQ_REF_F16 / HQQ_REF_BF16): X is
+ * given in that dtype and W_hat is the dequantization into it
+ * (hqq_ref_dequantize_dt); -8 for another dtype. */
+int hqq_ref_linear_dt(const uint16_t *X, int dtype, int64_t M, int64_t K,
+                      const uint32_t *packed, const float *scale, const float *zero,
+                      int64_t N, int nbits, int group_size, double *Y, double *absY);
+
 #ifdef __cplusplus
 }
 #endif
