@@ -267,9 +267,21 @@ HQQ_API int hqq_linear(const uint16_t *X, int64_t M, int64_t K,
                        const uint32_t *packed, const float *scale, const float *zero,
                        int64_t N, int nbits, int group_size, uint16_t *Y, void *stream);
 
+/* hqq_linear in compute dtype fp16 or bf16 (HQQ_DTYPE_FP16 / HQQ_DTYPE_BF16;
+ * lnwmold.com HQQ guide section 3.2: the layer computes in its
+ * compute_dtype): X and Y hold that dtype's bits, W_hat is what
+ * hqq_dequantize_ex writes for that dtype (the bf16 rounding of the same
+ * fp32 quotient), the products are exact in fp32 and each output is rounded
+ * to the dtype once, round-half-even.  Another dtype: HQQ_EINVAL_DTYPE.
+ * Otherwise as hqq_linear (which is this call with HQQ_DTYPE_FP16). */
+HQQ_API int hqq_linear_ex(const uint16_t *X, int64_t M, int64_t K,
+                          const uint32_t *packed, const float *scale, const float *zero,
+                          int64_t N, int nbits, int group_size, int dtype, uint16_t *Y,
+                          void *stream);
+
 /* One weight of hqq_linear_batch: its axis = 1 packed codes [N, K] and fp32
- * scale, zero [N, K / group_size] (read only), and its output Y fp16 bits
- * [M, N] (written).  All pointers device, 16-byte aligned. */
+ * scale, zero [N, K / group_size] (read only), and its output Y [M, N] in the
+ * compute dtype (written).  All pointers device, 16-byte aligned. */
 typedef struct hqq_linear_weight {
     const uint32_t *packed;
     const float *scale;
@@ -286,10 +298,11 @@ typedef struct hqq_linear_weight {
  * pipeline fill once per launch instead of once per weight.
  * Checks as for hqq_linear, per weight, before anything is enqueued; count =
  * 0 is a no-op, count < 0 HQQ_EINVAL_SHAPE, ws NULL with count > 0
- * HQQ_EINVAL_PTR.  The Y of different weights must not overlap each other or
+ * HQQ_EINVAL_PTR.  dtype: the compute dtype of X and the Y, as for
+ * hqq_linear_ex.  The Y of different weights must not overlap each other or
  * any input. */
 HQQ_API int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
-                             int count, int nbits, int group_size, void *stream);
+                             int count, int nbits, int group_size, int dtype, void *stream);
 
 /* Number of uint32 words of the packed layout; a negative HQQ_E* status for/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
                                "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
                                "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
-                               "hqq_linear_batch", "hqq_packed_words", "hqq_strerror"])
+                               "hqq_linear_ex", "hqq_linear_batch", "hqq_packed_words", "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
     # and nothing else: the dynamic symbol table holds exactly the C ABI
@@ -146,8 +146,8 @@ def test_linear_batch_rejects(lib):
 
     good = (0x1000, 0x2000, 0x3000, 32, 0x4000)
 
-    def call(arr, count, M=4, K=128, nbits=4, gs=64, X=A):
-        return lib.hqq_linear_batch(X, M, K, arr, count, nbits, gs, None)
+    def call(arr, count, M=4, K=128, nbits=4, gs=64, X=A, dtype=0):
+        return lib.hqq_linear_batch(X, M, K, arr, count, nbits, gs, dtype, None)
 
     assert call(ws(good), 0) == 0                  # no-op
     assert call(None, 0) == 0
@@ -162,6 +162,12 @@ def test_linear_batch_rejects(lib):
     assert call(ws(good, (0x1000, 0x2000, 0x3001, 32, 0x4000)), 2) == E["PTR"]
     assert call(ws(good, (0x1000, 0x2000, 0x3000, 32, None)), 2) == E["PTR"]
     assert call(ws(*([good] * 9), (None, 0x2000, 0x3000, 32, 0x4000)), 10) == E["PTR"]
+    assert call(ws(good), 1, dtype=2) == E["DTYPE"]
+    assert call(ws(good), 1, dtype=-1) == E["DTYPE"]
+    # the single-weight entry points
+    assert lib.hqq_linear_ex(A, 4, 128, A, A, A, 32, 4, 64, 5, A, None) == E["DTYPE"]
+    assert lib.hqq_linear_ex(A, 4, 128, A, A, A, 32, 3, 64, 1, A, None) == E["NBITS"]
+    assert lib.hqq_linear_ex(A, 4, 128, A, A, A, 32, 4, 64, 1, MIS, None) == E["PTR"]
 
 
 def test_streamed_rejects(lib):

@@ -256,3 +256,90 @@ def test_linear_batch_equals_single_calls(hq, oracle_mod, M, K, nbits, gs, Ns):
     p0, s0, z0 = ws[0]
     Yref, A = oracle_mod.linear(X16, p0, s0, z0, Ns[0], nbits, gs, with_abs=True)
     check(outs[0].cpu().numpy(), Yref, A, K, "batch weight 0")
+
+
+# ---------------------------------------------------------------------------
+# compute dtype bf16 (hqq_linear_ex): X and Y in bf16, W_hat the bf16
+# rounding of the same fp32 quotient.  Products of bf16 values are exact in
+# fp32; the output rounds once to bf16 (half an ulp: 2^-8 relative), so the
+# bound is |Y - Yref| <= 2^-8 |Yref| + 1.01 K 2^-24 A + 2^-133.
+
+
+def bf16_bits_to_f32(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def random_bf16(rng, shape, std=1.0):
+    """bf16 bits of seeded normal values (truncated to bf16: exact inputs)."""
+    f = (rng.randn(*shape) * std).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gpu_linear_bf16(hq, Xb, packed, scale, zero, N, nbits, gs):
+    import torch
+
+    X = torch.from_numpy(Xb.view(np.int16)).cuda().view(torch.bfloat16)
+    Y = hq.hqq_linear(X, _cuda(packed), _cuda(scale), _cuda(zero), N, nbits, gs)
+    torch.cuda.synchronize()
+    assert Y.dtype == torch.bfloat16
+    return Y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_bf16(Yb, Yref, A, K, tag=""):
+    Y = bf16_bits_to_f32(Yb).astype(np.float64)
+    assert np.all(np.isfinite(Y)), tag
+    err = np.abs(Y - Yref)
+    bound = 2.0 ** -8 * np.abs(Yref) + 1.01 * K * 2.0 ** -24 * A + 2.0 ** -133
+    worst = np.max(err / bound)
+    assert worst <= 1.0, f"{tag}: worst error / bound = {worst:.3g}"
+
+
+BF16_CASES = [c for i, c in enumerate(CASES) if i % 3 == 0] + [(400, 300, 256, 4, 64), (640, 256, 320, 8, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,nbits,gs", BF16_CASES)
+def test_linear_bf16_parity(hq, oracle_mod, M, N, K, nbits, gs):
+    rng = np.random.RandomState(5000 + M * 7 + N + K + nbits * 13 + gs)
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs)
+    Xb = random_bf16(rng, (M, K))
+    Y = gpu_linear_bf16(hq, Xb, packed, scale, zero, N, nbits, gs)
+    Yref, A = oracle_mod.linear(Xb, packed, scale, zero, N, nbits, gs, with_abs=True, dtype="bf16")
+    check_bf16(Y, Yref, A, K, f"bf16 {M}x{N}x{K} b{nbits} g{gs}")
+
+
+@pytest.mark.parametrize("nbits,gs,K", [(4, 64, 256), (2, 16, 256), (8, 128, 256), (4, 32, 384), (1, 32, 256)])
+def test_linear_bf16_identity_gives_bf16_w_hat_exactly(hq, oracle_mod, nbits, gs, K):
+    """X = I in bf16: Y = the oracle's bf16 dequantization, bit for bit (one
+    nonzero product per output; -0 weights come out +0).  K = 384 runs the
+    tiled kernel."""
+    rng = np.random.RandomState(70 + nbits + gs)
+    N = 40
+    codes = rng.randint(0, (1 << nbits), size=(N, K)).astype(np.uint8)
+    scale = (rng.uniform(1, 2, (N, K // gs)) * 2.0 ** rng.randint(-20, 60, (N, K // gs))).astype(np.float32)
+    zero = rng.uniform(-300, 300, (N, K // gs)).astype(np.float32)
+    packed = oracle_mod.pack(codes, nbits, 1)
+    X = (np.eye(K, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    Y = gpu_linear_bf16(hq, X, packed, scale, zero, N, nbits, gs)
+    W = oracle_mod.dequantize(packed, scale, zero, N, K, nbits, gs, 1, dtype="bf16").T
+    Yf, Wf = bf16_bits_to_f32(Y), bf16_bits_to_f32(W)
+    bad = np.argwhere((Y != W) & ((Wf != 0) | (Yf != 0)))
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}"
+
+
+def test_linear_bf16_batch_equals_single_calls(hq, oracle_mod):
+    import torch
+
+    rng = np.random.RandomState(77)
+    M, K, nbits, gs, Ns = 3, 256, 4, 64, [64, 100, 32]
+    X = torch.from_numpy(random_bf16(rng, (M, K)).view(np.int16)).cuda().view(torch.bfloat16)
+    dev = []
+    for N in Ns:
+        p, s, z = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+        dev.append((_cuda(p), _cuda(s), _cuda(z), N))
+    outs = hq.hqq_linear_batch(X, dev, nbits, gs)
+    torch.cuda.synchronize()
+    for (pk, sc, ze, N), Y in zip(dev, outs):
+        assert Y.dtype == torch.bfloat16
+        Y1 = hq.hqq_linear(X, pk, sc, ze, N, nbits, gs)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))

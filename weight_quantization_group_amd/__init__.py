@@ -29,7 +29,7 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
-           "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_batch",
+           "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_ex", "hqq_linear_batch",
            "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
@@ -110,7 +110,9 @@ def load_library(path: str = LIB_PATH):
     L.hqq_dequantize_meta_batch.restype = i32
     L.hqq_linear.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, P, P]
     L.hqq_linear.restype = i32
-    L.hqq_linear_batch.argtypes = [P, i64, i64, P, i32, i32, i32, P]
+    L.hqq_linear_ex.argtypes = [P, i64, i64, P, P, P, i64, i32, i32, i32, P, P]
+    L.hqq_linear_ex.restype = i32
+    L.hqq_linear_batch.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P]
     L.hqq_linear_batch.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
     L.hqq_packed_words.restype = i64
@@ -285,20 +287,29 @@ def hqq_unpack(packed: torch.Tensor, rows: int, cols: int, nbits: int, group_siz
     return out
 
 
+def _compute_dtype(X: torch.Tensor):
+    """(C dtype code, torch dtype, accepted tensor dtypes) of an activation."""
+    if X.dtype == torch.bfloat16:
+        return DTYPE_BF16, torch.bfloat16, (torch.bfloat16,)
+    return DTYPE_FP16, torch.float16, _F16
+
+
 def hqq_linear(X: torch.Tensor, packed, scale, zero, N: int, nbits: int, group_size: int,
                out=None) -> torch.Tensor:
-    """Y = X . W_hat^T (fp16 [M, N]) for X fp16 [M, K] and the axis = 1
-    quantized weight W [N, K] given by (packed, scale, zero)."""
+    """Y = X . W_hat^T ([M, N]) for X [M, K] and the axis = 1 quantized weight
+    W [N, K] given by (packed, scale, zero).  The compute dtype is X's: fp16
+    (or int16 / uint16 fp16 bits), or bfloat16."""
     L = load_library()
     M, K = X.shape
+    code, tdt, ok = _compute_dtype(X)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    st = L.hqq_linear(_dev_ptr(X, "X", _F16), M, K, _dev_ptr(packed, "packed", _U32),
-                      _dev_ptr(scale, "scale", (torch.float32,)),
-                      _dev_ptr(zero, "zero", (torch.float32,)), N, nbits, group_size,
-                      _dev_ptr(out, "out", _F16), _stream(X.device))
+        out = torch.empty((M, N), dtype=tdt, device=X.device)
+    st = L.hqq_linear_ex(_dev_ptr(X, "X", ok), M, K, _dev_ptr(packed, "packed", _U32),
+                         _dev_ptr(scale, "scale", (torch.float32,)),
+                         _dev_ptr(zero, "zero", (torch.float32,)), N, nbits, group_size, code,
+                         _dev_ptr(out, "out", ok), _stream(X.device))
     if st != 0:
-        raise HQQError("hqq_linear", st)
+        raise HQQError("hqq_linear_ex", st)
     return out
 
 
@@ -309,16 +320,18 @@ class LinearBatch:
     scale, zero, N, Y) with Y a preallocated fp16 [M, N] CUDA tensor; the
     tensors are kept alive by the object."""
 
-    def __init__(self, weights, nbits: int, group_size: int):
+    def __init__(self, weights, nbits: int, group_size: int, dtype=torch.float16):
         self._lib = load_library()
         self._items = [tuple(w) for w in weights]
         self.nbits, self.group_size = nbits, group_size
+        self._code, _, ok = _compute_dtype(torch.empty(0, dtype=dtype))
+        self._ok = ok
         arr = (HqqLinearWeight * max(1, len(self._items)))()
         for i, (pk, sc, ze, N, Y) in enumerate(self._items):
             arr[i] = HqqLinearWeight(_dev_ptr(pk, "packed", _U32).value,
                                      _dev_ptr(sc, "scale", (torch.float32,)).value,
                                      _dev_ptr(ze, "zero", (torch.float32,)).value, N,
-                                     _dev_ptr(Y, "Y", _F16).value)
+                                     _dev_ptr(Y, "Y", ok).value)
         self._arr = arr
 
     def run(self, X: torch.Tensor):
@@ -326,8 +339,8 @@ class LinearBatch:
         for (_, _, _, N, Y) in self._items:
             if tuple(Y.shape) != (M, N):
                 raise ValueError(f"Y must be [{M}, {N}], got {tuple(Y.shape)}")
-        st = self._lib.hqq_linear_batch(_dev_ptr(X, "X", _F16), M, K, self._arr, len(self._items),
-                                        self.nbits, self.group_size, _stream(X.device))
+        st = self._lib.hqq_linear_batch(_dev_ptr(X, "X", self._ok), M, K, self._arr, len(self._items),
+                                        self.nbits, self.group_size, self._code, _stream(X.device))
         if st != 0:
             raise HQQError("hqq_linear_batch", st)
         return [it[4] for it in self._items]
@@ -335,11 +348,13 @@ class LinearBatch:
 
 def hqq_linear_batch(X: torch.Tensor, weights, nbits: int, group_size: int):
     """[X . W_hat_i^T] for weights [(packed, scale, zero, N), ...] sharing X,
-    in one C-ABI call.  Returns the fp16 outputs."""
+    in one C-ABI call, in X's compute dtype (fp16 or bfloat16).  Returns the
+    outputs."""
     M = X.shape[0]
-    items = [(pk, sc, ze, N, torch.empty((M, N), dtype=torch.float16, device=X.device))
+    _, tdt, _ = _compute_dtype(X)
+    items = [(pk, sc, ze, N, torch.empty((M, N), dtype=tdt, device=X.device))
              for (pk, sc, ze, N) in weights]
-    return LinearBatch(items, nbits, group_size).run(X)
+    return LinearBatch(items, nbits, group_size, dtype=tdt).run(X)
 
 
 def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging: torch.Tensor,

@@ -334,10 +334,12 @@ int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols, int nbits, in
 }
 
 int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws, int count,
-                     int nbits, int group_size, void *stream)
+                     int nbits, int group_size, int dtype, void *stream)
 {
     if (!hqq::valid_nbits(nbits) || nbits == 3)
         return HQQ_EINVAL_NBITS;
+    if (dtype != HQQ_DTYPE_FP16 && dtype != HQQ_DTYPE_BF16)
+        return HQQ_EINVAL_DTYPE;
     if (count < 0)
         return HQQ_EINVAL_SHAPE;
     if (count > 0 && !ws)
@@ -387,19 +389,26 @@ int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_w
             b.Y[j] = w.Y;
             b.N[j] = w.N;
         }
-        if (hqq::launch_linear(nbits, b, (hipStream_t)stream) != hipSuccess)
+        if (hqq::launch_linear(nbits, dtype == HQQ_DTYPE_BF16, b, (hipStream_t)stream) != hipSuccess)
             return HQQ_EHIP;
     }
     return HQQ_OK;
+}
+
+int hqq_linear_ex(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
+                  const float *scale, const float *zero, int64_t N, int nbits, int group_size,
+                  int dtype, uint16_t *Y, void *stream)
+{
+    // null or misaligned pointers are rejected by the batch's alignment check
+    const hqq_linear_weight w{packed, scale, zero, N, Y};
+    return hqq_linear_batch(X, M, K, &w, 1, nbits, group_size, dtype, stream);
 }
 
 int hqq_linear(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,
                const float *scale, const float *zero, int64_t N, int nbits, int group_size,
                uint16_t *Y, void *stream)
 {
-    // null or misaligned pointers are rejected by the batch's alignment check
-    const hqq_linear_weight w{packed, scale, zero, N, Y};
-    return hqq_linear_batch(X, M, K, &w, 1, nbits, group_size, stream);
+    return hqq_linear_ex(X, M, K, packed, scale, zero, N, nbits, group_size, HQQ_DTYPE_FP16, Y, stream);
 }
 
 int hqq_quantize_meta(const float *meta, int64_t n, int group_size, uint8_t *codes, float *mscale,

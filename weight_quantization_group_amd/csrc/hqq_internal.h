@@ -69,11 +69,11 @@ struct CodecArgs {
 // Arguments of the fused dequantize + matmul kernels: Y[M, N] = X[M, K] .
 // W_hat[N, K]^T with W in the axis = 1 packed layout.
 struct LinearArgs {
-    const uint16_t *X;       // fp16 bits [M, K]
+    const uint16_t *X;       // fp16 (or bf16) bits [M, K]
     const uint32_t *packed;  // [N, wpr] words
     const float *scale;      // [N, gpl]
     const float *zero;       // [N, gpl]
-    uint16_t *Y;             // fp16 bits [M, N]
+    uint16_t *Y;             // fp16 (or bf16) bits [M, N]
     int64_t M, N, K;
     int64_t wpr;             // words per row of W: K * nbits / 32
     int64_t gpl;             // groups per row of W: K / gs
@@ -103,7 +103,7 @@ hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, const So
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
-hipError_t launch_linear(int nbits, LinearBatch &b, hipStream_t s);
+hipError_t launch_linear(int nbits, bool bf16, LinearBatch &b, hipStream_t s);
 // meta arrays per launch of the meta kernels (descriptors by value)
 constexpr int kMetaBatch = 64;
 

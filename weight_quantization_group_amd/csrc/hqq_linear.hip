@@ -77,25 +77,59 @@ __device__ __forceinline__ uint32_t f16x2(float lo, float hi)
     return u;
 }
 
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// two fp32 -> packed pair of the compute dtype (fp16, or BF: bf16), round to
+// nearest even (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32)
+template <bool BF>
+__device__ __forceinline__ uint32_t out2(float lo, float hi)
+{
+    if constexpr (BF) {
+        const bf2v h = __builtin_convertvector(float2v{lo, hi}, bf2v);
+        uint32_t u;
+        __builtin_memcpy(&u, &h, 4);
+        return u;
+    } else {
+        return f16x2(lo, hi);
+    }
+}
+
+// one fp32 -> 16-bit value of the compute dtype, round to nearest even
+template <bool BF>
+__device__ __forceinline__ uint16_t out1(float v)
+{
+    uint16_t u;
+    if constexpr (BF) {
+        const __bf16 h = (__bf16)v;
+        __builtin_memcpy(&u, &h, 2);
+    } else {
+        const _Float16 h = (_Float16)v;
+        __builtin_memcpy(&u, &h, 2);
+    }
+    return u;
+}
+
 // the exact dequantized value of code c (fp32, before the fp16 rounding)
 __device__ __forceinline__ float wq(float c, float z, double R)
 {
     return (float)((double)(c - z) * R);
 }
 
-// The 16 fp16 values of a 4-bit group as byte tables: L[q] holds the low
-// bytes of codes 4q .. 4q+3, H[q] the high bytes.
+// The 16 values (fp16, or BF: bf16) of a 4-bit group as byte tables: L[q]
+// holds the low bytes of codes 4q .. 4q+3, H[q] the high bytes.
 struct Tab4 {
     uint32_t L[4], H[4];
 };
 
+template <bool BF>
 __device__ __forceinline__ Tab4 make_tab4(float s, float z)
 {
     const double R = 1.0 / (double)s;
     uint32_t P[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        P[i] = f16x2(wq((float)(2 * i), z, R), wq((float)(2 * i + 1), z, R));
+        P[i] = out2<BF>(wq((float)(2 * i), z, R), wq((float)(2 * i + 1), z, R));
     Tab4 t;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -105,7 +139,7 @@ __device__ __forceinline__ Tab4 make_tab4(float s, float z)
     return t;
 }
 
-// 8 codes of a 4-bit word -> 8 fp16 in operand order (0,2,4,6,1,3,5,7)
+// 8 codes of a 4-bit word -> 8 16-bit values in operand order (0,2,4,6,1,3,5,7)
 __device__ __forceinline__ uint4 lookup4(const Tab4 &t, uint32_t w)
 {
     // byte q of se / so: low 3 bits of the even / odd code of byte q; the
@@ -233,7 +267,7 @@ __device__ __forceinline__ void load_x(XRuns<MT> &b, const LinearArgs &a, Chunk 
 }
 
 // B operand j (8-k run j of the chunk) by direct quotients, operand order
-template <int NB, int GPC>
+template <int NB, int GPC, bool BF>
 __device__ __forceinline__ uint4 dequant_run(const uint32_t *w, int j, const float *s,
                                              const float *z)
 {
@@ -247,7 +281,7 @@ __device__ __forceinline__ uint4 dequant_run(const uint32_t *w, int j, const flo
         const int bit = (8 * j + ord[i]) * NB;
         v[i] = wq((float)((w[bit / 32] >> (bit % 32)) & MASK), z[gi], R);
     }
-    return uint4{f16x2(v[0], v[1]), f16x2(v[2], v[3]), f16x2(v[4], v[5]), f16x2(v[6], v[7])};
+    return uint4{out2<BF>(v[0], v[1]), out2<BF>(v[2], v[3]), out2<BF>(v[4], v[5]), out2<BF>(v[6], v[7])};
 }
 
 __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m)
@@ -255,18 +289,27 @@ __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m)
     return uint4{v.x & m, v.y & m, v.z & m, v.w & m};
 }
 
+// one 16x16x32 MFMA of the compute dtype (fp16, or BF: bf16), fp32 accumulation
+template <bool BF>
 __device__ __forceinline__ float4v mfma(uint4 A, uint4 B, float4v c)
 {
-    half8 a, b;
-    __builtin_memcpy(&a, &A, 16);
-    __builtin_memcpy(&b, &B, 16);
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    if constexpr (BF) {
+        bf16x8 a, b;
+        __builtin_memcpy(&a, &A, 16);
+        __builtin_memcpy(&b, &B, 16);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    } else {
+        half8 a, b;
+        __builtin_memcpy(&a, &A, 16);
+        __builtin_memcpy(&b, &B, 16);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
 }
 
 // X staged in LDS: row m of the workgroup's X rows at xs + m * xrow (uint4
 // units), runs in operand order; the row pitch is K / 8 + 1 runs so that the
 // 16 rows of an operand fall in different banks.
-template <bool KT, int NB, int MT, int GPC, bool XL>
+template <bool KT, int NB, int MT, int GPC, bool XL, bool BF>
 __device__ __forceinline__ void compute_step(const StepBuf<NB, GPC> &b, const XRuns<XL ? 1 : MT> &xg,
                                              uint32_t km0, uint32_t km1, const uint4 *xs,
                                              const uint32_t (&xm)[MT], Chunk c,
@@ -274,14 +317,14 @@ __device__ __forceinline__ void compute_step(const StepBuf<NB, GPC> &b, const XR
 {
     uint4 B[8];
     if constexpr (NB == 4 && GPC == 1) {
-        const Tab4 t = make_tab4(b.s[0], b.z[0]);
+        const Tab4 t = make_tab4<BF>(b.s[0], b.z[0]);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             B[j] = lookup4(t, b.w[j]);
     } else if constexpr (NB == 4 && GPC == 2) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const Tab4 t = make_tab4(b.s[h], b.z[h]);
+            const Tab4 t = make_tab4<BF>(b.s[h], b.z[h]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 B[4 * h + j] = lookup4(t, b.w[4 * h + j]);
@@ -289,7 +332,7 @@ __device__ __forceinline__ void compute_step(const StepBuf<NB, GPC> &b, const XR
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            B[j] = dequant_run<NB, GPC>(b.w, j, b.s, b.z);
+            B[j] = dequant_run<NB, GPC, BF>(b.w, j, b.s, b.z);
     }
     // K % 256 != 0: a lane whose chunk (or its second half) lies past K adds
     // zeros; the operands are cleared with integer masks (a select would
@@ -311,7 +354,7 @@ __device__ __forceinline__ void compute_step(const StepBuf<NB, GPC> &b, const XR
                 A = run_order(xg.x[u][j]);
             if constexpr (KT)
                 A = and4(A, j < 4 ? km0 : km1);
-            acc[u] = mfma(A, B[j], acc[u]);
+            acc[u] = mfma<BF>(A, B[j], acc[u]);
         }
 }
 
@@ -324,7 +367,7 @@ constexpr int lin_waves_per_simd(int nb, int mt, int gpc, bool xl)
     return !xl ? (mt > 1 ? 3 : 4) : nb == 8 || mt > 1 || gpc == 8 ? 4 : 6;
 }
 
-template <bool KT, int NB, int MT, int GPC, bool XL, int WPB>
+template <bool KT, int NB, int MT, int GPC, bool XL, int WPB, bool BF>
 __global__ __launch_bounds__(WPB * 64)
 __attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void linear_skinny_kernel(LinearBatch lb)
 {
@@ -387,7 +430,7 @@ __attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void l
         const StepBuf<NB, GPC> cur = buf;
         if (i + 1 < my)
             load_step(buf, a, lane_chunk<KT>(kbase(i + 1), grp, K), nw, ng);
-        compute_step<KT, NB, MT, GPC, XL>(cur, xg, km0, km1, lds, xr, c, acc);
+        compute_step<KT, NB, MT, GPC, XL, BF>(cur, xg, km0, km1, lds, xr, c, acc);
     }
 
     // add the waves' partial sums: red[wave][u * 4 + r][lane]
@@ -409,10 +452,8 @@ __attribute__((amdgpu_waves_per_eu(lin_waves_per_simd(NB, MT, GPC, XL)))) void l
         const int u = v >> 2, r = v & 3;
         const int64_t m = m0 + 16 * u + 4 * (l >> 4) + r;
         const int64_t nn = (int64_t)bx * 16 + (l & 15);
-        if (m < a.M && nn < a.N) {
-            const _Float16 h = (_Float16)s;
-            __builtin_memcpy(&a.Y[m * a.N + nn], &h, 2);
-        }
+        if (m < a.M && nn < a.N)
+            a.Y[m * a.N + nn] = out1<BF>(s);
     }
 }
 
@@ -439,7 +480,7 @@ inline uint32_t fill_tiles(LinearBatch &b, int64_t cols_per_tile)
     return t;
 }
 
-template <int NB, int MT, int GPC, bool XL, int WPB>
+template <int NB, int MT, int GPC, bool XL, int WPB, bool BF>
 hipError_t launch_wpb(const LinearBatch &b, dim3 grid, hipStream_t s)
 {
     const LinearArgs &a = b.a;
@@ -450,43 +491,43 @@ hipError_t launch_wpb(const LinearBatch &b, dim3 grid, hipStream_t s)
         lds = x > lds ? x : lds;
     }
     if (a.K % kStepK != 0)
-        hipLaunchKernelGGL((linear_skinny_kernel<true, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
+        hipLaunchKernelGGL((linear_skinny_kernel<true, NB, MT, GPC, XL, WPB, BF>), grid, dim3(WPB * 64),
                            lds, s, b);
     else
-        hipLaunchKernelGGL((linear_skinny_kernel<false, NB, MT, GPC, XL, WPB>), grid, dim3(WPB * 64),
+        hipLaunchKernelGGL((linear_skinny_kernel<false, NB, MT, GPC, XL, WPB, BF>), grid, dim3(WPB * 64),
                            lds, s, b);
     return hipGetLastError();
 }
 
-template <int NB, int MT, int GPC, bool XL>
+template <int NB, int MT, int GPC, bool XL, bool BF>
 hipError_t launch_one(LinearBatch &b, hipStream_t s)
 {
     const LinearArgs &a = b.a;
     const dim3 grid(fill_tiles(b, 16), (unsigned)((a.M + 16 * MT - 1) / (16 * MT)));
     switch (lin_waves((int64_t)grid.x * grid.y, a.K)) {
-    case 4: return launch_wpb<NB, MT, GPC, XL, 4>(b, grid, s);
-    case 8: return launch_wpb<NB, MT, GPC, XL, 8>(b, grid, s);
-    default: return launch_wpb<NB, MT, GPC, XL, 16>(b, grid, s);
+    case 4: return launch_wpb<NB, MT, GPC, XL, 4, BF>(b, grid, s);
+    case 8: return launch_wpb<NB, MT, GPC, XL, 8, BF>(b, grid, s);
+    default: return launch_wpb<NB, MT, GPC, XL, 16, BF>(b, grid, s);
     }
 }
 
-template <int NB, int MT, int GPC>
+template <int NB, int MT, int GPC, bool BF>
 hipError_t launch_xl(LinearBatch &b, hipStream_t s)
 {
     const LinearArgs &a = b.a;
     const int64_t rows = a.M < 16 * MT ? a.M : 16 * MT;
     if (rows * (a.K / 8 + 1) * 16 <= kXldsMax)
-        return launch_one<NB, MT, GPC, true>(b, s);
-    return launch_one<NB, MT, GPC, false>(b, s);
+        return launch_one<NB, MT, GPC, true, BF>(b, s);
+    return launch_one<NB, MT, GPC, false, BF>(b, s);
 }
 
-template <int NB, int MT>
+template <int NB, int MT, bool BF>
 hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 {
     switch (groups_per_chunk(b.a.gs)) {
-    case 1: return launch_xl<NB, MT, 1>(b, s);
-    case 2: return launch_xl<NB, MT, 2>(b, s);
-    default: return launch_xl<NB, MT, 8>(b, s);
+    case 1: return launch_xl<NB, MT, 1, BF>(b, s);
+    case 2: return launch_xl<NB, MT, 2, BF>(b, s);
+    default: return launch_xl<NB, MT, 8, BF>(b, s);
     }
 }
 
@@ -552,11 +593,11 @@ struct TileW {
     float s[G1 ? 1 : 4], z[G1 ? 1 : 4];
 };
 
-template <int NB, bool G1>
+template <int NB, bool G1, bool BF>
 __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 (&out)[4])
 {
     if constexpr (NB == 4 && G1) {
-        const Tab4 t = make_tab4(b.s[0], b.z[0]);
+        const Tab4 t = make_tab4<BF>(b.s[0], b.z[0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             out[j] = lookup4n(t, b.w[j]);
@@ -572,13 +613,14 @@ __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 
                 const int bit = (8 * j + i) * NB;
                 v[i] = wq((float)((b.w[bit / 32] >> (bit % 32)) & MASK), b.z[g], R);
             }
-            out[j] = uint4{f16x2(v[0], v[1]), f16x2(v[2], v[3]), f16x2(v[4], v[5]), f16x2(v[6], v[7])};
+            out[j] = uint4{out2<BF>(v[0], v[1]), out2<BF>(v[2], v[3]), out2<BF>(v[4], v[5]),
+                           out2<BF>(v[6], v[7])};
         }
     }
 }
 
 
-template <int NB, bool G1>
+template <int NB, bool G1, bool BF>
 __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
 {
     uint32_t bx = blockIdx.x;
@@ -638,7 +680,7 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
     };
     auto store_w = [&](const TileW<NB, G1> &w, int b) {
         uint4 runs[4];
-        dequant_tile_runs<NB, G1>(w, runs);
+        dequant_tile_runs<NB, G1, BF>(w, runs);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             ws[b][wr * kWPitch + wr0 + j] = runs[j];
@@ -689,7 +731,7 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
             for (int u = 0; u < TM; ++u)
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
-                    acc[u][t] = mfma(A[ks][u], B[ks][t], acc[u][t]);
+                    acc[u][t] = mfma<BF>(A[ks][u], B[ks][t], acc[u][t]);
         load_w(clampk(st + 3), wn1);
         step_barrier();
     };
@@ -710,21 +752,19 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
             for (int r = 0; r < 4; ++r) {
                 const int64_t m = m0 + wm * (kTBM / 2) + 16 * u + 4 * (lane >> 4) + r;
                 const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
-                if (m < a.M && n < a.N) {
-                    const _Float16 h = (_Float16)acc[u][t][r];
-                    __builtin_memcpy(&a.Y[m * a.N + n], &h, 2);
-                }
+                if (m < a.M && n < a.N)
+                    a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
             }
 }
 
-template <int NB>
+template <int NB, bool BF>
 hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
     const dim3 grid(fill_tiles(b, kTBN), (unsigned)((b.a.M + kTBM - 1) / kTBM));
     if (b.a.gs >= 32)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF>), grid, dim3(256), 0, s, b);
     else
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, false>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
@@ -733,30 +773,36 @@ hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 // row blocks of the skinny kernel are faster (measured at N = 4096).
 constexpr int64_t kTiledMinRows = 384;
 
-template <int NB>
+template <int NB, bool BF>
 hipError_t launch_nb(LinearBatch &b, hipStream_t s)
 {
     if constexpr (NB >= 2) {
         if (b.a.M >= kTiledMinRows && b.a.K % kTK == 0)
-            return launch_tiled<NB>(b, s);
+            return launch_tiled<NB, BF>(b, s);
     }
     // skinny: M > 32 runs ceil(M / 32) row blocks of 32
     if (b.a.M <= 16)
-        return launch_gpc<NB, 1>(b, s);
-    return launch_gpc<NB, 2>(b, s);
+        return launch_gpc<NB, 1, BF>(b, s);
+    return launch_gpc<NB, 2, BF>(b, s);
+}
+
+template <bool BF>
+hipError_t launch_bits(int nbits, LinearBatch &b, hipStream_t s)
+{
+    switch (nbits) {
+    case 1: return launch_nb<1, BF>(b, s);
+    case 2: return launch_nb<2, BF>(b, s);
+    case 4: return launch_nb<4, BF>(b, s);
+    case 8: return launch_nb<8, BF>(b, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_linear(int nbits, LinearBatch &b, hipStream_t s)
+hipError_t launch_linear(int nbits, bool bf16, LinearBatch &b, hipStream_t s)
 {
-    switch (nbits) {
-    case 1: return launch_nb<1>(b, s);
-    case 2: return launch_nb<2>(b, s);
-    case 4: return launch_nb<4>(b, s);
-    case 8: return launch_nb<8>(b, s);
-    default: return hipErrorInvalidValue;
-    }
+    return bf16 ? launch_bits<true>(nbits, b, s) : launch_bits<false>(nbits, b, s);
 }
 
 }  // namespace hqq
