@@ -233,8 +233,9 @@ def bench_linear(args):
             scale = (qmax / (hi - lo)).float()
             zero = (-lo * scale).float()
             layers.append((N, K, packed, scale, zero))
-    X = {K: torch.randn((1, K), device=dev, generator=gen).half() for K in (4096, 11008)}
-    Y = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+    cdt = torch.bfloat16 if args.cdtype == "bf16" else torch.float16     # compute dtype
+    X = {K: torch.randn((1, K), device=dev, generator=gen).to(cdt) for K in (4096, 11008)}
+    Y = {N: torch.empty((1, N), dtype=cdt, device=dev) for N in (4096, 11008)}
     # per layer, the projections that read the same activations share one
     # hqq_linear_batch call: (q, k, v), (o), (gate, up), (down)
     nl = len(LLAMA7B_LINEARS)
@@ -244,8 +245,8 @@ def bench_linear(args):
         for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
             K = ly[idx[0]][1]
             items = [(ly[i][2], ly[i][3], ly[i][4], ly[i][0],
-                      torch.empty((1, ly[i][0]), dtype=torch.float16, device=dev)) for i in idx]
-            calls.append((K, hq.LinearBatch(items, nbits, gs)))
+                      torch.empty((1, ly[i][0]), dtype=cdt, device=dev)) for i in idx]
+            calls.append((K, hq.LinearBatch(items, nbits, gs, dtype=cdt)))
     torch.cuda.synchronize()
 
     def token():
@@ -307,17 +308,17 @@ def bench_linear(args):
         ms_per_layer, _ = timed(g, args.steps, args.warmup)
         del g
 
-    # the fp16 reference: the same 224 products with distinct fp16 weights
-    # (12.95 GB) through torch.matmul (hipBLASLt), with the same sharing of
-    # the inputs: q, k, v and gate, up as concatenated weights
+    # the dense reference: the same 224 products with distinct weights in the
+    # compute dtype (12.95 GB) through torch.matmul (hipBLASLt), with the same
+    # sharing of the inputs: q, k, v and gate, up as concatenated weights
     Wf = []
     for li in range(LLAMA7B_LAYERS):
         for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
             N = sum(LLAMA7B_LINEARS[i][0] for i in idx)
             K = LLAMA7B_LINEARS[idx[0]][1]
-            w = torch.empty((N, K), dtype=torch.float16, device=dev)
+            w = torch.empty((N, K), dtype=cdt, device=dev)
             w.normal_(0.0, 0.02, generator=gen)
-            Wf.append((K, w, torch.empty((1, N), dtype=torch.float16, device=dev),
+            Wf.append((K, w, torch.empty((1, N), dtype=cdt, device=dev),
                        [LLAMA7B_LINEARS[i][0] for i in idx]))
 
     def token_fp16():
@@ -331,7 +332,7 @@ def bench_linear(args):
                 torch.matmul(X[K], w[n0:n0 + N].t(), out=Yf[N])
                 n0 += N
 
-    Yf = {N: torch.empty((1, N), dtype=torch.float16, device=dev) for N in (4096, 11008)}
+    Yf = {N: torch.empty((1, N), dtype=cdt, device=dev) for N in (4096, 11008)}
     gf = Eager(token_fp16) if args.eager else graph_of(token_fp16)
     ms_fp16, _ = timed(gf, args.steps, args.warmup)
     del gf
@@ -346,7 +347,7 @@ def bench_linear(args):
                           for (N, K) in LLAMA7B_LINEARS) * LLAMA7B_LAYERS
     gbs = bytes_per_token / (ms_ev * 1e-3) / 1e9
     out = {
-        "metric": LINEAR_METRIC,
+        "metric": LINEAR_METRIC if args.cdtype == "f16" else LINEAR_METRIC + ", compute dtype bf16",
         "value": round(1e3 / ms_ev, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -356,7 +357,7 @@ def bench_linear(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.cdtype,
         "data": "synthetic",
         "config": {"workload": "llama7b_decode_b1_4b_g64", "linears": len(layers), "M": 1,
                    "weights": LLAMA7B_WEIGHTS, "nbits": nbits, "group_size": gs, "axis": 1},
@@ -366,10 +367,11 @@ def bench_linear(args):
                      "kernel": "linear_skinny_kernel (4-bit, g64)",
                      "bytes_per_step": int(bytes_per_token),
                      "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
-        "fp16_matmul": {"ms_per_step": round(ms_fp16, 4), "tokens_per_s": round(1e3 / ms_fp16, 3),
-                        "speedup": round(ms_fp16 / ms_ev, 3),
-                        "per_layer_calls_ms_per_step":
-                            round(ms_fp16_per_layer, 4) if ms_fp16_per_layer else None},
+        "dense_matmul": {"dtype": args.cdtype, "ms_per_step": round(ms_fp16, 4),
+                         "tokens_per_s": round(1e3 / ms_fp16, 3),
+                         "speedup": round(ms_fp16 / ms_ev, 3),
+                         "per_layer_calls_ms_per_step":
+                             round(ms_fp16_per_layer, 4) if ms_fp16_per_layer else None},
         "per_layer_calls": {"ms_per_step": round(ms_per_layer, 4),
                             "tokens_per_s": round(1e3 / ms_per_layer, 3)} if ms_per_layer else None,
         "wall_ms_per_step": round(ms_wall, 4),
@@ -541,6 +543,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--cdtype", choices=("f16", "bf16"), default="f16",
+                    help="linear: compute dtype of the activations and outputs")
     ap.add_argument("--no-per-layer", action="store_true",
                     help="linear: skip the one-call-per-product context timings (profiler runs)")
     ap.add_argument("--wdtype", choices=("f16", "bf16"), default="f16",
