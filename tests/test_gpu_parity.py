@@ -329,6 +329,54 @@ def test_70b_stack_sampled(hq, oracle_mod):
             print("70b", t["layer"], t["name"], st)
 
 
+def _bench_chunks(tensors, max_batch):
+    """The benchmark's launches: consecutive tensors of one format, up to
+    max_batch per hqq_quantize_batch call."""
+    chunks = []
+    for i, t in enumerate(tensors):
+        fmt = (t["nbits"], t["group_size"], t["axis"])
+        if chunks and chunks[-1][0] == fmt and len(chunks[-1][1]) < max_batch:
+            chunks[-1][1].append(i)
+        else:
+            chunks.append((fmt, [i]))
+    return chunks
+
+
+@pytest.mark.parametrize("wl,layers,nsample", [("llama7b_stack32_4b_g64", (0, 1, 2, 3), 6),
+                                               ("llama70b_stack80_mixed", (0, 1), 8)])
+def test_batched_launches_sampled(hq, oracle_mod, wl, layers, nsample):
+    """The benchmark's exact launch configuration (hqq_quantize_batch over
+    consecutive same-format tensors, the first 24 of the 7B stack in one
+    launch; the 70B layers' mixed formats in several), full-size tensors,
+    sampled rows of every tensor against the oracle."""
+    import torch
+
+    tensors = [t for t in synth.workload(wl) if t["layer"] in layers]
+    for fmt, idx in _bench_chunks(tensors, hq.MAX_BATCH):
+        items = []
+        for i in idx:
+            t = tensors[i]
+            W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device="cuda")
+            synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
+            ms = hq.meta_shape(t["rows"], t["cols"], fmt[1], fmt[2])
+            items.append((W, torch.empty(hq.packed_shape(t["rows"], t["cols"], fmt[0], fmt[2]),
+                                         dtype=torch.int32, device="cuda"),
+                          torch.empty(ms, dtype=torch.float32, device="cuda"),
+                          torch.empty(ms, dtype=torch.float32, device="cuda")))
+        hq.QuantizeBatch(items, *fmt).run()
+        torch.cuda.synchronize()
+        for i, (W, pk, sc, ze) in zip(idx, items):
+            t = tensors[i]
+            rng = np.random.RandomState(i * 17 + t["layer"])
+            rows = np.sort(rng.choice(t["rows"], nsample, replace=False))
+            it = torch.from_numpy(rows).cuda()
+            W16 = W.index_select(0, it).cpu().numpy().view(np.uint16)
+            check_parity(oracle_mod, W16, *fmt, _np_u32(pk.index_select(0, it)),
+                         sc.index_select(0, it).cpu().numpy(), ze.index_select(0, it).cpu().numpy(),
+                         tag=f"{wl} L{t['layer']} {t['name']} launch of {len(idx)}")
+        del items
+
+
 @pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])
 @pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1), (8, 128, 1)])
 def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters):
