@@ -106,6 +106,23 @@ __device__ __forceinline__ uint16_t narrow(float f)
         return float_to_half_bits(f);
 }
 
+// Two values that came from 16-bit weights, narrowed back into one word (lo
+// in the low half).  fp16: v_cvt_pkrtz_f16_f32, whose rounding toward zero
+// is exact on fp16 values (subnormals included: fp16 denormals are not
+// flushed), one instruction per pair.
+template <bool BF>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi)
+{
+    if constexpr (BF) {
+        return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    } else {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
+        uint32_t u;
+        __builtin_memcpy(&u, &h, 4);
+        return u;
+    }
+}
+
 // eight 16-bit values of a 16-byte vector, widened to fp32
 template <bool BF>
 __device__ __forceinline__ void widen8(u32x4 v, float *out)
@@ -525,8 +542,7 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
             uint32_t hw[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hw[i] = (uint32_t)narrow<BF>(w[8 * j + 2 * i]) |
-                        ((uint32_t)narrow<BF>(w[8 * j + 2 * i + 1]) << 16);
+                hw[i] = narrow2<BF>(w[8 * j + 2 * i], w[8 * j + 2 * i + 1]);
             wf.cw[mine * K::SEG + j] = u32x4{hw[0], hw[1], hw[2], hw[3]};
         }
         wf.cg[mine] = CompactGroup{g.s, r.z, g.mn, g.mx, g.amag, r.beta, r.it, 0, g.sw};
