@@ -3,27 +3,28 @@
 //
 // This is the consumer of the codes: the HQQLinear forward of the lnwmold.com
 // HQQ guide (section 3.2: the quantized layer is called like the Linear it
-// replaces and computes in compute_dtype, fp16 here; section 4.1: a backend
-// fuses the dequantization and the matrix product into one kernel and needs
-// axis = 1; section 4.2: axis = 1 4-bit layers with optimized kernels).  W is
+// replaces and computes in compute_dtype, fp16 or bf16 here; section 4.1: a
+// backend fuses the dequantization and the matrix product into one kernel and
+// needs axis = 1; section 4.2: axis = 1 4-bit layers with optimized kernels).  W is
 // the axis = 1 layout, so a packed word holds C = 32 / nbits consecutive k of
 // one output row n, and the group of gs consecutive k shares (scale, zero).
 //
-// Exact dequantization.  W_hat[n][k] is the fp16 rounding of the fp32 quotient
-// (q - zero) / scale, both steps round-to-nearest-even, as the dequantize
-// kernel computes it.  Here the quotient comes from one fp64 product instead
+// Exact dequantization.  W_hat[n][k] is the fp16 (or bf16) rounding of the
+// fp32 quotient (q - zero) / scale, both steps round-to-nearest-even, as the
+// dequantize kernel computes it.  Here the quotient comes from one fp64 product instead
 // of an fp32 division: with a = fl32(q - zero) and R = fl64(1 / scale),
 // fl32(a * R) equals fl32(a / scale).  The fp64 product is within 2^-52 of
 // a / scale (relative), while a quotient of two 24-bit significands is never
 // a rounding midpoint of fp32 and never closer to one than 2^-49 relative, so
-// both round to the same fp32 value.  Products of fp16 inputs are exact in
-// the fp32 accumulators, so the kernel differs from an exact dot product of
-// X with W_hat only by fp32 accumulation order and the final fp16 rounding.
+// both round to the same fp32 value.  Products of fp16 (or bf16) inputs are
+// exact in the fp32 accumulators, so the kernel differs from an exact dot
+// product of X with W_hat only by fp32 accumulation order and the final
+// rounding to the compute dtype.
 //
 // Code tables (4-bit codes, groups of 32 or more).  A group has only 16
 // distinct W_hat values, so a lane computes them once (16 exact quotients)
 // and keeps them as two 16-byte tables, the low and the high bytes, in 8
-// VGPRs.  A packed word then becomes 8 fp16 values with v_perm_b32 byte
+// VGPRs.  A packed word then becomes 8 16-bit values with v_perm_b32 byte
 // lookups (two 8-entry halves joined on bit 3 of each code with v_bfi_b32):
 // about 3 VALU operations per weight instead of about 10 for the quotient.
 // The lookups give the 8 k of a word in the order 0,2,4,6,1,3,5,7; the X run
@@ -58,7 +59,7 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// an 8-k run of fp16 X (natural order) in operand order 0,2,4,6,1,3,5,7
+// an 8-k run of X (16-bit values, natural order) in operand order 0,2,4,6,1,3,5,7
 __device__ __forceinline__ uint4 run_order(uint4 x)
 {
     return uint4{perm(x.y, x.x, 0x05040100u), perm(x.w, x.z, 0x05040100u),
@@ -110,7 +111,8 @@ __device__ __forceinline__ uint16_t out1(float v)
     return u;
 }
 
-// the exact dequantized value of code c (fp32, before the fp16 rounding)
+// the exact dequantized value of code c (fp32, before the rounding to the
+// compute dtype)
 __device__ __forceinline__ float wq(float c, float z, double R)
 {
     return (float)((double)(c - z) * R);
@@ -577,7 +579,7 @@ __device__ __forceinline__ void step_barrier()
     asm volatile("" ::: "memory");
 }
 
-// 8 codes of a 4-bit word -> 8 fp16 in natural k order
+// 8 codes of a 4-bit word -> 8 16-bit values in natural k order
 __device__ __forceinline__ uint4 lookup4n(const Tab4 &t, uint32_t w)
 {
     const uint4 q = lookup4(t, w);   // (c0,c2) (c4,c6) (c1,c3) (c5,c7)
