@@ -29,8 +29,9 @@
  * fp64 (the two first sums exact, sum W_e in ascending element order), then
  * rounded once to fp32.
  *
- * Layout.  W is fp16 (IEEE binary16 bits), row-major [rows, cols] with
- * rows = out_features and cols = in_features.
+ * Layout.  W is fp16 (IEEE binary16 bits; the _ex entry points also take
+ * bf16), row-major [rows, cols] with rows = out_features and
+ * cols = in_features.
  *   axis = 1: a group is group_size consecutive elements of one row
  *             (along in_features, contiguous); scale/zero are [rows, cols/gs].
  *   axis = 0: a group is group_size consecutive rows of one column
@@ -43,10 +44,13 @@
  * scale is codes per unit of weight: dequantization divides by it.
  *
  * Conventions for every entry point.
- *   - Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors), owned by
- *     the caller; the library allocates nothing and keeps no state, so calls
- *     are thread-safe.  Inputs are never written; outputs must not overlap
- *     inputs.  Every pointer must be 16-byte aligned.
+ *   - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *     owned by the caller; arrays of descriptors (the batched calls) and the
+ *     weights of hqq_quantize_streamed are host memory, as their entries
+ *     say.  The library allocates nothing and keeps no state, so calls are
+ *     thread-safe.  Inputs are never written; outputs must not overlap
+ *     inputs.  Tensor pointers must be 16-byte aligned unless the entry point
+ *     states a weaker requirement (the meta calls).
  *   - stream is a hipStream_t passed as void*; NULL is the null stream.  Calls
  *     only enqueue work: results are ready when the stream reaches them.
  *   - Arguments are validated on the host before any HIP call; on failure
