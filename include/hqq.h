@@ -308,7 +308,7 @@ typedef struct hqq_linear_weight {
 HQQ_API int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
                              int count, int nbits, int group_size, int dtype, void *stream);
 
-/* Number of uint32 words of the packed layout; a negative HQQ_E* status for/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
+/* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */
 HQQ_API int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);
 

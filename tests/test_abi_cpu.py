@@ -36,6 +36,23 @@ def test_header_codes_match():
         assert m and int(m.group(1)) == val, key
 
 
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles_cleanly(lang, compiler, tmp_path):
+    """The public header is plain C and C++: it compiles on its own with every
+    warning turned into an error (a stray comment opener or a missing type
+    fails here)."""
+    import shutil
+    import subprocess
+
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not installed")
+    src = tmp_path / ("use." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "hqq.h"\nint main(void) { return hqq_packed_words(1, 8, 4, 1) < 0; }\n')
+    r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
