@@ -116,6 +116,8 @@ CASES = [
     (400, 300, 256, 4, 64),
     (513, 130, 128, 2, 32),
     (640, 256, 320, 8, 64),
+    (448, 96, 384, 4, 32),      # tiled, 4-bit: two groups per 64-k step
+    (390, 140, 512, 4, 128),    # tiled, 4-bit: a group spans two steps
 ]
 
 
@@ -294,7 +296,8 @@ def check_bf16(Yb, Yref, A, K, tag=""):
     assert worst <= 1.0, f"{tag}: worst error / bound = {worst:.3g}"
 
 
-BF16_CASES = [c for i, c in enumerate(CASES) if i % 3 == 0] + [(400, 300, 256, 4, 64), (640, 256, 320, 8, 64)]
+BF16_CASES = list(dict.fromkeys([c for i, c in enumerate(CASES) if i % 3 == 0]
+                                + [(400, 300, 256, 4, 64), (640, 256, 320, 8, 64), (390, 140, 512, 4, 128)]))
 
 
 @pytest.mark.parametrize("M,N,K,nbits,gs", BF16_CASES)

@@ -141,6 +141,33 @@ __device__ __forceinline__ Tab4 make_tab4(float s, float z)
     return t;
 }
 
+// make_tab4 shared by two adjacent lanes that hold the same group: each lane
+// evaluates 8 of the 16 values (the even lane codes 0-7, the odd lane codes
+// 8-15) and takes the other 8 from its neighbour by a DPP quad permutation
+// [1, 0, 3, 2].  The values are those of make_tab4, bit for bit.  Both lanes
+// must be active.
+template <bool BF>
+__device__ __forceinline__ Tab4 make_tab4_pair(float s, float z, bool odd)
+{
+    const double R = 1.0 / (double)s;
+    const float c0 = odd ? 8.0f : 0.0f;
+    uint32_t P[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t mine = out2<BF>(wq(c0 + (float)(2 * j), z, R), wq(c0 + (float)(2 * j + 1), z, R));
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)mine, 0xB1, 0xF, 0xF, false);
+        P[j] = odd ? other : mine;
+        P[4 + j] = odd ? mine : other;
+    }
+    Tab4 t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        t.L[q] = perm(P[2 * q + 1], P[2 * q], 0x06040200u);
+        t.H[q] = perm(P[2 * q + 1], P[2 * q], 0x07050301u);
+    }
+    return t;
+}
+
 // 8 codes of a 4-bit word -> 8 16-bit values in operand order (0,2,4,6,1,3,5,7)
 __device__ __forceinline__ uint4 lookup4(const Tab4 &t, uint32_t w)
 {
@@ -541,8 +568,9 @@ hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 //     registers), runs of 8 k XOR-swizzled by row so the MFMA reads of 16
 //     rows spread over the banks;
 //   * W's 128 x 64 tile is dequantized once by the workgroup (two threads
-//     per row, 32 k each; 4-bit codes through the group's code table) into
-//     LDS in natural k order;
+//     per row, 32 k each; 4-bit codes through the group's code table, whose
+//     16 values the two threads split when they share the group) into LDS
+//     in natural k order;
 //   * the waves run their 64 MFMAs from LDS.
 // X goes through a ring of three LDS buffers, W through two, with one
 // barrier per step.  Within step s a wave first reads all of its MFMA
@@ -595,11 +623,14 @@ struct TileW {
     float s[G1 ? 1 : 4], z[G1 ? 1 : 4];
 };
 
-template <int NB, bool G1, bool BF>
+// PR: the two threads of a row hold the same group (gs >= 64) and share the
+// code table
+template <int NB, bool G1, bool BF, bool PR>
 __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 (&out)[4])
 {
     if constexpr (NB == 4 && G1) {
-        const Tab4 t = make_tab4<BF>(b.s[0], b.z[0]);
+        const Tab4 t = PR ? make_tab4_pair<BF>(b.s[0], b.z[0], (threadIdx.x & 1) != 0)
+                          : make_tab4<BF>(b.s[0], b.z[0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             out[j] = lookup4n(t, b.w[j]);
@@ -622,7 +653,7 @@ __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 
 }
 
 
-template <int NB, bool G1, bool BF>
+template <int NB, bool G1, bool BF, bool PR>
 __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
 {
     uint32_t bx = blockIdx.x;
@@ -682,7 +713,7 @@ __global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
     };
     auto store_w = [&](const TileW<NB, G1> &w, int b) {
         uint4 runs[4];
-        dequant_tile_runs<NB, G1, BF>(w, runs);
+        dequant_tile_runs<NB, G1, BF, PR>(w, runs);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             ws[b][wr * kWPitch + wr0 + j] = runs[j];
@@ -763,10 +794,12 @@ template <int NB, bool BF>
 hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
     const dim3 grid(fill_tiles(b, kTBN), (unsigned)((b.a.M + kTBM - 1) / kTBM));
-    if (b.a.gs >= 32)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF>), grid, dim3(256), 0, s, b);
+    if (NB == 4 && b.a.gs >= 64)
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4>), grid, dim3(256), 0, s, b);
+    else if (b.a.gs >= 32)
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, false>), grid, dim3(256), 0, s, b);
     else
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF, false>), grid, dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
