@@ -562,47 +562,37 @@ hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (many rows of X: prefill).  A workgroup computes a 256 x 128
-// tile of Y with four waves (2 x 2, each 128 x 64 as 8 x 4 MFMA 16x16x32
-// tiles).  Per 64-wide step of K:
-//   * X's 256 x 64 tile is copied global -> LDS by DMA (global_load_lds, no
-//     registers), runs of 8 k XOR-swizzled by row so the MFMA reads of 16
-//     rows spread over the banks;
-//   * W's 128 x 64 tile is dequantized once by the workgroup (two threads
-//     per row, 32 k each; 4-bit codes through the group's code table, whose
-//     16 values the two threads split when they share the group) into LDS
-//     in natural k order;
-//   * the waves run their 64 MFMAs from LDS.
-// X goes through a ring of three LDS buffers, W through two, with one
-// barrier per step.  Within step s a wave first reads all of its MFMA
-// operands into registers, then dequantizes W for step s + 1 into the other
-// W buffer (its codes were loaded two steps earlier), then starts the DMA of
-// X for step s + 2, then runs its MFMAs and loads the codes of step s + 3.
-// Nothing touches LDS between the DMA and the barrier, so the wait the
-// compiler places for the DMA before the next LDS read comes after a full
-// step of matrix work.  The dequantization is shared by the 256 rows of X.
+// tile of Y with eight waves in two roles, one of each on every SIMD:
+//   * waves 0-3 (MFMA waves, 2 x 2, each 128 x 64 outputs as 8 x 4 MFMA
+//     16x16x32 tiles) copy X's 256 x 64 tile of a 64-wide k step global ->
+//     LDS by DMA (global_load_lds, no registers; runs of 8 k XOR-swizzled
+//     by row so the MFMA reads of 16 rows spread over the banks) and run the
+//     step's 64 MFMAs per wave from LDS;
+//   * waves 4-7 (dequantization waves) turn W's 128 x 64 tile of the next
+//     step into 16-bit values in LDS, in natural k order (two threads per
+//     row, 32 k each; 4-bit codes through the group's code table, whose 16
+//     values the two threads split when they share the group).
+// The VALU work of the dequantization issues beside the other role's MFMAs
+// on the same SIMD.  X goes through a ring of three LDS buffers (its DMA two
+// steps ahead), W through two, with one barrier per step.  An MFMA wave
+// reads all of a step's operands into registers before it issues the next
+// DMA, so the wait the compiler places for the DMA before the next LDS read
+// comes after a full step of matrix work.  The dequantization is shared by
+// the 256 rows of X.
 
 constexpr int kTK = 64;              // k per step
 constexpr int kTBM = 256, kTBN = 128;
 constexpr int kWPitch = kTK / 8 + 1; // W tile row pitch in 8-k runs (uint4)
 
-// End of a k step.  A plain __syncthreads() is a workgroup release fence,
-// which waits for every vector memory operation of the wave (vmcnt(0)): the
-// code loads and X DMA just issued for later steps, a full memory latency
-// per step.  What the next step needs is narrower: this wave's W stores in
-// LDS (lgkmcnt(0)) and its DMA of the X tile the next step reads, issued one
-// step earlier.  In program order that DMA is followed by this step's X DMA
-// (kDmaOps operations) and code and meta loads (at least 3), so waiting
-// until at most kStepVm operations are outstanding is enough.  The empty
-// asm statements keep the compiler from moving memory accesses across.
-constexpr int kDmaOps = 8;                 // global_load_lds per thread per X tile
-constexpr int kStepVm = kDmaOps + 3;
-static_assert(kTBM * kTK * 2 / 16 / 256 == kDmaOps, "X tile DMA operations per thread");
-constexpr int kWaitStep = (kStepVm & 15) | ((kStepVm >> 4) << 14) | (7 << 4);   // vmcnt(11) lgkmcnt(0)
-
-__device__ __forceinline__ void step_barrier()
+// End of a k step: this wave's LDS writes are complete (lgkmcnt(0)), then
+// the workgroup barrier.  A plain __syncthreads() would also wait for every
+// vector memory operation of the wave (it is a release fence: vmcnt(0)),
+// including the loads just issued for later steps.  The empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier()
 {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kWaitStep);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -654,140 +644,146 @@ __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 
 
 
 template <int NB, bool G1, bool BF, bool PR>
-__global__ __launch_bounds__(256, 1) void linear_tiled_kernel(LinearBatch lb)
+__global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
 {
     uint32_t bx = blockIdx.x;
     const LinearArgs a = batch_item(lb, bx);
-    constexpr int TM = kTBM / 32, TN = kTBN / 32;   // MFMA tiles per wave (8 x 4)
+    constexpr int TM = kTBM / 32, TN = kTBN / 32;   // MFMA tiles per MFMA wave (8 x 4)
     typedef __attribute__((address_space(3))) void *lds_ptr;
     __shared__ uint4 xs[3][kTBM * 8];
     __shared__ uint4 ws[2][kTBN * kWPitch];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * kTBM, n0 = (int64_t)bx * kTBN;
     const uint32_t K = (uint32_t)a.K;
     const uint32_t steps = K / kTK;
-
-    // X DMA: wave w moves rows 64 w .. 64 w + 63, 8 rows (64 runs) per
-    // instruction; lane l fills slot (row 8 i + l / 8, column l % 8), which
-    // holds run (l % 8) ^ (row % 8) of that row
-    uint32_t xsrc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 64 * wave + 8 * i + (lane >> 3);
-        const int64_t m = m0 + r < a.M ? m0 + r : a.M - 1;
-        xsrc[i] = (uint32_t)(m * a.K) + 8 * ((lane & 7) ^ (r & 7));      // halves
-    }
-    auto dma_x = [&](uint32_t k0, int b) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_global_load_lds(a.X + xsrc[i] + k0, (lds_ptr)&xs[b][(64 * wave + 8 * i) * 8], 16,
-                                             0, 0);
-    };
-
-    // W: thread t dequantizes row t / 2, runs 4 (t % 2) .. + 3
-    const int wr = tid >> 1, wr0 = (tid & 1) * 4;
-    const int64_t wn_ = n0 + wr < a.N ? n0 + wr : a.N - 1;
-    const uint32_t wbase = (uint32_t)(wn_ * a.wpr) + (8 * wr0 * NB) / 32;
-    const uint32_t gbase = (uint32_t)(wn_ * a.gpl);
-    auto load_w = [&](uint32_t k0, TileW<NB, G1> &w) {
-        const uint32_t wo = 4 * (wbase + (k0 * NB) / 32);
-        if constexpr (NB == 8) {
-            const uint4 u = *at<uint4>(a.packed, wo), v = *at<uint4>(a.packed, wo + 16);
-            w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
-            w.w[4] = v.x; w.w[5] = v.y; w.w[6] = v.z; w.w[7] = v.w;
-        } else if constexpr (NB == 4) {
-            const uint4 u = *at<uint4>(a.packed, wo);
-            w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
-        } else {
-            const uint2 u = *at<uint2>(a.packed, wo);
-            w.w[0] = u.x; w.w[1] = u.y;
-        }
-#pragma unroll
-        for (int j = 0; j < (G1 ? 1 : 4); ++j) {
-            const uint32_t g = 4 * (gbase + ((k0 + 8 * (wr0 + j)) >> a.gshift));
-            w.s[j] = *at<float>(a.scale, g);
-            w.z[j] = *at<float>(a.zero, g);
-        }
-    };
-    auto store_w = [&](const TileW<NB, G1> &w, int b) {
-        uint4 runs[4];
-        dequant_tile_runs<NB, G1, BF, PR>(w, runs);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ws[b][wr * kWPitch + wr0 + j] = runs[j];
-    };
-
-    float4v acc[TM][TN];
-#pragma unroll
-    for (int u = 0; u < TM; ++u)
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-            acc[u][t] = float4v{0.f, 0.f, 0.f, 0.f};
-
-    // Past the last step the loads repeat it (in bounds, never used).
-    // Prologue: X(0) and X(1) by DMA, W(0) in LDS, the codes of W(1) and
-    // W(2) in registers.
+    // past the last step the loads repeat it (in bounds, never used)
     auto clampk = [&](uint32_t s_) { return (s_ < steps ? s_ : steps - 1) * kTK; };
-    TileW<NB, G1> wb0, wb1;
-    load_w(0, wb0);
-    store_w(wb0, 0);
-    load_w(clampk(1), wb1);
-    load_w(clampk(2), wb0);
-    dma_x(0, 0);
-    dma_x(clampk(1), 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): X(0) has landed
-    __syncthreads();
 
-    // step st: X in buffer st % 3, W in buffer st & 1; wn1 holds the codes
-    // of step st + 1
-    auto step = [&](uint32_t st, TileW<NB, G1> &wn1) {
-        const int bx = (int)(st % 3), bw = (int)(st & 1);
-        uint4 A[2][TM], B[2][TN];
+    if (wave < 4) {
+        // MFMA wave: step st reads X from buffer st % 3 and W from st & 1
+        const int wm = wave >> 1, wn = wave & 1;
+        // X DMA: wave w moves rows 64 w .. 64 w + 63, 8 rows (64 runs) per
+        // instruction; lane l fills slot (row 8 i + l / 8, column l % 8),
+        // which holds run (l % 8) ^ (row % 8) of that row
+        uint32_t xsrc[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int i = 0; i < 8; ++i) {
+            const int r = 64 * wave + 8 * i + (lane >> 3);
+            const int64_t m = m0 + r < a.M ? m0 + r : a.M - 1;
+            xsrc[i] = (uint32_t)(m * a.K) + 8 * ((lane & 7) ^ (r & 7));      // halves
+        }
+        auto dma_x = [&](uint32_t k0, int b) {
 #pragma unroll
-            for (int u = 0; u < TM; ++u) {
-                const int r = wm * (kTBM / 2) + 16 * u + (lane & 15);
-                A[ks][u] = xs[bx][r * 8 + ((4 * ks + (lane >> 4)) ^ (r & 7))];
-            }
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_global_load_lds(a.X + xsrc[i] + k0, (lds_ptr)&xs[b][(64 * wave + 8 * i) * 8],
+                                                 16, 0, 0);
+        };
+        float4v acc[TM][TN];
+#pragma unroll
+        for (int u = 0; u < TM; ++u)
 #pragma unroll
             for (int t = 0; t < TN; ++t)
-                B[ks][t] = ws[bw][(wn * (kTBN / 2) + 16 * t + (lane & 15)) * kWPitch + 4 * ks + (lane >> 4)];
-        }
-        store_w(wn1, bw ^ 1);
-        dma_x(clampk(st + 2), (int)((st + 2) % 3));
+                acc[u][t] = float4v{0.f, 0.f, 0.f, 0.f};
+        dma_x(0, 0);
+        dma_x(clampk(1), 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): X(0) has landed
+        lds_barrier();                        // and W(0) is in LDS
+        for (uint32_t st = 0; st < steps; ++st) {
+            const int bx_ = (int)(st % 3), bw = (int)(st & 1);
+            uint4 A[2][TM], B[2][TN];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int u = 0; u < TM; ++u)
+                for (int u = 0; u < TM; ++u) {
+                    const int r = wm * (kTBM / 2) + 16 * u + (lane & 15);
+                    A[ks][u] = xs[bx_][r * 8 + ((4 * ks + (lane >> 4)) ^ (r & 7))];
+                }
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
-                    acc[u][t] = mfma<BF>(A[ks][u], B[ks][t], acc[u][t]);
-        load_w(clampk(st + 3), wn1);
-        step_barrier();
-    };
-    // two steps per trip, so that the register buffers are named statically
-    for (uint32_t st = 0; st < steps; st += 2) {
-        step(st, wb1);
-        if (st + 1 < steps)
-            step(st + 1, wb0);
-    }
-
-    // accumulator r of lane l in tile (u, t) is Y[m][n] with
-    // m = 4 (l / 16) + r + 16 u, n = l % 16 + 16 t in the wave's quadrant
-#pragma unroll
-    for (int u = 0; u < TM; ++u)
-#pragma unroll
-        for (int t = 0; t < TN; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * (kTBM / 2) + 16 * u + 4 * (lane >> 4) + r;
-                const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
-                if (m < a.M && n < a.N)
-                    a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
+                    B[ks][t] = ws[bw][(wn * (kTBN / 2) + 16 * t + (lane & 15)) * kWPitch + 4 * ks + (lane >> 4)];
             }
+            dma_x(clampk(st + 2), (int)((st + 2) % 3));
+            // all of the step's LDS reads are issued before the DMA
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int u = 0; u < TM; ++u)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        acc[u][t] = mfma<BF>(A[ks][u], B[ks][t], acc[u][t]);
+            lds_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outlives the block
+
+        // accumulator r of lane l in tile (u, t) is Y[m][n] with
+        // m = 4 (l / 16) + r + 16 u, n = l % 16 + 16 t in the wave's quadrant
+#pragma unroll
+        for (int u = 0; u < TM; ++u)
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + wm * (kTBM / 2) + 16 * u + 4 * (lane >> 4) + r;
+                    const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
+                    if (m < a.M && n < a.N)
+                        a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
+                }
+    } else {
+        // dequantization wave: thread p = tid - 256 dequantizes row p / 2,
+        // runs 4 (p % 2) .. + 3; in step st it writes W(st + 1) and loads
+        // the codes of step st + 3
+        const int pt = tid - 256;
+        const int wr = pt >> 1, wr0 = (pt & 1) * 4;
+        const int64_t wn_ = n0 + wr < a.N ? n0 + wr : a.N - 1;
+        const uint32_t wbase = (uint32_t)(wn_ * a.wpr) + (8 * wr0 * NB) / 32;
+        const uint32_t gbase = (uint32_t)(wn_ * a.gpl);
+        auto load_w = [&](uint32_t k0, TileW<NB, G1> &w) {
+            const uint32_t wo = 4 * (wbase + (k0 * NB) / 32);
+            if constexpr (NB == 8) {
+                const uint4 u = *at<uint4>(a.packed, wo), v = *at<uint4>(a.packed, wo + 16);
+                w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
+                w.w[4] = v.x; w.w[5] = v.y; w.w[6] = v.z; w.w[7] = v.w;
+            } else if constexpr (NB == 4) {
+                const uint4 u = *at<uint4>(a.packed, wo);
+                w.w[0] = u.x; w.w[1] = u.y; w.w[2] = u.z; w.w[3] = u.w;
+            } else {
+                const uint2 u = *at<uint2>(a.packed, wo);
+                w.w[0] = u.x; w.w[1] = u.y;
+            }
+#pragma unroll
+            for (int j = 0; j < (G1 ? 1 : 4); ++j) {
+                const uint32_t g = 4 * (gbase + ((k0 + 8 * (wr0 + j)) >> a.gshift));
+                w.s[j] = *at<float>(a.scale, g);
+                w.z[j] = *at<float>(a.zero, g);
+            }
+        };
+        auto store_w = [&](const TileW<NB, G1> &w, int b) {
+            uint4 runs[4];
+            dequant_tile_runs<NB, G1, BF, PR>(w, runs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ws[b][wr * kWPitch + wr0 + j] = runs[j];
+        };
+        TileW<NB, G1> wb0, wb1;
+        load_w(0, wb0);
+        store_w(wb0, 0);
+        load_w(clampk(1), wb1);
+        load_w(clampk(2), wb0);
+        lds_barrier();
+        auto step = [&](uint32_t st, TileW<NB, G1> &wn1) {
+            store_w(wn1, (int)(st & 1) ^ 1);
+            load_w(clampk(st + 3), wn1);
+            lds_barrier();
+        };
+        // two steps per trip, so that the register buffers are named statically
+        for (uint32_t st = 0; st < steps; st += 2) {
+            step(st, wb1);
+            if (st + 1 < steps)
+                step(st + 1, wb0);
+        }
+    }
 }
 
 template <int NB, bool BF>
@@ -795,11 +791,11 @@ hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
     const dim3 grid(fill_tiles(b, kTBN), (unsigned)((b.a.M + kTBM - 1) / kTBM));
     if (NB == 4 && b.a.gs >= 64)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4>), grid, dim3(512), 0, s, b);
     else if (b.a.gs >= 32)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, false>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, false>), grid, dim3(512), 0, s, b);
     else
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF, false>), grid, dim3(256), 0, s, b);
+        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF, false>), grid, dim3(512), 0, s, b);
     return hipGetLastError();
 }
 
