@@ -190,10 +190,13 @@ def test_matches_gpu_dequantize_then_matmul_operand(hq, oracle_mod):
     assert_same_weights(Y.view(np.uint16), W[:, sel].T)
 
 
-# the 7B decoder's linear shapes at one token (decode): q/k/v/o, gate/up, down
+# the 7B decoder's linear shapes at one token (decode): q/k/v/o, gate/up, down;
+# and batches of rows: M = 96 and 200 take the tiled kernel by its time
+# estimate (one partly filled 256-row tile), M = 64 at N = 4096 the row blocks
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008),
                                    (8, 11008, 4096), (32, 4096, 4096), (512, 4096, 4096),
-                                   (256, 11008, 4096)])
+                                   (256, 11008, 4096), (96, 11008, 4096), (200, 4096, 4096),
+                                   (64, 4096, 4096)])
 def test_linear_full_size(hq, oracle_mod, M, N, K):
     rng = np.random.RandomState(M + N // 7 + K // 5)
     nbits, gs = 4, 64

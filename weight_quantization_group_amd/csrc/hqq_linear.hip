@@ -799,16 +799,40 @@ hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
     return hipGetLastError();
 }
 
-// rows of X from which the tiled kernel is used (K a multiple of 64; 2-, 4-
-// and 8-bit codes).  Below it the 256-row tiles leave most CUs idle and the
-// row blocks of the skinny kernel are faster (measured at N = 4096).
+// Kernel choice for M > 32 (K a multiple of 64; 2-, 4- and 8-bit codes).
+// The row-block kernel re-derives W for every 32 rows of X, so its time
+// grows with ceil(M / 32) * N * K; the tiled kernel's time is its number of
+// rounds of tiles over the 256 CUs times K / 64 steps.  Both estimates use
+// the times measured for 4-bit g64 codes at K = 4096 on MI355X: 9.1 us per
+// 32-row block at N = 4096, 0.92 us per tiled step.  The tiled kernel is
+// taken when its estimate is the smaller one; from 384 rows it always is at
+// the shapes measured, and from there it is taken whatever the shape.
 constexpr int64_t kTiledMinRows = 384;
+
+inline bool use_tiled(const LinearBatch &b)
+{
+    const LinearArgs &a = b.a;
+    if (a.M <= 32 || a.K % kTK != 0)
+        return false;
+    if (a.M >= kTiledMinRows)
+        return true;
+    int64_t n = 0, ntiles = 0;
+    for (int j = 0; j < b.count; ++j) {
+        n += b.N[j];
+        ntiles += (b.N[j] + kTBN - 1) / kTBN;
+    }
+    const double row_blocks = (double)((a.M + 31) / 32);
+    const double skinny_us = row_blocks * 9.1 * ((double)n * (double)a.K) / (4096.0 * 4096.0);
+    const int64_t tiles = ntiles * ((a.M + kTBM - 1) / kTBM);
+    const double tiled_us = (double)((tiles + 255) / 256) * (double)(a.K / kTK) * 0.92;
+    return tiled_us < skinny_us;
+}
 
 template <int NB, bool BF>
 hipError_t launch_nb(LinearBatch &b, hipStream_t s)
 {
     if constexpr (NB >= 2) {
-        if (b.a.M >= kTiledMinRows && b.a.K % kTK == 0)
+        if (use_tiled(b))
             return launch_tiled<NB, BF>(b, s);
     }
     // skinny: M > 32 runs ceil(M / 32) row blocks of 32
