@@ -155,6 +155,8 @@ def _cpu_job(job):
 
 
 LINEAR_METRIC = "tokens/s, 7B decode (batch 1) through all 224 HQQ 4b g64 linear layers"
+PREFILL_METRIC = "tokens/s, 7B prefill ({m} rows per step) through all 224 HQQ 4b g64 linear layers"
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 / bf16 MFMA
 # HBM traffic of the linear kernel per step, from the committed rocprofv3
 # summary; used only while the kernel's sources are the ones it was taken with
 LINEAR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_4b_g64_llama7b_decode.traffic.json")
@@ -234,18 +236,22 @@ def bench_linear(args):
             zero = (-lo * scale).float()
             layers.append((N, K, packed, scale, zero))
     cdt = torch.bfloat16 if args.cdtype == "bf16" else torch.float16     # compute dtype
-    X = {K: torch.randn((1, K), device=dev, generator=gen).to(cdt) for K in (4096, 11008)}
-    Y = {N: torch.empty((1, N), dtype=cdt, device=dev) for N in (4096, 11008)}
+    M = args.rows                                                          # rows of X per step
+    if M < 1:
+        raise SystemExit("--rows must be at least 1")
+    X = {K: torch.randn((M, K), device=dev, generator=gen).to(cdt) for K in (4096, 11008)}
+    Y = {N: torch.empty((M, N), dtype=cdt, device=dev) for N in (4096, 11008)}
     # per layer, the projections that read the same activations share one
     # hqq_linear_batch call: (q, k, v), (o), (gate, up), (down)
+    # (the outputs of one projection are shared by the 32 layers)
     nl = len(LLAMA7B_LINEARS)
+    outs = [torch.empty((M, N), dtype=cdt, device=dev) for (N, K) in LLAMA7B_LINEARS]
     calls = []
     for li in range(LLAMA7B_LAYERS):
         ly = layers[li * nl:(li + 1) * nl]
         for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
             K = ly[idx[0]][1]
-            items = [(ly[i][2], ly[i][3], ly[i][4], ly[i][0],
-                      torch.empty((1, ly[i][0]), dtype=cdt, device=dev)) for i in idx]
+            items = [(ly[i][2], ly[i][3], ly[i][4], ly[i][0], outs[i]) for i in idx]
             calls.append((K, hq.LinearBatch(items, nbits, gs, dtype=cdt)))
     torch.cuda.synchronize()
 
@@ -318,7 +324,7 @@ def bench_linear(args):
             K = LLAMA7B_LINEARS[idx[0]][1]
             w = torch.empty((N, K), dtype=cdt, device=dev)
             w.normal_(0.0, 0.02, generator=gen)
-            Wf.append((K, w, torch.empty((1, N), dtype=cdt, device=dev),
+            Wf.append((K, w, torch.empty((M, N), dtype=cdt, device=dev),
                        [LLAMA7B_LINEARS[i][0] for i in idx]))
 
     def token_fp16():
@@ -332,7 +338,7 @@ def bench_linear(args):
                 torch.matmul(X[K], w[n0:n0 + N].t(), out=Yf[N])
                 n0 += N
 
-    Yf = {N: torch.empty((1, N), dtype=cdt, device=dev) for N in (4096, 11008)}
+    Yf = {N: torch.empty((M, N), dtype=cdt, device=dev) for N in (4096, 11008)}
     gf = Eager(token_fp16) if args.eager else graph_of(token_fp16)
     ms_fp16, _ = timed(gf, args.steps, args.warmup)
     del gf
@@ -346,9 +352,27 @@ def bench_linear(args):
     bytes_per_token = sum(N * K * nbits / 8 + N * (K // gs) * 8 + K * 2 + N * 2
                           for (N, K) in LLAMA7B_LINEARS) * LLAMA7B_LAYERS
     gbs = bytes_per_token / (ms_ev * 1e-3) / 1e9
+    metric = LINEAR_METRIC if M == 1 else PREFILL_METRIC.format(m=M)
+    if M == 1:
+        # decode: the codes and meta cross HBM once per token
+        roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": (lambda c: c["hbm_bytes_per_step"] if c else None)(linear_counter_summary()),
+                    "kernel": "linear_skinny_kernel (4-bit, g64)",
+                    "bytes_per_step": int(bytes_per_token),
+                    "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)}
+    else:
+        # many rows: 2 M N K flops per product on the MFMA units (fp16 or
+        # bf16 inputs, fp32 accumulation)
+        flops = 2.0 * M * LLAMA7B_WEIGHTS
+        tfs = flops / (ms_ev * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfs / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "linear_tiled_kernel (4-bit, g64)" if M > 32 else "linear_skinny_kernel (4-bit, g64)",
+                    "flops_per_step": flops}
     out = {
-        "metric": LINEAR_METRIC if args.cdtype == "f16" else LINEAR_METRIC + ", compute dtype bf16",
-        "value": round(1e3 / ms_ev, 3),
+        "metric": metric if args.cdtype == "f16" else metric + ", compute dtype bf16",
+        "value": round(M * 1e3 / ms_ev, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -359,21 +383,17 @@ def bench_linear(args):
         "vs_baseline": None,
         "dtype": args.cdtype,
         "data": "synthetic",
-        "config": {"workload": "llama7b_decode_b1_4b_g64", "linears": len(layers), "M": 1,
+        "config": {"workload": "llama7b_decode_b1_4b_g64" if M == 1 else f"llama7b_prefill_m{M}_4b_g64",
+                   "linears": len(layers), "M": M,
                    "weights": LLAMA7B_WEIGHTS, "nbits": nbits, "group_size": gs, "axis": 1},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": (lambda c: c["hbm_bytes_per_step"] if c else None)(linear_counter_summary()),
-                     "kernel": "linear_skinny_kernel (4-bit, g64)",
-                     "bytes_per_step": int(bytes_per_token),
-                     "bytes_per_weight": round(bytes_per_token / LLAMA7B_WEIGHTS, 4)},
+        "roofline": roofline,
         "dense_matmul": {"dtype": args.cdtype, "ms_per_step": round(ms_fp16, 4),
-                         "tokens_per_s": round(1e3 / ms_fp16, 3),
+                         "tokens_per_s": round(M * 1e3 / ms_fp16, 3),
                          "speedup": round(ms_fp16 / ms_ev, 3),
                          "per_layer_calls_ms_per_step":
                              round(ms_fp16_per_layer, 4) if ms_fp16_per_layer else None},
         "per_layer_calls": {"ms_per_step": round(ms_per_layer, 4),
-                            "tokens_per_s": round(1e3 / ms_per_layer, 3)} if ms_per_layer else None,
+                            "tokens_per_s": round(M * 1e3 / ms_per_layer, 3)} if ms_per_layer else None,
         "wall_ms_per_step": round(ms_wall, 4),
         "launch": ("eager" if args.eager else "hip graph") +
                   " of 128 calls: hqq_linear_batch of (q, k, v), (o), (gate, up), (down) per layer",
@@ -545,6 +565,8 @@ def main():
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--cdtype", choices=("f16", "bf16"), default="f16",
                     help="linear: compute dtype of the activations and outputs")
+    ap.add_argument("--rows", type=int, default=1,
+                    help="linear: rows of X per step (1: decode; e.g. 2048: a prefill chunk)")
     ap.add_argument("--no-per-layer", action="store_true",
                     help="linear: skip the one-call-per-product context timings (profiler runs)")
     ap.add_argument("--wdtype", choices=("f16", "bf16"), default="f16",
