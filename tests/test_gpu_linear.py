@@ -192,11 +192,13 @@ def test_matches_gpu_dequantize_then_matmul_operand(hq, oracle_mod):
 
 # the 7B decoder's linear shapes at one token (decode): q/k/v/o, gate/up, down;
 # and batches of rows: M = 96 and 200 take the tiled kernel by its time
-# estimate (one partly filled 256-row tile), M = 64 at N = 4096 the row blocks
+# estimate, M = 64 at N = 4096 the row blocks; the tiled kernel runs 128-row
+# tiles where they fit the CUs in as few rounds (M = 96 ... 512 here) and
+# 256-row tiles at M = 768, N = 11008
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008),
                                    (8, 11008, 4096), (32, 4096, 4096), (512, 4096, 4096),
                                    (256, 11008, 4096), (96, 11008, 4096), (200, 4096, 4096),
-                                   (64, 4096, 4096)])
+                                   (64, 4096, 4096), (768, 11008, 4096)])
 def test_linear_full_size(hq, oracle_mod, M, N, K):
     rng = np.random.RandomState(M + N // 7 + K // 5)
     nbits, gs = 4, 64
@@ -297,6 +299,22 @@ def check_bf16(Yb, Yref, A, K, tag=""):
     bound = 2.0 ** -8 * np.abs(Yref) + 1.01 * K * 2.0 ** -24 * A + 2.0 ** -133
     worst = np.max(err / bound)
     assert worst <= 1.0, f"{tag}: worst error / bound = {worst:.3g}"
+
+
+@pytest.mark.parametrize("M,N,K", [(768, 11008, 4096), (300, 4096, 4096)])
+def test_linear_bf16_full_size(hq, oracle_mod, M, N, K):
+    """bf16 at full size, 256-row tiles (M = 768, N = 11008) and 128-row tiles
+    (M = 300), against the oracle on a sample of output columns."""
+    rng = np.random.RandomState(7000 + M + N // 7)
+    nbits, gs = 4, 64
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    Xb = random_bf16(rng, (M, K))
+    Y = gpu_linear_bf16(hq, Xb, packed, scale, zero, N, nbits, gs)
+    cols = np.sort(rng.choice(N, 64, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    Yref, A = oracle_mod.linear(Xb, packed[cols], scale[cols], zero[cols], len(cols), nbits, gs,
+                                with_abs=True, dtype="bf16")
+    check_bf16(Y[:, cols], Yref, A, K, f"bf16 {M}x{N}x{K}")
 
 
 BF16_CASES = list(dict.fromkeys([c for i, c in enumerate(CASES) if i % 3 == 0]

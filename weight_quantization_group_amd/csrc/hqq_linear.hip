@@ -643,18 +643,22 @@ __device__ __forceinline__ void dequant_tile_runs(const TileW<NB, G1> &b, uint4 
 }
 
 
-template <int NB, bool G1, bool BF, bool PR>
+// BM: rows of the tile, 256 or 128 (per-thread arrays are sized for 256 and
+// use the first BM / 32 entries)
+template <int NB, bool G1, bool BF, bool PR, int BM>
 __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
 {
     uint32_t bx = blockIdx.x;
     const LinearArgs a = batch_item(lb, bx);
-    constexpr int TM = kTBM / 32, TN = kTBN / 32;   // MFMA tiles per MFMA wave (8 x 4)
+    static_assert(BM == 256 || BM == 128, "tile rows");
+    constexpr int TM = BM / 32, TN = kTBN / 32;     // MFMA tiles per MFMA wave (8 x 4 at BM = 256)
+    constexpr int XI = BM / 32;                     // X DMA instructions per MFMA wave and step
     typedef __attribute__((address_space(3))) void *lds_ptr;
     __shared__ uint4 xs[3][kTBM * 8];
     __shared__ uint4 ws[2][kTBN * kWPitch];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t m0 = (int64_t)blockIdx.y * kTBM, n0 = (int64_t)bx * kTBN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)bx * kTBN;
     const uint32_t K = (uint32_t)a.K;
     const uint32_t steps = K / kTK;
     // past the last step the loads repeat it (in bounds, never used)
@@ -663,23 +667,23 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
     if (wave < 4) {
         // MFMA wave: step st reads X from buffer st % 3 and W from st & 1
         const int wm = wave >> 1, wn = wave & 1;
-        // X DMA: wave w moves rows 64 w .. 64 w + 63, 8 rows (64 runs) per
-        // instruction; lane l fills slot (row 8 i + l / 8, column l % 8),
-        // which holds run (l % 8) ^ (row % 8) of that row
-        uint32_t xsrc[8];
+        // X DMA: wave w moves rows BM/4 w .. BM/4 (w + 1) - 1, 8 rows (64
+        // runs) per instruction; lane l fills slot (row 8 i + l / 8, column
+        // l % 8), which holds run (l % 8) ^ (row % 8) of that row
+        uint32_t xsrc[kTBM / 32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 64 * wave + 8 * i + (lane >> 3);
+        for (int i = 0; i < XI; ++i) {
+            const int r = (BM / 4) * wave + 8 * i + (lane >> 3);
             const int64_t m = m0 + r < a.M ? m0 + r : a.M - 1;
             xsrc[i] = (uint32_t)(m * a.K) + 8 * ((lane & 7) ^ (r & 7));      // halves
         }
         auto dma_x = [&](uint32_t k0, int b) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds(a.X + xsrc[i] + k0, (lds_ptr)&xs[b][(64 * wave + 8 * i) * 8],
-                                                 16, 0, 0);
+            for (int i = 0; i < XI; ++i)
+                __builtin_amdgcn_global_load_lds(a.X + xsrc[i] + k0,
+                                                 (lds_ptr)&xs[b][((BM / 4) * wave + 8 * i) * 8], 16, 0, 0);
         };
-        float4v acc[TM][TN];
+        float4v acc[kTBM / 32][TN];
 #pragma unroll
         for (int u = 0; u < TM; ++u)
 #pragma unroll
@@ -691,12 +695,12 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
         lds_barrier();                        // and W(0) is in LDS
         for (uint32_t st = 0; st < steps; ++st) {
             const int bx_ = (int)(st % 3), bw = (int)(st & 1);
-            uint4 A[2][TM], B[2][TN];
+            uint4 A[2][kTBM / 32], B[2][TN];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int u = 0; u < TM; ++u) {
-                    const int r = wm * (kTBM / 2) + 16 * u + (lane & 15);
+                    const int r = wm * (BM / 2) + 16 * u + (lane & 15);
                     A[ks][u] = xs[bx_][r * 8 + ((4 * ks + (lane >> 4)) ^ (r & 7))];
                 }
 #pragma unroll
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
             for (int t = 0; t < TN; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t m = m0 + wm * (kTBM / 2) + 16 * u + 4 * (lane >> 4) + r;
+                    const int64_t m = m0 + wm * (BM / 2) + 16 * u + 4 * (lane >> 4) + r;
                     const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
                     if (m < a.M && n < a.N)
                         a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
@@ -786,27 +790,56 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
     }
 }
 
+// Time estimates of the two kernels (the row-block kernel re-derives W for
+// every 32 rows of X, so its time grows with ceil(M / 32) * N * K; the tiled
+// kernel's is its rounds of tiles over the 256 CUs times K / 64 steps), from
+// times measured for 4-bit g64 codes at K = 4096 on MI355X: 9.1 us per
+// 32-row block at N = 4096; a step of 0.92 us with 256-row tiles and 0.74 us
+// with 128-row tiles.
+inline double skinny_us(const LinearBatch &b)
+{
+    int64_t n = 0;
+    for (int j = 0; j < b.count; ++j)
+        n += b.N[j];
+    return (double)((b.a.M + 31) / 32) * 9.1 * ((double)n * (double)b.a.K) / (4096.0 * 4096.0);
+}
+
+inline double tiled_us(const LinearBatch &b, int bm)
+{
+    int64_t cols = 0;
+    for (int j = 0; j < b.count; ++j)
+        cols += (b.N[j] + kTBN - 1) / kTBN;
+    const int64_t tiles = cols * ((b.a.M + bm - 1) / bm);
+    return (double)((tiles + 255) / 256) * (double)(b.a.K / kTK) * (bm == 128 ? 0.74 : 0.92);
+}
+
+#define HQQ_LAUNCH_TILED(BMV)                                                                           \
+    {                                                                                                   \
+        const dim3 grid(cols, (unsigned)((b.a.M + BMV - 1) / BMV));                                     \
+        if (NB == 4 && b.a.gs >= 64)                                                                    \
+            hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4, BMV>), grid, dim3(512), 0, s, b); \
+        else if (b.a.gs >= 32)                                                                          \
+            hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, false, BMV>), grid, dim3(512), 0, s, b);   \
+        else                                                                                            \
+            hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF, false, BMV>), grid, dim3(512), 0, s, b);  \
+    }
+
+// 128-row tiles where their estimate is the smaller (few 256-row tiles)
 template <int NB, bool BF>
 hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
-    const dim3 grid(fill_tiles(b, kTBN), (unsigned)((b.a.M + kTBM - 1) / kTBM));
-    if (NB == 4 && b.a.gs >= 64)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4>), grid, dim3(512), 0, s, b);
-    else if (b.a.gs >= 32)
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, false>), grid, dim3(512), 0, s, b);
+    const uint32_t cols = fill_tiles(b, kTBN);
+    if (tiled_us(b, 128) < tiled_us(b, 256))
+        HQQ_LAUNCH_TILED(128)
     else
-        hipLaunchKernelGGL((linear_tiled_kernel<NB, false, BF, false>), grid, dim3(512), 0, s, b);
+        HQQ_LAUNCH_TILED(256)
     return hipGetLastError();
 }
+#undef HQQ_LAUNCH_TILED
 
-// Kernel choice for M > 32 (K a multiple of 64; 2-, 4- and 8-bit codes).
-// The row-block kernel re-derives W for every 32 rows of X, so its time
-// grows with ceil(M / 32) * N * K; the tiled kernel's time is its number of
-// rounds of tiles over the 256 CUs times K / 64 steps.  Both estimates use
-// the times measured for 4-bit g64 codes at K = 4096 on MI355X: 9.1 us per
-// 32-row block at N = 4096, 0.92 us per tiled step.  The tiled kernel is
-// taken when its estimate is the smaller one; from 384 rows it always is at
-// the shapes measured, and from there it is taken whatever the shape.
+// Kernel choice for M > 32 (K a multiple of 64; 2-, 4- and 8-bit codes): the
+// smaller estimate; from 384 rows the tiled kernel whatever the shape (its
+// estimate is the smaller one at every shape measured there).
 constexpr int64_t kTiledMinRows = 384;
 
 inline bool use_tiled(const LinearBatch &b)
@@ -816,16 +849,8 @@ inline bool use_tiled(const LinearBatch &b)
         return false;
     if (a.M >= kTiledMinRows)
         return true;
-    int64_t n = 0, ntiles = 0;
-    for (int j = 0; j < b.count; ++j) {
-        n += b.N[j];
-        ntiles += (b.N[j] + kTBN - 1) / kTBN;
-    }
-    const double row_blocks = (double)((a.M + 31) / 32);
-    const double skinny_us = row_blocks * 9.1 * ((double)n * (double)a.K) / (4096.0 * 4096.0);
-    const int64_t tiles = ntiles * ((a.M + kTBM - 1) / kTBM);
-    const double tiled_us = (double)((tiles + 255) / 256) * (double)(a.K / kTK) * 0.92;
-    return tiled_us < skinny_us;
+    const double t = tiled_us(b, 128) < tiled_us(b, 256) ? tiled_us(b, 128) : tiled_us(b, 256);
+    return t < skinny_us(b);
 }
 
 template <int NB, bool BF>
