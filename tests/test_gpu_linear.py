@@ -118,6 +118,8 @@ CASES = [
     (640, 256, 320, 8, 64),
     (448, 96, 384, 4, 32),      # tiled, 4-bit: two groups per 64-k step
     (390, 140, 512, 4, 128),    # tiled, 4-bit: a group spans two steps
+    (400, 70, 64, 4, 64),       # tiled, a single k step
+    (390, 40, 64, 8, 32),       # tiled, a single k step, 8-bit
 ]
 
 
