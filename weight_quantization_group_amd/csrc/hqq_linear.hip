@@ -562,9 +562,11 @@ hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (many rows of X: prefill).  A workgroup computes a 256 x 128
-// tile of Y with eight waves in two roles, one of each on every SIMD:
+// tile of Y (or 128 x 128 where that fills the CUs better) with eight waves in
+// two roles, one of each on every SIMD:
 //   * waves 0-3 (MFMA waves, 2 x 2, each 128 x 64 outputs as 8 x 4 MFMA
-//     16x16x32 tiles) copy X's 256 x 64 tile of a 64-wide k step global ->
+//     16x16x32 tiles, 64 x 64 as 4 x 4 with 128-row tiles) copy X's tile of
+//     a 64-wide k step global ->
 //     LDS by DMA (global_load_lds, no registers; runs of 8 k XOR-swizzled
 //     by row so the MFMA reads of 16 rows spread over the banks) and run the
 //     step's 64 MFMAs per wave from LDS;
@@ -578,7 +580,7 @@ hipError_t launch_gpc(LinearBatch &b, hipStream_t s)
 // reads all of a step's operands into registers before it issues the next
 // DMA, so the wait the compiler places for the DMA before the next LDS read
 // comes after a full step of matrix work.  The dequantization is shared by
-// the 256 rows of X.
+// the 256 (or 128) rows of X.
 
 constexpr int kTK = 64;              // k per step
 constexpr int kTBM = 256, kTBN = 128;
