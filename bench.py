@@ -581,7 +581,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the solve shards with no communication; see DESIGN.md)", file=sys.stderr)
+              "(the solve shards by whole tensors or row blocks with no communication, so N GPUs "
+              "would give N times the one-GPU rate)", file=sys.stderr)
         sys.exit(2)
 
     import torch
