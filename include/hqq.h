@@ -151,9 +151,11 @@ typedef struct hqq_host_tensor {
  * The weights cross PCIe once, in chunks of whole row blocks (whole groups
  * and packed words) that fit half of the caller's device staging buffer:
  * chunk c is copied into half c % 2 on copy_stream while the solve of chunk
- * c - 1 runs on compute_stream.  Everything is enqueued asynchronously; the
- * results are complete when compute_stream has finished, and the host
- * weights and the staging buffer must stay untouched until then.
+ * c - 1 runs on compute_stream.  The first copies wait for the work enqueued
+ * on compute_stream before the call, so back-to-back calls may share one
+ * staging buffer.  Everything is enqueued asynchronously; the results are
+ * complete when compute_stream has finished, and the host weights and the
+ * staging buffer must stay untouched until then.
  *   tensors        HOST array of n descriptors (read during the call only)
  *   staging        device buffer, 16-byte aligned, staging_bytes long; each
  *                  half must hold at least one block unit of every tensor
@@ -162,7 +164,7 @@ typedef struct hqq_host_tensor {
  *                  HQQ_EINVAL_SHAPE
  *   copy_stream, compute_stream  HIP streams (may be the same stream)
  * Every descriptor is validated before anything is enqueued.  n = 0 is a
- * no-op.  The call creates four HIP events and releases them before it
+ * no-op.  The call creates five HIP events and releases them before it
  * returns (pending ones when they complete); it allocates no memory. */
 HQQ_API int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n,
                                   int nbits, int group_size, int axis,

@@ -67,18 +67,20 @@ def check_parity(oracle_mod, W16, nbits, gs, axis, g_packed, g_scale, g_zero, o=
     assert np.abs(diff).max(initial=0) <= 1, f"{tag}: code differs by more than 1"
     assert mism <= 1e-4 * diff.size, f"{tag}: {mism} of {diff.size} codes differ"
     assert g_codes.max() <= QMAX[nbits]
-    # scale (computed identically: exact), zero (1e-4 relative)
-    assert np.array_equal(g_scale, o_scale), f"{tag}: scale differs"
+    # scale and zero: the method's bar is 1e-4 relative; the kernel computes
+    # both exactly as the oracle does, so scale must match bit for bit and
+    # zero in value (+0 and -0 are the same zero)
     rel = np.abs(g_zero.astype(np.float64) - o_zero) / np.maximum(np.abs(o_zero.astype(np.float64)), 1e-30)
-    bad = (rel > 1e-4) & (np.abs(g_zero - o_zero) > 1e-6)
-    assert not bad.any(), f"{tag}: {bad.sum()} zeros beyond 1e-4 (max rel {rel.max()})"
+    assert rel.max(initial=0.0) <= 1e-4, f"{tag}: zeros beyond 1e-4 (max rel {rel.max()})"
+    assert np.array_equal(g_scale.view(np.uint32), o_scale.view(np.uint32)), f"{tag}: scale differs"
+    assert np.array_equal(g_zero, o_zero), f"{tag}: {np.sum(g_zero != o_zero)} zeros differ (max rel {rel.max()})"
     # MSE
     mg = recon_mse(W16, g_codes, g_scale, g_zero, gs, axis)
     mo = recon_mse(W16, o_codes, o_scale, o_zero, gs, axis)
     assert abs(mg - mo) <= 1e-3 * mo + 1e-30, f"{tag}: MSE {mg} vs {mo}"
     # the packed words must also be exactly the oracle's packing of the GPU codes
     assert np.array_equal(g_packed, oracle_mod.pack(g_codes, nbits, axis))
-    return dict(code_mismatch=mism, zero_exact=float(np.mean(g_zero == o_zero)), mse=mg)
+    return dict(code_mismatch=mism, zero_max_rel=float(rel.max(initial=0.0)), mse=mg, mse_oracle=mo)
 
 
 # --------------------------------------------------------------------------
@@ -141,12 +143,15 @@ def test_quantize_formats(hq, oracle_mod, nbits, gs, axis):
     # several work items per wave plus a ragged last block along the line
     ngroups = 7 if gs <= 64 else 3
     if axis == 1:
-        shape = (67, gs * ngroups)
+        shapes = [(67, gs * ngroups)]
     else:
-        shape = (gs * ngroups, 67)
-    W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.002)
-    g = gpu_quantize(hq, W16, nbits, gs, axis)
-    check_parity(oracle_mod, W16, nbits, gs, axis, *g, tag=f"{nbits}b g{gs} ax{axis}")
+        # 67 columns: groups loaded directly; 128 columns (cols % 64 == 0):
+        # groups fetched into LDS by DMA, eight rows per 16-byte transfer
+        shapes = [(gs * ngroups, 67), (gs * ngroups, 128)]
+    for shape in shapes:
+        W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.002)
+        g = gpu_quantize(hq, W16, nbits, gs, axis)
+        check_parity(oracle_mod, W16, nbits, gs, axis, *g, tag=f"{nbits}b g{gs} ax{axis} {shape}")
 
 
 @pytest.mark.parametrize("nbits,gs,axis,p,beta0,kappa", [
@@ -198,7 +203,7 @@ def test_single_linear_workload_full(hq, oracle_mod):
     W16 = synth.generate_np(t["seed"], t["layer"], t["tensor_id"], t["rows"], t["cols"])
     g = gpu_quantize(hq, W16, 4, 64, 1)
     st = check_parity(oracle_mod, W16, 4, 64, 1, *g, tag="single linear")
-    assert st["code_mismatch"] == 0 and st["zero_exact"] == 1.0
+    assert st["code_mismatch"] == 0 and st["zero_max_rel"] == 0.0
     print("single linear", st)
 
 
@@ -273,108 +278,6 @@ def test_synth_gpu_generator_matches_numpy():
         same = np.mean(g == c)
         d = np.abs(g.astype(np.int32) - c.astype(np.int32))
         assert same > 0.9999 and d.max() <= 1, (same, d.max())
-
-
-# --------------------------------------------------------------------------
-# full-size workloads, in the benchmark's launch configuration, sampled
-# --------------------------------------------------------------------------
-
-def _sampled_parity(hq, oracle_mod, t, nsample, seed_extra=0):
-    import torch
-
-    rows, cols, nb, gs, axis = t["rows"], t["cols"], t["nbits"], t["group_size"], t["axis"]
-    W = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
-    synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
-    packed, scale, zero = hq.hqq_quantize(W, nb, gs, axis)
-    torch.cuda.synchronize()
-    rng = np.random.RandomState((t["tensor_id"] * 131 + t["layer"] * 7 + seed_extra) & 0xFFFF)
-    if axis == 1:
-        idx = np.sort(rng.choice(rows, nsample, replace=False))
-        it = torch.from_numpy(idx).cuda()
-        W16 = W.index_select(0, it).cpu().numpy().view(np.uint16)
-        gp = _np_u32(packed.index_select(0, it))
-        gsc = scale.index_select(0, it).cpu().numpy()
-        gz = zero.index_select(0, it).cpu().numpy()
-    else:
-        idx = np.sort(rng.choice(cols, nsample, replace=False))
-        it = torch.from_numpy(idx).cuda()
-        W16 = np.ascontiguousarray(W.index_select(1, it).cpu().numpy().view(np.uint16))
-        gp = np.ascontiguousarray(_np_u32(packed.index_select(1, it)))
-        gsc = np.ascontiguousarray(scale.index_select(1, it).cpu().numpy())
-        gz = np.ascontiguousarray(zero.index_select(1, it).cpu().numpy())
-    del W, packed, scale, zero
-    st = check_parity(oracle_mod, W16, nb, gs, axis, gp, gsc, gz,
-                      tag=f"L{t['layer']} {t['name']} {nb}b g{gs} ax{axis}")
-    return st
-
-
-@pytest.mark.parametrize("wl", ["llama7b_layer_4b_g64", "llama7b_layer_3b2b_axis0"])
-def test_7b_layer_sampled(hq, oracle_mod, wl):
-    for t in synth.workload(wl):
-        n = 48 if t["axis"] == 1 else 24
-        st = _sampled_parity(hq, oracle_mod, t, n)
-        print(wl, t["name"], st)
-
-
-def test_7b_stack_last_layer_sampled(hq, oracle_mod):
-    for t in synth.workload("llama7b_stack32_4b_g64"):
-        if t["layer"] in (17, 31):
-            _sampled_parity(hq, oracle_mod, t, 24)
-
-
-def test_70b_stack_sampled(hq, oracle_mod):
-    for t in synth.workload("llama70b_stack80_mixed"):
-        if t["layer"] in (0, 79):
-            st = _sampled_parity(hq, oracle_mod, t, 16 if t["name"] in ("gate", "up") else 32)
-            print("70b", t["layer"], t["name"], st)
-
-
-def _bench_chunks(tensors, max_batch):
-    """The benchmark's launches: consecutive tensors of one format, up to
-    max_batch per hqq_quantize_batch call."""
-    chunks = []
-    for i, t in enumerate(tensors):
-        fmt = (t["nbits"], t["group_size"], t["axis"])
-        if chunks and chunks[-1][0] == fmt and len(chunks[-1][1]) < max_batch:
-            chunks[-1][1].append(i)
-        else:
-            chunks.append((fmt, [i]))
-    return chunks
-
-
-@pytest.mark.parametrize("wl,layers,nsample", [("llama7b_stack32_4b_g64", (0, 1, 2, 3), 6),
-                                               ("llama70b_stack80_mixed", (0, 1), 8)])
-def test_batched_launches_sampled(hq, oracle_mod, wl, layers, nsample):
-    """The benchmark's exact launch configuration (hqq_quantize_batch over
-    consecutive same-format tensors, the first 24 of the 7B stack in one
-    launch; the 70B layers' mixed formats in several), full-size tensors,
-    sampled rows of every tensor against the oracle."""
-    import torch
-
-    tensors = [t for t in synth.workload(wl) if t["layer"] in layers]
-    for fmt, idx in _bench_chunks(tensors, hq.MAX_BATCH):
-        items = []
-        for i in idx:
-            t = tensors[i]
-            W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device="cuda")
-            synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
-            ms = hq.meta_shape(t["rows"], t["cols"], fmt[1], fmt[2])
-            items.append((W, torch.empty(hq.packed_shape(t["rows"], t["cols"], fmt[0], fmt[2]),
-                                         dtype=torch.int32, device="cuda"),
-                          torch.empty(ms, dtype=torch.float32, device="cuda"),
-                          torch.empty(ms, dtype=torch.float32, device="cuda")))
-        hq.QuantizeBatch(items, *fmt).run()
-        torch.cuda.synchronize()
-        for i, (W, pk, sc, ze) in zip(idx, items):
-            t = tensors[i]
-            rng = np.random.RandomState(i * 17 + t["layer"])
-            rows = np.sort(rng.choice(t["rows"], nsample, replace=False))
-            it = torch.from_numpy(rows).cuda()
-            W16 = W.index_select(0, it).cpu().numpy().view(np.uint16)
-            check_parity(oracle_mod, W16, *fmt, _np_u32(pk.index_select(0, it)),
-                         sc.index_select(0, it).cpu().numpy(), ze.index_select(0, it).cpu().numpy(),
-                         tag=f"{wl} L{t['layer']} {t['name']} launch of {len(idx)}")
-        del items
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])

@@ -387,6 +387,10 @@ def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging
                                  ctypes.c_void_p(cs.cuda_stream), ctypes.c_void_p(ks.cuda_stream))
     if st != 0:
         raise HQQError("hqq_quantize_streamed", st)
+    # the staging buffer is in use on both streams until compute_stream
+    # completes: keep torch's allocator from handing it out earlier
+    staging.record_stream(cs)
+    staging.record_stream(ks)
 
 
 def hqq_quantize_meta(meta: torch.Tensor, group_size: int = 128):

@@ -7,7 +7,9 @@
 // row blocks that fit half of a caller-provided device staging buffer; chunk
 // c is copied into half c % 2 on the copy stream while the solve of chunk
 // c - 1 runs on the compute stream from the other half.  Events order the two
-// streams: a solve waits for its chunk's copy, and a copy into a half waits
+// streams: the first copies wait for all work enqueued on the compute stream
+// before the call (an earlier call's solves may still read the staging
+// buffer), a solve waits for its chunk's copy, and a copy into a half waits
 // for the solve that last read it.  Each chunk is one batched solve launch
 // (up to 24 row blocks), so results are identical to hqq_quantize on device
 // copies of the weights.
@@ -45,9 +47,11 @@ struct Piece {
 
 struct Events {
     hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+    hipEvent_t entry = nullptr;
     bool ok = true;
     Events()
     {
+        ok = hipEventCreateWithFlags(&entry, hipEventDisableTiming) == hipSuccess;
         for (int b = 0; b < 2; ++b)
             ok = ok && hipEventCreateWithFlags(&copied[b], hipEventDisableTiming) == hipSuccess &&
                  hipEventCreateWithFlags(&done[b], hipEventDisableTiming) == hipSuccess;
@@ -55,6 +59,8 @@ struct Events {
     ~Events()
     {
         // an event destroyed while still pending is released when it completes
+        if (entry)
+            (void)hipEventDestroy(entry);
         for (int b = 0; b < 2; ++b) {
             if (copied[b])
                 (void)hipEventDestroy(copied[b]);
@@ -128,6 +134,10 @@ int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int 
     const hipStream_t cs = (hipStream_t)copy_stream, ks = (hipStream_t)compute_stream;
     Events ev;
     if (!ev.ok)
+        return HQQ_EHIP;
+    // the staging buffer may still be read by solves enqueued on the compute
+    // stream before this call: the copies start after them
+    if (hipEventRecord(ev.entry, ks) != hipSuccess || hipStreamWaitEvent(cs, ev.entry, 0) != hipSuccess)
         return HQQ_EHIP;
     const int64_t C = hqq::codes_per_word(nbits);
     for (size_t c = 0; c < chunks.size(); ++c) {
