@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import re
 import subprocess
 
 import numpy as np
@@ -66,7 +67,8 @@ def workload(name: str):
     group_size, axis, seed.  Names: 'linear_4096x1024_4b_g64',
     'llama7b_layer_4b_g64', 'llama7b_layer_3b2b_axis0', 'llama7b_stack32_4b_g64',
     'llama7b_stack32_8b_g128' (the same weights at 8 bits, group 128),
-    'llama70b_stack80_mixed'."""
+    'llama70b_stack80_mixed', and 'llama7b_stack<L>_<b>b_g<gs>[_axis0]' (L layers
+    of the 7B shapes in one format)."""
     out = []
     if name == "linear_4096x1024_4b_g64":
         out.append(dict(layer=0, name="q", tensor_id=0, rows=4096, cols=1024, nbits=4,
@@ -101,7 +103,16 @@ def workload(name: str):
                 out.append(dict(layer=layer, name=n, tensor_id=TENSOR_IDS[n], rows=r, cols=c,
                                 nbits=nb, group_size=gs, axis=1, seed=SEED_70B))
     else:
-        raise KeyError(name)
+        # llama7b_stack<L>_<b>b_g<gs>[_axis0]: L decoder layers of the 7B shapes,
+        # every tensor in one format (axis 1 unless the suffix says 0)
+        m = re.fullmatch(r"llama7b_stack(\d+)_([12348])b_g(\d+)(_axis0)?", name)
+        if not m:
+            raise KeyError(name)
+        L, nb, gs, ax = int(m.group(1)), int(m.group(2)), int(m.group(3)), 0 if m.group(4) else 1
+        for layer in range(L):
+            for n, r, c in _layer_7b():
+                out.append(dict(layer=layer, name=n, tensor_id=TENSOR_IDS[n], rows=r, cols=c,
+                                nbits=nb, group_size=gs, axis=ax, seed=SEED_7B))
     return out
 
 
