@@ -44,6 +44,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -81,6 +82,7 @@ def hbm_bytes_per_weight(nbits: int, group_size: int) -> float:
 # byte-identical to the ones the counters were taken with.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "solve_4b_g64_llama7b_stack32.traffic.json")
 KERNEL_SOURCES = ["weight_quantization_group_amd/csrc/hqq_solve_impl.h",
+                  "weight_quantization_group_amd/csrc/hqq_solve_seg.h",
                   "weight_quantization_group_amd/csrc/hqq_solve_b4.hip",
                   "weight_quantization_group_amd/csrc/hqq_internal.h"]
 
@@ -111,7 +113,47 @@ def counter_summary(workload: str, wdtype: str):
     return t
 
 
-def cpu_baseline(workload: str, iters: int, max_procs: int = 16):
+def work_items(t, nbits, group_size, axis):
+    """Work items of one tensor in a solve launch: lcm(gs, codes per word)
+    elements of a line each."""
+    C = {8: 4, 4: 8, 3: 10, 2: 16, 1: 32}[nbits]
+    lb = group_size * C // math.gcd(group_size, C)
+    L, lines = (t["cols"], t["rows"]) if axis == 1 else (t["rows"], t["cols"])
+    return -(-L // lb) * lines
+
+
+def solve_kernel_name(hq, fmt, wdtype, items):
+    nb, gs, ax = fmt
+    if hq.hqq_solve_mapping(nb, gs, ax, wdtype, items) == hq.MAPPING_SEG:
+        return f"solve_seg_kernel<{nb},{gs}>"
+    return f"solve_kernel<{nb},{gs},{ax},{'true' if wdtype == hq.DTYPE_BF16 else 'false'}>"
+
+
+def host_cpu():
+    """(CPU model, cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return model, n
+
+
+# The host share of a one-GPU box is 16 cores; the oracle runs on at most
+# this many processes whatever the machine reports.
+CPU_BASELINE_MAX_PROCS = 16
+
+
+def cpu_baseline(workload: str, iters: int, p: float = 0.7, beta0: float = 10.0,
+                 max_procs: int = CPU_BASELINE_MAX_PROCS):
     """Time the oracle (single-threaded C, as it stands) on decoder layer 0 of
     the workload, in P independent processes over row slices."""
     import multiprocessing as mp
@@ -119,12 +161,13 @@ def cpu_baseline(workload: str, iters: int, max_procs: int = 16):
     import synth
 
     tensors = [t for t in synth.workload(workload) if t["layer"] == 0]
-    P = max(1, min(max_procs, os.cpu_count() or 1))
+    model, avail = host_cpu()
+    P = max(1, min(max_procs, avail))
     jobs = []
     for t in tensors:
         step = max(1, t["rows"] // P)
         for r0 in range(0, t["rows"], step):
-            jobs.append((t, r0, min(step, t["rows"] - r0), iters))
+            jobs.append((t, r0, min(step, t["rows"] - r0), iters, p, beta0))
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(P) as pool:
@@ -139,6 +182,9 @@ def cpu_baseline(workload: str, iters: int, max_procs: int = 16):
                 sample=f"decoder layer 0 of {workload} ({n:,} weights), oracle in {P} "
                        f"single-threaded processes over row slices; {busy:.1f} core-s, "
                        f"{wall:.1f} s wall incl. host generation",
+                cpu_model=model, cores_available=avail,
+                cores_note=f"{P} processes: all available cores up to the {max_procs}-core host "
+                           f"share of one GPU",
                 weights_per_s=round(n / eff_wall, 1))
 
 
@@ -146,11 +192,11 @@ def _cpu_job(job):
     import oracle
     import synth
 
-    t, r0, nr, iters = job
+    t, r0, nr, iters, p, beta0 = job
     W = synth.generate_np(t["seed"], t["layer"], t["tensor_id"], t["rows"], t["cols"], row0=r0,
                           nrows=nr)
     t0 = time.perf_counter()
-    oracle.quantize(W, t["nbits"], t["group_size"], t["axis"], iters=iters)
+    oracle.quantize(W, t["nbits"], t["group_size"], t["axis"], iters=iters, p=p, beta0=beta0)
     return W.size, time.perf_counter() - t0
 
 
@@ -560,6 +606,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama7b_stack32_4b_g64")
     ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--p", type=float, default=0.7,
+                    help="solve: the lp norm's p (p > 1 or a large beta0 keeps the shrink active, "
+                         "so the exact W_e = 0 shortcut never applies)")
+    ap.add_argument("--beta0", type=float, default=10.0, help="solve: the initial beta")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
@@ -641,9 +691,14 @@ def main():
             chunks.append((fmt, [i]))
     # the descriptor arrays are marshalled once (host metadata only); a step
     # is then one C-ABI call per launch
-    calls = [(fmt, hq.QuantizeBatch([(ins[i], *outs[i]) for i in idx], *fmt, iters=args.iters),
+    calls = [(fmt, hq.QuantizeBatch([(ins[i], *outs[i]) for i in idx], *fmt, iters=args.iters,
+                                    p=args.p, beta0=args.beta0),
               sum(tensors[i]["rows"] * tensors[i]["cols"] for i in idx))
              for fmt, idx in chunks]
+    # the kernel each launch runs (the library picks the mapping by launch size)
+    wdt = hq.DTYPE_BF16 if args.wdtype == "bf16" else hq.DTYPE_FP16
+    kernels = [solve_kernel_name(hq, fmt, wdt, sum(work_items(tensors[i], *fmt) for i in idx))
+               for fmt, idx in chunks]
 
     def step(events=None):
         for j, (_, batch, _) in enumerate(calls):
@@ -676,11 +731,14 @@ def main():
         d["launches"] += args.steps
     # dominant kernel: the format with the most weights
     (nb, gs, ax), dom = max(by_fmt.items(), key=lambda kv: kv[1]["w"])
+    dom_kernel = max(((kernels[j], w) for j, (fmt, _, w) in enumerate(calls) if fmt == (nb, gs, ax)),
+                     key=lambda kw: kw[1])[0]
     w_per_launch = dom["w"] / dom["launches"]
     avg_ms = dom["ms"] / dom["launches"]
     bpw = hbm_bytes_per_weight(nb, gs)
     hbm_gbs = bpw * w_per_launch / (avg_ms * 1e-3) / 1e9
-    cs = counter_summary(args.workload, args.wdtype)
+    default_params = args.p == 0.7 and args.beta0 == 10.0 and args.iters == 20
+    cs = counter_summary(args.workload, args.wdtype) if default_params else None
     traffic = round(cs["hbm_bytes_per_weight"] * w_per_launch) if cs else None
     valu = {"peak_TOPs": round(VALU_PEAK_TOPS, 3)}
     if cs:
@@ -691,9 +749,11 @@ def main():
 
     gbs = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     out = {
-        "metric": METRIC if args.workload == "llama7b_stack32_4b_g64" and args.wdtype == "f16" else
+        "metric": METRIC if (args.workload == "llama7b_stack32_4b_g64" and args.wdtype == "f16"
+                             and default_params) else
                   f"GB/s of {'fp16' if args.wdtype == 'f16' else 'bf16'} weights quantized "
-                  f"(HQQ {nb}b g{gs}, {args.iters} it), workload {args.workload}",
+                  f"(HQQ {nb}b g{gs}, {args.iters} it, p={args.p:g}, beta0={args.beta0:g}), "
+                  f"workload {args.workload}",
         "value": round(gbs, 3),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -708,11 +768,11 @@ def main():
         "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
                    "launches_per_step": len(calls),
                    "nbits": nb, "group_size": gs, "axis": ax, "iters": args.iters,
-                   "p": 0.7, "beta0": 10.0, "kappa": 1.01},
+                   "p": args.p, "beta0": args.beta0, "kappa": 1.01},
         "weights_per_s": round(n_weights / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"solve_kernel<{nb},{gs},{ax},{'true' if args.wdtype == 'bf16' else 'false'}>", "avg_launch_ms": round(avg_ms, 5),
+                     "kernel": dom_kernel, "avg_launch_ms": round(avg_ms, 5),
                      "weights_per_launch": round(w_per_launch), "bytes_per_weight": bpw,
                      "valu": valu},
         "context": {"pages_hqq_llama7b_quantize_minutes": 8.2, "hardware": "not stated on the pages"},
@@ -721,7 +781,7 @@ def main():
     # before it slows the GPU's launches measurably), in spawned processes
     # that never touch the GPU
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.iters)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.iters, args.p, args.beta0)
     print(json.dumps(out), flush=True)
 
 
