@@ -134,6 +134,21 @@ HQQ_API int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype,
                                   int nbits, int group_size, int axis,
                                   int iters, float p, float beta0, float kappa, void *stream);
 
+/* Which solve kernel a batched launch runs (host query, no GPU call): for a
+ * launch of `work_items` work items of this format (a work item is
+ * lcm(group_size, codes per word) elements of one line; for the formats below
+ * it is one group), HQQ_MAPPING_LANE: one lane per work item, the whole group
+ * in its registers; HQQ_MAPPING_SEG: group_size / 8 lanes per group with 8
+ * weights each, for axis 1, 32 <= group_size <= 128, fp16 weights and every
+ * width but 3 bits, taken for launches too small to fill the device with one
+ * lane per group (a threshold per width).  Both give identical outputs.
+ * The environment variable HQQ_SOLVE_MAPPING=lane or =seg, read at each
+ * call, forces one where the format allows it.  Invalid arguments: a
+ * negative HQQ_E* status. */
+#define HQQ_MAPPING_LANE 0
+#define HQQ_MAPPING_SEG 1
+HQQ_API int hqq_solve_mapping(int nbits, int group_size, int axis, int wdtype, int64_t work_items);
+
 /* One tensor of a streamed quantize call: W in HOST memory, outputs on the
  * device (16-byte aligned; layouts as for hqq_quantize). */
 typedef struct hqq_host_tensor {

@@ -28,11 +28,15 @@ static int g_fail = 0;
 
 // ---------------------------------------------------------------- stubs
 static std::vector<hqq::SolveArgs> g_solve;
+static std::vector<bool> g_seg;
 
 namespace hqq {
-hipError_t launch_solve(int, int, int, bool, const SolveArgs &a, hipStream_t)
+hipError_t launch_solve(int nbits, int gs, int axis, bool bf16, bool seg, const SolveArgs &a, hipStream_t)
 {
+    if (seg && !seg_format(nbits, gs, axis, bf16))
+        return hipErrorInvalidValue;
     g_solve.push_back(a);
+    g_seg.push_back(seg);
     return hipSuccess;
 }
 hipError_t launch_dequantize(int, int, const CodecArgs &, hipStream_t) { return hipSuccess; }
@@ -96,10 +100,27 @@ static void check_launches(const std::vector<hqq_tensor> &ts, int nbits, int gs,
     const int C = hqq::codes_per_word(nbits);
     const int64_t lb = hqq::lcm_c(gs, C);
     size_t k = 0;
-    for (const hqq::SolveArgs &a : g_solve) {
+    const char *force = getenv("HQQ_SOLVE_MAPPING");
+    for (size_t li = 0; li < g_solve.size(); ++li) {
+        const hqq::SolveArgs &a = g_solve[li];
+        const bool seg = g_seg[li];
         CHECK(a.n >= 1 && a.n <= hqq::kMaxBatch);
         CHECK(a.depth >= 1 && a.depth <= hqq::kMaxDepth);
-        const int64_t per = (int64_t)hqq::kSolveBlock * a.depth;
+        // several lanes per group: only where the format allows it, always
+        // when forced, never when one lane per item is forced
+        if (!hqq::seg_format(nbits, gs, axis, false))
+            CHECK(!seg);
+        else if (force && strcmp(force, "seg") == 0)
+            CHECK(seg);
+        else if (force && strcmp(force, "lane") == 0)
+            CHECK(!seg);
+        const int64_t per = (seg ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(gs)
+                                 : (int64_t)hqq::kSolveBlock) * a.depth;
+        int64_t items = 0;
+        for (int j = 0; j < a.n; ++j)
+            items += a.t[j].n_items;
+        if (!force && hqq::seg_format(nbits, gs, axis, false))
+            CHECK(seg == (items < hqq::seg_max_items(nbits)));
         int64_t b = 0;
         for (int j = 0; j < a.n; ++j, ++k) {
             CHECK(k < ts.size());
@@ -172,6 +193,7 @@ static void test_certificate()
     for (float p : ps)
         for (float b0 : b0s) {
             g_solve.clear();
+            g_seg.clear();
             CHECK(hqq_quantize(W, 64, 128, 4, 64, 1, 20, p, b0, 1.01f, pk, sc, ze, nullptr) == HQQ_OK);
             CHECK(g_solve.size() == 1);
             if (g_solve.empty())
@@ -192,6 +214,7 @@ static void test_certificate()
             }
         }
     g_solve.clear();
+    g_seg.clear();
     CHECK(hqq_quantize(W, 64, 128, 4, 64, 1, 0, 0.7f, 10.f, 1.01f, pk, sc, ze, nullptr) == HQQ_OK);
     CHECK(g_solve.size() == 1 && g_solve[0].thr == 0.0f);
     free(W);
@@ -200,33 +223,43 @@ static void test_certificate()
     free(ze);
 }
 
-// Batched launches: 30 tensors of mixed shapes, every format and axis.
+// Batched launches: 30 tensors of mixed shapes, every format and axis, small
+// and large (the automatic mapping changes at seg_max_items groups per
+// launch), with the mapping automatic or forced either way.
 static void test_batches()
 {
     const int fmts[][3] = {{4, 64, 1}, {3, 64, 0}, {2, 16, 1}, {1, 16, 0}, {8, 128, 1}, {4, 32, 1}, {2, 64, 1}};
-    unsigned seed = 12345;
-    auto rnd = [&](int m) { seed = seed * 1103515245u + 12345u; return (int)((seed >> 8) % (unsigned)m); };
-    for (const auto &f : fmts)
-        {
-            std::vector<hqq_tensor> ts;
-            std::vector<void *> mem;
-            for (int i = 0; i < 30; ++i) {
-                const int64_t lines = 1 + rnd(3000), other = (int64_t)f[1] * (1 + rnd(40));
-                const int64_t rows = f[2] == 1 ? lines : other, cols = f[2] == 1 ? other : lines;
-                // pointers are only recorded, never dereferenced: one small
-                // aligned block stands in for every buffer
-                void *p = aligned(256);
-                mem.push_back(p);
-                ts.push_back(hqq_tensor{(const uint16_t *)p, rows, cols, (uint32_t *)p, (float *)p, (float *)p});
+    for (const char *force : {(const char *)nullptr, "lane", "seg"}) {
+        if (force)
+            setenv("HQQ_SOLVE_MAPPING", force, 1);
+        else
+            unsetenv("HQQ_SOLVE_MAPPING");
+        unsigned seed = 12345;
+        auto rnd = [&](int m) { seed = seed * 1103515245u + 12345u; return (int)((seed >> 8) % (unsigned)m); };
+        for (const auto &f : fmts)
+            for (int64_t scale : {(int64_t)1, (int64_t)40}) {
+                std::vector<hqq_tensor> ts;
+                std::vector<void *> mem;
+                for (int i = 0; i < 30; ++i) {
+                    const int64_t lines = 1 + rnd(3000) * scale, other = (int64_t)f[1] * (1 + rnd(40));
+                    const int64_t rows = f[2] == 1 ? lines : other, cols = f[2] == 1 ? other : lines;
+                    // pointers are only recorded, never dereferenced: one small
+                    // aligned block stands in for every buffer
+                    void *p = aligned(256);
+                    mem.push_back(p);
+                    ts.push_back(hqq_tensor{(const uint16_t *)p, rows, cols, (uint32_t *)p, (float *)p, (float *)p});
+                }
+                g_solve.clear();
+                g_seg.clear();
+                CHECK(hqq_quantize_batch(ts.data(), (int)ts.size(), f[0], f[1], f[2], 20, 0.7f, 10.f, 1.01f,
+                                         nullptr) == HQQ_OK);
+                CHECK(g_solve.size() >= 2);
+                check_launches(ts, f[0], f[1], f[2]);
+                for (void *p : mem)
+                    free(p);
             }
-            g_solve.clear();
-            CHECK(hqq_quantize_batch(ts.data(), (int)ts.size(), f[0], f[1], f[2], 20, 0.7f, 10.f, 1.01f, nullptr) ==
-                  HQQ_OK);
-            CHECK(g_solve.size() >= 2);
-            check_launches(ts, f[0], f[1], f[2]);
-            for (void *p : mem)
-                free(p);
-        }
+    }
+    unsetenv("HQQ_SOLVE_MAPPING");
 }
 
 // Streamed solve: the copies cover every row of every tensor exactly once,
@@ -259,6 +292,7 @@ static void test_streamed()
             char *staging = (char *)aligned(staging_bytes);
             g_copies.clear();
             g_solve.clear();
+            g_seg.clear();
             g_event_log.clear();
             g_events = 0;
             g_events_live = 0;

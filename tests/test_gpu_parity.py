@@ -34,6 +34,20 @@ def hq():
     return w
 
 
+def seg_format(nbits, gs, axis):
+    """Formats the solve can also run with several lanes per group (fp16)."""
+    return axis == 1 and nbits != 3 and 32 <= gs <= 128
+
+
+@pytest.fixture(params=["lane", "seg"])
+def mapping(request, monkeypatch):
+    """Force the solve's mapping: one lane per work item, or gs/8 lanes per
+    group (the library picks by launch size; both must give identical
+    results)."""
+    monkeypatch.setenv("HQQ_SOLVE_MAPPING", request.param)
+    return request.param
+
+
 def _dev16(W16: np.ndarray):
     import torch
 
@@ -138,7 +152,9 @@ def _format_cases():
 
 
 @pytest.mark.parametrize("nbits,gs,axis", _format_cases())
-def test_quantize_formats(hq, oracle_mod, nbits, gs, axis):
+def test_quantize_formats(hq, oracle_mod, nbits, gs, axis, mapping):
+    if mapping == "seg" and not seg_format(nbits, gs, axis):
+        pytest.skip("one mapping for this format")
     rng = np.random.RandomState(nbits * 1000 + gs * 2 + axis)
     # several work items per wave plus a ragged last block along the line
     ngroups = 7 if gs <= 64 else 3
@@ -164,8 +180,13 @@ def test_quantize_formats(hq, oracle_mod, nbits, gs, axis):
     (3, 64, 1, 1.0, 0.1, 1.5),
     (4, 32, 0, 2.5, 10.0, 1.01),     # p > 2: no certificate, every residual evaluated
     (4, 64, 1, 0.3, 1.0, 1.01),
+    (2, 32, 1, 0.7, 1000.0, 1.01),   # frozen groups finished two at a time (gs 32)
+    (8, 128, 1, 2.5, 10.0, 1.01),    # two elements per lane in the finish (gs 128)
+    (1, 64, 1, 0.7, 100.0, 1.01),
 ])
-def test_quantize_shrink_paths(hq, oracle_mod, nbits, gs, axis, p, beta0, kappa):
+def test_quantize_shrink_paths(hq, oracle_mod, nbits, gs, axis, p, beta0, kappa, mapping):
+    if mapping == "seg" and not seg_format(nbits, gs, axis):
+        pytest.skip("one mapping for this format")
     rng = np.random.RandomState(int(p * 100) + nbits * 7 + gs + axis)
     shape = (64, gs * 9) if axis == 1 else (gs * 9, 64)
     W16 = random_f16(rng, shape, std=0.05, outlier_frac=0.01)
@@ -175,7 +196,7 @@ def test_quantize_shrink_paths(hq, oracle_mod, nbits, gs, axis, p, beta0, kappa)
     print("shrink path", nbits, gs, axis, p, beta0, st)
 
 
-def test_quantize_edge_values(hq, oracle_mod):
+def test_quantize_edge_values(hq, oracle_mod, mapping):
     rng = np.random.RandomState(7)
     gs = 64
     W = (rng.randn(16, gs * 8) * 0.02).astype(np.float16)
@@ -282,9 +303,11 @@ def test_synth_gpu_generator_matches_numpy():
 
 @pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])
 @pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1), (8, 128, 1)])
-def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters):
+def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters, mapping):
     """Groups that stop before, at and after the point where the solve parks
     unfinished groups for later batches, and long runs, match the oracle."""
+    if mapping == "seg" and not seg_format(nbits, gs, axis):
+        pytest.skip("one mapping for this format")
     rng = np.random.RandomState(iters * 100 + nbits * 10 + gs + axis)
     shape = (96, 1024) if axis == 1 else (1024, 96)
     W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.001)

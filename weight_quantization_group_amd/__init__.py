@@ -30,7 +30,7 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
            "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_ex", "hqq_linear_batch",
-           "hqq_packed_words", "hqq_strerror")
+           "hqq_solve_mapping", "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
 DTYPE_FP16, DTYPE_BF16 = 0, 1
@@ -114,6 +114,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_linear_ex.restype = i32
     L.hqq_linear_batch.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P]
     L.hqq_linear_batch.restype = i32
+    L.hqq_solve_mapping.argtypes = [i32, i32, i32, i32, i64]
+    L.hqq_solve_mapping.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
     L.hqq_packed_words.restype = i64
     L.hqq_strerror.argtypes = [i32]
@@ -124,6 +126,18 @@ def load_library(path: str = LIB_PATH):
 
 def hqq_strerror(status: int) -> str:
     return load_library().hqq_strerror(int(status)).decode()
+
+
+def hqq_solve_mapping(nbits: int, group_size: int, axis: int, wdtype: int, work_items: int) -> int:
+    """MAPPING_LANE or MAPPING_SEG: the solve kernel a launch of work_items
+    work items of this format runs."""
+    m = load_library().hqq_solve_mapping(nbits, group_size, axis, wdtype, work_items)
+    if m < 0:
+        raise HQQError("hqq_solve_mapping", m)
+    return int(m)
+
+
+MAPPING_LANE, MAPPING_SEG = 0, 1
 
 
 def hqq_packed_words(rows: int, cols: int, nbits: int, axis: int) -> int:

@@ -5,6 +5,8 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace {
 
@@ -33,6 +35,30 @@ int check_common(int64_t rows, int64_t cols, int nbits, int group_size, int axis
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 bool finite_pos(float v) { return isfinite(v) && v > 0.0f; }
+
+// HQQ_SOLVE_MAPPING=lane or =seg forces the solve's mapping where the format
+// allows it (tests exercise both on the same inputs); otherwise the size of
+// the launch decides.  0: automatic, 1: one lane per work item, 2: several
+// lanes per group.
+int mapping_override()
+{
+    const char *e = getenv("HQQ_SOLVE_MAPPING");
+    if (!e)
+        return 0;
+    if (strcmp(e, "lane") == 0)
+        return 1;
+    if (strcmp(e, "seg") == 0)
+        return 2;
+    return 0;
+}
+
+// The solve's mapping for a launch of `items` work items of a format that
+// allows both (seg_ok).
+bool use_seg(bool seg_ok, int nbits, int64_t items)
+{
+    const int force = mapping_override();
+    return seg_ok && (force == 2 || (force == 0 && items < hqq::seg_max_items(nbits)));
+}
 
 // Threshold below which the lp shrinkage is provably inactive in every
 // iteration.  The shrink is nonzero iff |x|^(1-pm1) > 1/beta_k, i.e.
@@ -210,6 +236,7 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
     const int C = hqq::codes_per_word(nbits);
     const int64_t lb = hqq::lcm_c(group_size, C);
     const int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+    const bool seg_ok = hqq::seg_format(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16);
     int i = 0;
     while (i < n) {
         // the tensors of this launch, and its work items
@@ -231,11 +258,19 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
             items += d.n_items;
             ++a.n;
         }
-        // work items per lane: deep enough to overlap each item's loads with
-        // the previous item's solve, shallow enough to keep many workgroups
-        int64_t depth = items / (hqq::kSolveBlock * hqq::kTargetBlocks);
+        // the mapping: one lane per work item, or gs / 8 lanes per group for
+        // launches too small to fill the device that way
+        const bool seg = use_seg(seg_ok, nbits, items);
+        // work items per workgroup at depth 1 (one item per lane, or
+        // 512 / gs groups per wave)
+        const int64_t unit = seg ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(group_size)
+                                 : (int64_t)hqq::kSolveBlock;
+        // items per lane (or per wave's group slot): deep enough to overlap
+        // each item's loads with the previous item's solve, shallow enough
+        // to keep many workgroups
+        int64_t depth = items / (unit * hqq::kTargetBlocks);
         a.depth = (int)(depth < 1 ? 1 : depth > hqq::kMaxDepth ? hqq::kMaxDepth : depth);
-        const int64_t per_block = (int64_t)hqq::kSolveBlock * a.depth;
+        const int64_t per_block = unit * a.depth;
         a.blocks = 0;
         int used = 0;
         for (; used < a.n; ++used) {
@@ -247,12 +282,30 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
         }
         a.n = used;
         i += used;
-        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, a,
+        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, seg, a,
                                                (hipStream_t)stream);
         if (e != hipSuccess)
             return HQQ_EHIP;
     }
     return HQQ_OK;
+}
+
+int hqq_solve_mapping(int nbits, int group_size, int axis, int wdtype, int64_t work_items)
+{
+    if (wdtype != HQQ_DTYPE_FP16 && wdtype != HQQ_DTYPE_BF16)
+        return HQQ_EINVAL_DTYPE;
+    if (!hqq::valid_nbits(nbits))
+        return HQQ_EINVAL_NBITS;
+    if (axis != 0 && axis != 1)
+        return HQQ_EINVAL_AXIS;
+    if (group_size != 8 && group_size != 16 && group_size != 32 && group_size != 64 && group_size != 128 &&
+        group_size != 256)
+        return HQQ_EINVAL_GROUP;
+    if (work_items < 0)
+        return HQQ_EINVAL_SHAPE;
+    return use_seg(hqq::seg_format(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16), nbits, work_items)
+               ? HQQ_MAPPING_SEG
+               : HQQ_MAPPING_LANE;
 }
 
 int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int group_size,

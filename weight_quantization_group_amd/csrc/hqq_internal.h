@@ -35,6 +35,24 @@ constexpr int kSolveBlock = 256;
 constexpr int kMaxDepth = 8;
 constexpr int64_t kTargetBlocks = 8192;
 
+// The axis = 1 solve can also spread a group over gs / 8 lanes (8 weights per
+// lane, 512 / gs groups per wave): formats 32 <= gs <= 128, fp16 weights,
+// every code width but 3 bits.  The host takes it for launches of fewer than
+// seg_max_items groups (measured crossovers): below them one lane per group
+// leaves most of the device idle and a wave waits for the slowest of its 64
+// groups.  1-bit groups often need the exact finish, which runs up to
+// 64 / gs groups at a time per wave: many more waves win there at every size
+// measured.
+constexpr bool seg_format(int nbits, int gs, int axis, bool bf16)
+{
+    return axis == 1 && !bf16 && nbits != 3 && gs >= 32 && gs <= 128;
+}
+constexpr int seg_groups_per_wave(int gs) { return 512 / gs; }
+constexpr int64_t seg_max_items(int nbits)
+{
+    return nbits == 1 ? (int64_t(1) << 23) : nbits == 8 ? (int64_t(1) << 16) : int64_t(320) << 10;
+}
+
 // Arguments of the solve kernels (passed by value as the kernel argument).
 struct SolveArgs {
     int iters;
@@ -99,7 +117,9 @@ int check_params(int iters, float p, float beta0, float kappa);
 int check_tensor(const ::hqq_tensor &t, int nbits, int group_size, int axis);
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, const SolveArgs &a, hipStream_t s);
+// seg: the several-lanes-per-group kernel (a format seg_format accepts)
+hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, bool seg, const SolveArgs &a,
+                        hipStream_t s);
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);

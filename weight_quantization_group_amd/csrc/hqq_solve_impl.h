@@ -347,16 +347,192 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
     }
 }
 
-// Finish the frozen groups of the wave (every lane of the wave takes part).
-// frozen: this lane's group is frozen; on return its z is the final zero.
+// Sum over the SEG lanes of a compact group (aligned blocks of 4, 8 or 16
+// lanes) with DPP row permutations; every lane gets the total.
+template <int SEG>
+__device__ __forceinline__ int seg_sum(int v)
+{
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
+    if constexpr (SEG >= 8)
+        v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);     // row_half_mirror
+    if constexpr (SEG >= 16)
+        v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);     // row_mirror
+    return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
+// The same block sums in fp64: each level adds the sibling block's sum, as
+// a butterfly does (fp64 addition commutes, so the result is the pairwise
+// tree's, bit for bit).
+template <int SEG>
+__device__ __forceinline__ double seg_sum_f64(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    if constexpr (SEG >= 8)
+        v += dpp_f64<0x141>(v);
+    if constexpr (SEG >= 16)
+        v += dpp_f64<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
+// Finish the nb frozen groups staged in an area with fields w (B groups x GS
+// 16-bit weights) and g (their FrozenGroup states): one lane per element (EPL
+// consecutive elements per lane), every remaining iteration with the exact
+// residual and shrink; each group's final zero is written back to g[slot].z.
+template <int NB, int GS, bool BF, typename A>
+__device__ __forceinline__ void finish_staged(const SolveArgs &a, A &wf, int nb)
+{
+    using F = Finish<GS>;
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    constexpr double INV_GS = 1.0 / GS;
+    const uint32_t lane = __lane_id();
+    const int slot = (int)lane / F::SEG;
+    const int pos = (int)lane % F::SEG;
+    const bool ok = slot < nb;
+    const FrozenGroup st = wf.g[ok ? slot : 0];
+    float we[F::EPL];
+#pragma unroll
+    for (int k = 0; k < F::EPL; ++k)
+        we[k] = widen<BF>(wf.w[(ok ? slot : 0) * GS + pos * F::EPL + k]);
+    const float gs_s = st.s;
+    const float thr_s = a.thr * gs_s;
+    const float lim = a.thr_m * gs_s;
+    float gz = st.z, gbeta = st.beta;
+    int it = ok ? st.it : a.iters;
+    while (__any(it < a.iters)) {
+        const bool act = it < a.iters;
+        // certificate of the group for the current zero
+        const float tmin = __builtin_fmaf(st.mn, gs_s, gz);
+        const float tmax = __builtin_fmaf(st.mx, gs_s, gz);
+        const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+        const bool est_ok = __builtin_fmaf(st.amag, gs_s, fabsf(gz)) + QMAX <= lim;
+        const bool cand = !(est_ok && bound <= thr_s);
+        uint32_t ck[F::EPL];
+        double te[F::EPL];
+#pragma unroll
+        for (int k = 0; k < F::EPL; ++k) {
+            const float t = __builtin_fmaf(we[k], gs_s, gz);
+            const float qk = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, QMAX);
+            ck[k] = (uint32_t)qk;
+            float e = 0.0f;
+            if (act && cand && !(est_ok && fabsf(t - qk) <= thr_s)) {
+                const float wr = (qk - gz) / gs_s;
+                const float x = we[k] - wr;
+                const float ax = fabsf(x);
+                if (ax > a.thr) {
+                    const float pw = pow_rounded(ax, a.pm1);
+                    const float v = ax - pw / gbeta;
+                    if (v > 0.0f)
+                        e = copysignf(v, x);
+                }
+            }
+            te[k] = (double)e;
+        }
+        // in-lane levels of W_e's pairwise tree
+#pragma unroll
+        for (int st2 = 1; st2 < F::EPL; st2 *= 2)
+#pragma unroll
+            for (int k = 0; k + st2 < F::EPL; k += 2 * st2)
+                te[k] += te[k + st2];
+        double se = te[0];
+        int sqi;
+        if constexpr (F::EPL > 2) {
+            // gs = 256 (four elements per lane, every register in use): the
+            // butterfly through LDS for both sums
+            float sf = 0.0f;
+#pragma unroll
+            for (int k = 0; k < F::EPL; ++k)
+                sf += (float)ck[k];
+#pragma unroll
+            for (int m = 1; m < F::SEG; m *= 2) {
+                sf += __shfl_xor(sf, m);
+                se += __shfl_xor(se, m);
+            }
+            sqi = (int)sf;
+        } else if constexpr (F::SEG == 64) {
+            // one group per pass.  sum W_q: the codes are integers (exact in
+            // any order), counted bit by bit with ballots.  sum W_e: where at
+            // most two lanes hold a nonzero partial sum, the tree's result is
+            // their sum (every other term is an exact +0), read with
+            // readlane; otherwise the butterfly.
+            sqi = 0;
+#pragma unroll
+            for (int bit = 0; bit < NB; ++bit) {
+#pragma unroll
+                for (int k = 0; k < F::EPL; ++k)
+                    sqi += __popcll(__ballot((ck[k] >> bit) & 1u)) << bit;
+            }
+            const uint64_t nz = __ballot(se != 0.0);
+            if (__popcll(nz) <= 2) {
+                double v = 0.0;
+                if (nz) {
+                    v = readlane_f64(se, __builtin_ctzll(nz));
+                    if (nz & (nz - 1ull))
+                        v = v + readlane_f64(se, 63 - __builtin_clzll(nz));
+                }
+                se = v;
+            } else {
+                se = seg_sum_f64<16>(se);
+                se += __shfl_xor(se, 16);
+                se += __shfl_xor(se, 32);
+            }
+        } else {
+            // the butterfly across the group's lanes, by DPP within rows of
+            // 16 lanes (and one exchange between rows at gs = 32)
+            int cs = 0;
+#pragma unroll
+            for (int k = 0; k < F::EPL; ++k)
+                cs += (int)ck[k];
+            constexpr int R = F::SEG < 16 ? F::SEG : 16;
+            sqi = seg_sum<R>(cs);
+            se = seg_sum_f64<R>(se);
+            if constexpr (F::SEG == 32) {
+                sqi += __shfl_xor(sqi, 16);
+                se += __shfl_xor(se, 16);
+            }
+        }
+        const float sq = (float)sqi;
+        const float zn = (float)(((double)sq - (double)gs_s * (st.sw - se)) * INV_GS);
+        if (act) {
+            // where the certificate holds every W_e is 0 and the update is
+            // the fast one: a returned zero is then a fixed point
+            const bool fixed = !cand && zn == gz;
+            gz = zn;
+            gbeta = gbeta * a.kappa;
+            it = fixed ? a.iters : it + 1;
+        }
+    }
+    if (ok && pos == 0)
+        wf.g[slot].z = gz;
+    wave_sync();
+}
+
+// The frozen lanes' groups (one group per lane) through finish_staged, up to
+// Finish::B at a time in lane order; z returns each group's final zero.
 template <int NB, int GS, bool BF>
 __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS> &wf, bool frozen,
                                               const float (&w)[GS], float s, float &z, float beta,
                                               float mn, float mx, float amag, int it_f, double sw)
 {
     using F = Finish<GS>;
-    constexpr float QMAX = (float)((1 << NB) - 1);
-    constexpr double INV_GS = 1.0 / GS;
     const uint32_t lane = __lane_id();
     const uint64_t below = (1ull << lane) - 1ull;
     uint64_t pending = __ballot(frozen);
@@ -379,76 +555,7 @@ __device__ __forceinline__ void finish_frozen(const SolveArgs &a, WaveFinish<GS>
             wf.g[slot] = FrozenGroup{s, z, beta, mn, mx, amag, it_f, 0, sw};
         }
         wave_sync();
-
-        // one lane per element (EPL consecutive elements per lane)
-        const int slot = (int)lane / F::SEG;
-        const int pos = (int)lane % F::SEG;
-        const bool ok = slot < nb;
-        const FrozenGroup st = wf.g[ok ? slot : 0];
-        float we[F::EPL];
-#pragma unroll
-        for (int k = 0; k < F::EPL; ++k)
-            we[k] = widen<BF>(wf.w[(ok ? slot : 0) * GS + pos * F::EPL + k]);
-        const float gs_s = st.s;
-        const float thr_s = a.thr * gs_s;
-        const float lim = a.thr_m * gs_s;
-        float gz = st.z, gbeta = st.beta;
-        int it = ok ? st.it : a.iters;
-        while (__any(it < a.iters)) {
-            const bool act = it < a.iters;
-            // certificate of the group for the current zero
-            const float tmin = __builtin_fmaf(st.mn, gs_s, gz);
-            const float tmax = __builtin_fmaf(st.mx, gs_s, gz);
-            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
-            const bool est_ok = __builtin_fmaf(st.amag, gs_s, fabsf(gz)) + QMAX <= lim;
-            const bool cand = !(est_ok && bound <= thr_s);
-            float sq = 0.0f;
-            double te[F::EPL];
-#pragma unroll
-            for (int k = 0; k < F::EPL; ++k) {
-                const float t = __builtin_fmaf(we[k], gs_s, gz);
-                const float qk = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, QMAX);
-                sq += qk;
-                float e = 0.0f;
-                if (act && cand && !(est_ok && fabsf(t - qk) <= thr_s)) {
-                    const float wr = (qk - gz) / gs_s;
-                    const float x = we[k] - wr;
-                    const float ax = fabsf(x);
-                    if (ax > a.thr) {
-                        const float pw = pow_rounded(ax, a.pm1);
-                        const float v = ax - pw / gbeta;
-                        if (v > 0.0f)
-                            e = copysignf(v, x);
-                    }
-                }
-                te[k] = (double)e;
-            }
-            // sum W_e: in-lane levels of the pairwise tree, then the butterfly
-            // across the group's lanes (each level adds the sibling block)
-#pragma unroll
-            for (int st2 = 1; st2 < F::EPL; st2 *= 2)
-#pragma unroll
-                for (int k = 0; k + st2 < F::EPL; k += 2 * st2)
-                    te[k] += te[k + st2];
-            double se = te[0];
-#pragma unroll
-            for (int m = 1; m < F::SEG; m *= 2) {
-                sq += __shfl_xor(sq, m);
-                se += __shfl_xor(se, m);
-            }
-            const float zn = (float)(((double)sq - (double)gs_s * (st.sw - se)) * INV_GS);
-            if (act) {
-                // where the certificate holds every W_e is 0 and the update is
-                // the fast one: a returned zero is then a fixed point
-                const bool fixed = !cand && zn == gz;
-                gz = zn;
-                gbeta = gbeta * a.kappa;
-                it = fixed ? a.iters : it + 1;
-            }
-        }
-        if (ok && pos == 0)
-            wf.g[slot].z = gz;
-        wave_sync();
+        finish_staged<NB, GS, BF>(a, wf, nb);
         if (mine)
             z = wf.g[__popcll(take & below)].z;
         wave_sync();
@@ -505,20 +612,6 @@ struct LaneRun {
     bool run;       // still iterating
     bool frozen;    // certificate failed at iteration it (beta is its beta)
 };
-
-// Sum over the SEG lanes of a compact group (aligned blocks of 4, 8 or 16
-// lanes) with DPP row permutations; every lane gets the total.
-template <int SEG>
-__device__ __forceinline__ int seg_sum(int v)
-{
-    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
-    if constexpr (SEG >= 8)
-        v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);     // row_half_mirror
-    if constexpr (SEG >= 16)
-        v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);     // row_mirror
-    return v;
-}
 
 // Compact mode: the running lanes' groups (at most B) move to LDS, SEG lanes
 // per group iterate them with the same update as the fast loop (codes by
@@ -999,6 +1092,14 @@ void solve_kernel(SolveArgs a)
     }
 }
 
+}  // namespace
+}  // namespace hqq
+
+#include "hqq_solve_seg.h"
+
+namespace hqq {
+namespace {
+
 template <int NB, int GS, int AXIS, bool BF>
 void launch_one(dim3 grid, dim3 block, const SolveArgs &a, hipStream_t st)
 {
@@ -1027,8 +1128,22 @@ hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 // launcher of the NB-bit solve kernels for fp16 (BF = false) or bf16 inputs
 // (defined in hqq_solve_b<NB>.hip and hqq_solve_b<NB>_bf16.hip)
 template <int NB, bool BF>
-hipError_t launch_solve_nb(int group_size, int axis, const SolveArgs &a, hipStream_t st)
+hipError_t launch_solve_nb(int group_size, int axis, bool seg, const SolveArgs &a, hipStream_t st)
 {
+    if (seg) {
+        if constexpr (NB != 3 && !BF) {
+            const dim3 block(kBlock);
+            const dim3 grid((unsigned)a.blocks);
+            switch (group_size) {
+            case 32: hipLaunchKernelGGL((solve_seg_kernel<NB, 32>), grid, block, 0, st, a); break;
+            case 64: hipLaunchKernelGGL((solve_seg_kernel<NB, 64>), grid, block, 0, st, a); break;
+            case 128: hipLaunchKernelGGL((solve_seg_kernel<NB, 128>), grid, block, 0, st, a); break;
+            default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     return axis == 1 ? launch_gs<NB, 1, BF>(group_size, a, st) : launch_gs<NB, 0, BF>(group_size, a, st);
 }
 

@@ -1,0 +1,283 @@
+// hqq_solve_seg.h -- the axis = 1 solve with several lanes per group, for
+// launches too small to fill the device with one lane per group.
+//
+// Included by hqq_solve_impl.h after the lane-per-group kernel, whose
+// helpers it uses (widen8, seg_sum, FrozenGroup, Finish, finish_staged,
+// wave_sync, Item).  Formats: axis = 1, 32 <= gs <= 128, fp16 weights, every
+// code width whose words tile a group (all but 3 bits).
+//
+// Layout: SEG = gs / 8 lanes hold a group, 8 consecutive weights each, and a
+// wave holds B = 64 / SEG consecutive groups of the tensor.  Along axis 1 the
+// groups of a tensor follow each other in memory (cols is a multiple of gs),
+// so a wave's groups are 1024 contiguous bytes: one 16-byte load per lane,
+// issued a step ahead.  The per-group quantities of the HQQ solve (lnwmold.com
+// HQQ guide, section 2.1: alternating W_q / W_e / zero updates; section 2.2:
+// nbits, group_size, axis) are formed across the group's lanes with DPP: min
+// and max, the exact fp64 sum of the weights (every partial sum of at most 128
+// fp16 values is exact in fp64, so the lane order cannot change it), and the
+// sum of the codes (integers).  The certificate, the fixed-point stop and the
+// exact finish of frozen groups are the lane-per-group kernel's, so every
+// output is identical bit for bit.  The wave runs until its slowest of B
+// groups is done instead of its slowest of 64.
+#pragma once
+
+namespace hqq {
+namespace {
+
+template <int GS>
+struct Seg {
+    static constexpr int SEG = GS / 8;   // lanes per group
+    static constexpr int B = 64 / SEG;   // groups per wave
+};
+
+template <int GS>
+struct SegFinish {
+    alignas(16) uint16_t w[64 * Finish<GS>::EPL];   // staged frozen groups (fp16 bits)
+    FrozenGroup g[Finish<GS>::B];
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Reductions over the SEG lanes of a group (aligned blocks of 4, 8 or 16
+// lanes): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror; every lane of the block gets the result.  All 64 lanes must be
+// active.
+template <int SEG>
+__device__ __forceinline__ float seg_min(float v)
+{
+    v = fminf(v, dpp_f32<0xB1>(v));
+    v = fminf(v, dpp_f32<0x4E>(v));
+    if constexpr (SEG >= 8)
+        v = fminf(v, dpp_f32<0x141>(v));
+    if constexpr (SEG >= 16)
+        v = fminf(v, dpp_f32<0x140>(v));
+    return v;
+}
+
+template <int SEG>
+__device__ __forceinline__ float seg_max(float v)
+{
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    if constexpr (SEG >= 8)
+        v = fmaxf(v, dpp_f32<0x141>(v));
+    if constexpr (SEG >= 16)
+        v = fmaxf(v, dpp_f32<0x140>(v));
+    return v;
+}
+
+// Eight clamped codes of a lane (bytes of d0: codes 0-3, d1: codes 4-7,
+// each <= qmax) folded into NB-bit fields, LSB first: 8 bits: the two words
+// as they are; 4 bits: one word; 2 bits: the low 16 bits; 1 bit: the low 8.
+template <int NB>
+__device__ __forceinline__ uint32_t fold_codes(uint32_t d0, uint32_t d1)
+{
+    if constexpr (NB == 4) {
+        const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
+        const uint32_t x1 = d1 | (d1 >> 4);
+        return __builtin_amdgcn_perm(x1, x0, 0x06040200u);
+    } else if constexpr (NB == 2) {
+        uint32_t x0 = d0 | (d0 >> 6);         // bits 0-3: c0 c1, bits 16-19: c2 c3
+        uint32_t x1 = d1 | (d1 >> 6);
+        x0 = (x0 | (x0 >> 12)) & 0xFFu;       // bits 0-7: c0 c1 c2 c3
+        x1 = (x1 | (x1 >> 12)) & 0xFFu;
+        return x0 | (x1 << 8);
+    } else {
+        static_assert(NB == 1, "8-bit codes are stored as bytes");
+        uint32_t x0 = d0 | (d0 >> 7);         // bits 0-1: c0 c1, bits 16-17: c2 c3
+        uint32_t x1 = d1 | (d1 >> 7);
+        x0 = (x0 | (x0 >> 14)) & 0xFu;        // bits 0-3: c0 c1 c2 c3
+        x1 = (x1 | (x1 >> 14)) & 0xFu;
+        return x0 | (x1 << 4);
+    }
+}
+
+// Occupancy target: the largest at which the kernel needs no scratch (the
+// out-of-line power of the frozen finish sets the register count; a spill
+// would make the wave wait for the next step's load at once).
+constexpr int seg_waves_per_simd(int gs) { return gs == 64 ? 6 : 5; }
+
+// A workgroup owns kWaves * B * depth consecutive groups of one tensor, its
+// waves B * depth each; a step of a wave solves B groups.
+template <int NB, int GS>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(seg_waves_per_simd(GS))))
+void solve_seg_kernel(SolveArgs a)
+{
+    using S = Seg<GS>;
+    using F = Finish<GS>;
+    constexpr int C = codes_per_word(NB);
+    constexpr float QMAX = (float)((1 << NB) - 1);
+    constexpr uint32_t QB = (uint32_t)((1 << NB) - 1) * 0x01010101u;
+    constexpr double INV_GS = 1.0 / GS;
+    static_assert(GS >= 32 && GS <= 128 && GS % C == 0 && NB != 3, "format of the multi-lane kernel");
+    __shared__ SegFinish<GS> finish[kWaves];
+
+    int ti = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxBatch; ++j)
+        ti += (j < a.n && (int64_t)blockIdx.x >= a.block0[j]) ? 1 : 0;
+    ti = __builtin_amdgcn_readfirstlane(ti);
+    const SolveTensor &T = a.t[ti];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    SegFinish<GS> &wf = finish[wave];
+    const int lane = (int)(threadIdx.x & 63);
+    const int b = lane / S::SEG;     // the lane's group in the step
+    const int j = lane % S::SEG;     // its 8 weights: 8j .. 8j + 7 of the group
+    const int64_t per_wave = (int64_t)S::B * a.depth;
+    const int64_t g0 = ((int64_t)blockIdx.x - a.block0[ti]) * kWaves * per_wave + wave * per_wave;
+    const int64_t gend = g0 + per_wave < T.n_items ? g0 + per_wave : T.n_items;
+    if (g0 >= gend)
+        return;
+
+    // lanes past the tensor's last group read that group (in bounds) and
+    // store nothing
+    auto load = [&](int64_t gbase) {
+        int64_t gi = gbase + b;
+        gi = gi < T.n_items ? gi : T.n_items - 1;
+        return *reinterpret_cast<const u32x4 *>(T.W + gi * GS + 8 * j);
+    };
+    u32x4 next = load(g0);
+    for (int64_t gb = g0; gb < gend; gb += S::B) {
+        const u32x4 raw = next;
+        if (gb + S::B < gend)
+            next = load(gb + S::B);
+        const int64_t gi = gb + b;
+        const bool valid = gi < gend;
+        float we[8];
+        widen8<false>(raw, we);
+
+        // set-up: the lane-per-group kernel's min, max, scale, zero and sum
+        float mn = we[0], mx = we[0];
+        double sw = (double)we[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            mn = fminf(mn, we[k]);
+            mx = fmaxf(mx, we[k]);
+            sw += (double)we[k];
+        }
+        mn = seg_min<S::SEG>(mn);
+        mx = seg_max<S::SEG>(mx);
+        sw = seg_sum_f64<S::SEG>(sw);
+        const float rng = mx - mn;
+        float s, z;
+        if (rng == 0.0f) {
+            s = 1.0f;
+            z = -mn;
+        } else {
+            s = QMAX / rng;
+            z = -(mn * s);
+        }
+        const float amag = fmaxf(fabsf(mn), fabsf(mx));
+        const float thr_s = a.thr * s;
+        const float lim = a.thr_m * s;
+        const double ssw = (double)s * sw;
+
+        // iterations under the certificate, as in the lane-per-group kernel
+        float beta = a.beta0;
+        int it = 0;
+        bool run = valid && a.iters > 0, frozen = false;
+        while (__any(run)) {
+            if (run) {
+                const float tmin = __builtin_fmaf(mn, s, z);
+                const float tmax = __builtin_fmaf(mx, s, z);
+                const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+                const bool est_ok = __builtin_fmaf(amag, s, fabsf(z)) + QMAX <= lim;
+                if (!(est_ok && bound <= thr_s)) {
+                    run = false;
+                    frozen = true;
+                }
+            }
+            // every lane computes (the DPP sums read whole blocks of lanes)
+            uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[0], s, z), 0, 0u);
+            uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4], s, z), 0, 0u);
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[k], s, z), k, d0);
+                d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 + k], s, z), k, d1);
+            }
+            const uint32_t c = __builtin_amdgcn_sad_u8(d1, 0u, __builtin_amdgcn_sad_u8(d0, 0u, 0u));
+            const uint32_t q = __builtin_amdgcn_sad_u8(d1, QB, __builtin_amdgcn_sad_u8(d0, QB, 0u));
+            const int tot = seg_sum<S::SEG>((int)c - (int)q);
+            const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
+            const float zn = (float)(((double)sq - ssw) * INV_GS);
+            if (run) {
+                it = zn == z ? a.iters : it + 1;
+                beta = beta * a.kappa;
+                z = zn;
+                if (it >= a.iters)
+                    run = false;
+            }
+        }
+
+        // frozen groups: staged by their lanes, finished F::B at a time with
+        // the exact residual and shrink
+        {
+            const int lead = lane - j;   // the group's first lane
+            uint64_t pending = __ballot(frozen && j == 0);
+            while (pending) {
+                uint64_t take = 0;
+#pragma unroll
+                for (int k = 0; k < F::B; ++k) {
+                    if (pending & ~take)
+                        take |= (pending & ~take) & (~(pending & ~take) + 1ull);
+                }
+                pending &= ~take;
+                const int nb = __popcll(take);
+                const bool mine = (take >> lead) & 1ull;
+                const int slot = __popcll(take & ((1ull << lead) - 1ull));
+                if (mine) {
+                    *reinterpret_cast<u32x4 *>(&wf.w[slot * GS + 8 * j]) = raw;
+                    if (j == 0)
+                        wf.g[slot] = FrozenGroup{s, z, beta, mn, mx, amag, it, 0, sw};
+                }
+                wave_sync();
+                finish_staged<NB, GS, false>(a, wf, nb);
+                if (mine)
+                    z = wf.g[slot].z;
+                wave_sync();
+            }
+        }
+
+        // final codes at the final zero, packed and stored
+        uint32_t d0 = 0, d1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(__builtin_fmaf(we[k], s, z), 0.0f, QMAX), k, d0);
+            d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(__builtin_fmaf(we[4 + k], s, z), 0.0f, QMAX), k,
+                                                d1);
+        }
+        uint32_t *gw = T.packed + gi * (GS / C);   // the group's words (axis 1: groups are contiguous)
+        if constexpr (NB == 8) {
+            if (valid)
+                *reinterpret_cast<uint2 *>(gw + 2 * j) = uint2{d0, d1};
+        } else if constexpr (NB == 4) {
+            if (valid)
+                gw[j] = fold_codes<4>(d0, d1);
+        } else if constexpr (NB == 2) {
+            // a word holds the 16 codes of lanes j, j + 1 (j even)
+            const uint32_t h = fold_codes<2>(d0, d1);
+            const uint32_t w = h | ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xB1, 0xF, 0xF, false) << 16);
+            if (valid && (j & 1) == 0)
+                gw[j >> 1] = w;
+        } else {
+            // a word holds the 32 codes of lanes j .. j + 3 (j % 4 == 0)
+            const uint32_t h = fold_codes<1>(d0, d1);
+            const uint32_t w = h | ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x55, 0xF, 0xF, false) << 8) |
+                               ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xAA, 0xF, 0xF, false) << 16) |
+                               ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xFF, 0xF, 0xF, false) << 24);
+            if (valid && (j & 3) == 0)
+                gw[j >> 2] = w;
+        }
+        if (valid && j == 0) {
+            T.scale[gi] = s;
+            T.zero[gi] = z;
+        }
+    }
+}
+
+}  // namespace
+}  // namespace hqq
