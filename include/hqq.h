@@ -83,6 +83,7 @@ extern "C" {
 #define HQQ_EINVAL_PARAM (-6) /* iters < 0, or p, beta0, kappa not finite and > 0    */
 #define HQQ_EHIP (-7)         /* a HIP launch failed                                  */
 #define HQQ_EINVAL_DTYPE (-8) /* dtype not HQQ_DTYPE_FP16 or HQQ_DTYPE_BF16           */
+#define HQQ_ESCRATCH (-9)     /* a row block too large for the static staging array   */
 
 /* Element types of 16-bit weight / dequantized tensors (the pages load models
  * in fp16 or bf16 and set compute_dtype to either: devpress.csdn.net tutorial
@@ -186,6 +187,29 @@ HQQ_API int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n,
                                   int iters, float p, float beta0, float kappa,
                                   void *staging, int64_t staging_bytes,
                                   void *copy_stream, void *compute_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * hqq_quantize_streamed through the library's own staging buffer instead of
+ * a caller's.  The buffer is a static device array of
+ * HQQ_STATIC_STAGING_BYTES on each device the library runs on, held until the
+ * process ends; at the first call on a device (with it current) the library
+ * looks up the array's address there and creates five HIP events, which it
+ * keeps and reuses.  No call allocates device memory.  Every call on a device
+ * shares that device's array and events, which keep the last call's contents
+ * (nothing needs to start at zero: each byte a solve reads was copied in by
+ * the same call): calls that overlap on one device race, so a caller orders
+ * them (one compute stream, or the previous call's compute stream completed
+ * or waited on).  The first copies wait for the work enqueued on
+ * compute_stream before the call, as in hqq_quantize_streamed.  A tensor
+ * whose block unit (see hqq_quantize_streamed) exceeds half the array
+ * returns HQQ_ESCRATCH before anything is enqueued; other arguments and
+ * results as for hqq_quantize_streamed. */
+#define HQQ_STATIC_STAGING_BYTES ((int64_t)64 << 20)
+HQQ_API int hqq_quantize_streamed_static(const hqq_host_tensor *tensors, int n,
+                                         int nbits, int group_size, int axis,
+                                         int iters, float p, float beta0, float kappa,
+                                         void *copy_stream, void *compute_stream);
 
 /* Dequantize: W_hat = fp16_round_half_even((W_q - zero) / scale) with an
  * IEEE fp32 subtraction and division (lnwmold.com HQQ guide section 3.2,

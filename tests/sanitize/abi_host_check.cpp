@@ -78,6 +78,20 @@ hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned)
     g_event_log.push_back(2);
     return hipSuccess;
 }
+static const void *g_symbol = nullptr;   // the static staging array's (host) address
+static int g_symbol_lookups = 0;
+hipError_t hipGetDevice(int *d)
+{
+    *d = 0;
+    return hipSuccess;
+}
+hipError_t hipGetSymbolAddress(void **p, const void *symbol)
+{
+    ++g_symbol_lookups;
+    g_symbol = symbol;
+    *p = const_cast<void *>(symbol);
+    return hipSuccess;
+}
 hipError_t hipMemcpyAsync(void *dst, const void *src, size_t bytes, hipMemcpyKind, hipStream_t)
 {
     g_copies.push_back(Copy{(char *)dst, (const char *)src, bytes});
@@ -355,12 +369,62 @@ static void test_streamed()
     free(small);
 }
 
+// The no-allocation streamed entry point: the static array's address is
+// looked up once and its events created once (five, never released); the
+// copies of two calls in a row (the second smaller) land inside one half of
+// the array and cover every row once; a row block larger than half the array
+// is refused with HQQ_ESCRATCH before anything is enqueued.
+static void test_streamed_static()
+{
+    g_events = 0;
+    g_events_live = 0;
+    g_symbol_lookups = 0;
+    const int64_t half = (HQQ_STATIC_STAGING_BYTES / 2) / 256 * 256;
+    for (int call = 0; call < 2; ++call) {
+        const int64_t rows = call == 0 ? 5000 : 700, cols = 4096;
+        uint16_t *h = (uint16_t *)aligned(rows * cols * 2);
+        hqq_host_tensor t{h, rows, cols, (uint32_t *)aligned(256), (float *)aligned(256), (float *)aligned(256)};
+        g_copies.clear();
+        g_solve.clear();
+        g_seg.clear();
+        CHECK(hqq_quantize_streamed_static(&t, 1, 4, 64, 1, 20, 0.7f, 10.f, 1.01f, (void *)1, (void *)2) ==
+              HQQ_OK);
+        CHECK(g_symbol_lookups == 1 && g_events == 5 && g_events_live == 5);
+        int64_t total = 0;
+        for (const Copy &c : g_copies) {
+            const int64_t off = c.dst - (const char *)g_symbol;
+            CHECK(off >= 0 && off + (int64_t)c.bytes <= 2 * half);
+            CHECK((off < half) == (off + (int64_t)c.bytes <= half));
+            total += (int64_t)c.bytes;
+        }
+        CHECK(total == rows * cols * 2);
+        CHECK(!g_solve.empty());
+        free(h);
+        free(t.packed);
+        free(t.scale);
+        free(t.zero);
+    }
+    // a 3-bit axis-0 row block (320 rows) of 65536 columns is 40 MiB
+    uint16_t dummy[8];
+    hqq_host_tensor big{dummy, 320, 65536, (uint32_t *)aligned(256), (float *)aligned(256), (float *)aligned(256)};
+    g_copies.clear();
+    g_solve.clear();
+    CHECK(hqq_quantize_streamed_static(&big, 1, 3, 64, 0, 20, 0.7f, 10.f, 1.01f, (void *)1, (void *)2) ==
+          HQQ_ESCRATCH);
+    CHECK(g_copies.empty() && g_solve.empty() && g_events == 5);
+    CHECK(strcmp(hqq_strerror(HQQ_ESCRATCH), "unknown status") != 0);
+    free(big.packed);
+    free(big.scale);
+    free(big.zero);
+}
+
 int main()
 {
     test_validation();
     test_certificate();
     test_batches();
     test_streamed();
+    test_streamed_static();
     if (g_fail) {
         fprintf(stderr, "%d checks failed\n", g_fail);
         return 1;

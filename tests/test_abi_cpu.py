@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hqq.h")
 LIB = os.path.join(ROOT, "weight_quantization_group_amd", "libhqq.so")
 
-E = dict(OK=0, NBITS=-1, AXIS=-2, GROUP=-3, SHAPE=-4, PTR=-5, PARAM=-6, HIP=-7, DTYPE=-8)
+E = dict(OK=0, NBITS=-1, AXIS=-2, GROUP=-3, SHAPE=-4, PTR=-5, PARAM=-6, HIP=-7, DTYPE=-8, SCRATCH=-9)
 
 
 def _declared():
@@ -31,7 +31,8 @@ def lib():
 def test_header_codes_match():
     text = open(HEADER).read()
     for name, val in E.items():
-        key = "HQQ_OK" if name == "OK" else ("HQQ_EHIP" if name == "HIP" else f"HQQ_EINVAL_{name}")
+        key = ("HQQ_OK" if name == "OK" else "HQQ_EHIP" if name == "HIP" else
+               "HQQ_ESCRATCH" if name == "SCRATCH" else f"HQQ_EINVAL_{name}")
         m = re.search(rf"#define {key} \(?(-?\d+)\)?", text)
         assert m and int(m.group(1)) == val, key
 
@@ -56,7 +57,8 @@ def test_header_compiles_cleanly(lang, compiler, tmp_path):
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
     assert declared == sorted(["hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex",
-                               "hqq_quantize_streamed", "hqq_dequantize", "hqq_dequantize_ex",
+                               "hqq_quantize_streamed", "hqq_quantize_streamed_static",
+                               "hqq_dequantize", "hqq_dequantize_ex",
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
                                "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
                                "hqq_linear_ex", "hqq_linear_batch", "hqq_solve_mapping", "hqq_packed_words",
@@ -238,6 +240,34 @@ def test_streamed_rejects(lib):
     # ... or lcm(gs, codes per word) rows (axis 0, 3-bit g64: 320 rows of 256 B)
     big = w.HqqHostTensor(host, 640, 128, 0x1000, 0x2000, 0x3000)
     assert call([big], nbits=3, axis=0, staging_bytes=2 * 320 * 256 - 512) == E["SHAPE"]
+
+
+def test_streamed_static_rejects(lib):
+    """The no-allocation streamed entry point checks every argument before
+    any HIP call (these run without a GPU); a row block larger than half the
+    static staging array is HQQ_ESCRATCH."""
+    import weight_quantization_group_amd as w
+
+    def call(tensors, n=None, nbits=4, gs=64, axis=1, iters=20):
+        arr = (w.HqqHostTensor * max(len(tensors), 1))(*tensors)
+        return lib.hqq_quantize_streamed_static(ctypes.cast(arr, ctypes.c_void_p),
+                                                len(tensors) if n is None else n, nbits, gs, axis, iters,
+                                                0.7, 10.0, 1.01, None, None)
+
+    host = 0x7000
+    ok = w.HqqHostTensor(host, 64, 128, 0x1000, 0x2000, 0x3000)
+    assert call([ok], n=-1) == E["SHAPE"]
+    assert call([], n=0) == E["OK"]
+    assert call([ok], iters=-1) == E["PARAM"]
+    assert call([w.HqqHostTensor(0, 64, 128, 0x1000, 0x2000, 0x3000)]) == E["PTR"]
+    assert call([w.HqqHostTensor(host, 64, 128, 0x1004, 0x2000, 0x3000)]) == E["PTR"]
+    assert call([ok], nbits=5) == E["NBITS"]
+    assert call([w.HqqHostTensor(host, 64, 100, 0x1000, 0x2000, 0x3000)]) == E["GROUP"]
+    # 3-bit axis 0: a block unit is 320 rows; at 65536 columns that is 40 MiB,
+    # more than half of the 64 MiB array
+    big = w.HqqHostTensor(host, 320, 65536, 0x1000, 0x2000, 0x3000)
+    assert call([big], nbits=3, axis=0) == E["SCRATCH"]
+    assert w.STATIC_STAGING_BYTES == 64 << 20
 
 
 def test_dtype_rejects(lib):

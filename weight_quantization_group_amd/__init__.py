@@ -28,6 +28,7 @@ P_DEFAULT, BETA0_DEFAULT, KAPPA_DEFAULT, ITERS_DEFAULT = 0.7, 10.0, 1.01, 20
 
 # exported symbols, in include/hqq.h order
 EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_quantize_streamed",
+           "hqq_quantize_streamed_static",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
            "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_ex", "hqq_linear_batch",
            "hqq_solve_mapping", "hqq_packed_words", "hqq_strerror")
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_unpack.restype = i32
     L.hqq_quantize_streamed.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P, i64, P, P]
     L.hqq_quantize_streamed.restype = i32
+    L.hqq_quantize_streamed_static.argtypes = [P, i32, i32, i32, i32, i32, f32, f32, f32, P, P]
+    L.hqq_quantize_streamed_static.restype = i32
     L.hqq_quantize_meta.argtypes = [P, i64, i32, P, P, P, P]
     L.hqq_quantize_meta.restype = i32
     L.hqq_dequantize_meta.argtypes = [P, P, P, i64, i32, P, P]
@@ -405,6 +408,42 @@ def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging
     # completes: keep torch's allocator from handing it out earlier
     staging.record_stream(cs)
     staging.record_stream(ks)
+
+
+def _host_items(items):
+    n = len(items)
+    arr = (HqqHostTensor * max(n, 1))()
+    for i, (W, pk, sc, ze) in enumerate(items):
+        if not isinstance(W, torch.Tensor) or W.is_cuda or W.dtype not in _F16 or not W.is_contiguous():
+            raise TypeError("W must be a contiguous CPU fp16 tensor")
+        rows, cols = W.shape
+        arr[i] = HqqHostTensor(W.data_ptr(), rows, cols, _dev_ptr(pk, "packed", _U32).value,
+                               _dev_ptr(sc, "scale", (torch.float32,)).value,
+                               _dev_ptr(ze, "zero", (torch.float32,)).value)
+    return arr, n
+
+
+STATIC_STAGING_BYTES = 64 << 20
+
+
+def hqq_quantize_streamed_static(items, nbits: int, group_size: int, axis: int, copy_stream=None,
+                                 compute_stream=None, iters: int = ITERS_DEFAULT,
+                                 p: float = P_DEFAULT, beta0: float = BETA0_DEFAULT,
+                                 kappa: float = KAPPA_DEFAULT, device=None):
+    """hqq_quantize_streamed through the library's static staging array
+    (STATIC_STAGING_BYTES per device): no device allocation in the call.
+    Calls on one device must not overlap (they share the array)."""
+    L = load_library()
+    arr, n = _host_items(items)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    cs = copy_stream if copy_stream is not None else torch.cuda.current_stream(dev)
+    ks = compute_stream if compute_stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = L.hqq_quantize_streamed_static(ctypes.cast(arr, ctypes.c_void_p), n, nbits, group_size, axis,
+                                            iters, p, beta0, kappa, ctypes.c_void_p(cs.cuda_stream),
+                                            ctypes.c_void_p(ks.cuda_stream))
+    if st != 0:
+        raise HQQError("hqq_quantize_streamed_static", st)
 
 
 def hqq_quantize_meta(meta: torch.Tensor, group_size: int = 128):

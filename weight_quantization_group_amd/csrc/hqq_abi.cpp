@@ -199,6 +199,7 @@ const char *hqq_strerror(int status)
     case HQQ_EINVAL_PARAM: return "iters must be in [0, 65536] and p, beta0, kappa finite and > 0";
     case HQQ_EHIP: return "a HIP kernel launch failed";
     case HQQ_EINVAL_DTYPE: return "dtype must be HQQ_DTYPE_FP16 or HQQ_DTYPE_BF16";
+    case HQQ_ESCRATCH: return "a tensor's row block does not fit half of the static staging array (HQQ_STATIC_STAGING_BYTES)";
     default: return "unknown status";
     }
 }

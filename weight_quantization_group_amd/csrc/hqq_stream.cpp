@@ -18,6 +18,7 @@
 
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -45,17 +46,22 @@ struct Piece {
     int64_t r0, nr;  // row block
 };
 
-struct Events {
+// The five events that order the copy and compute streams of one call.
+struct EventSet {
     hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
     hipEvent_t entry = nullptr;
-    bool ok = true;
-    Events()
+    bool create()
     {
-        ok = hipEventCreateWithFlags(&entry, hipEventDisableTiming) == hipSuccess;
+        bool ok = hipEventCreateWithFlags(&entry, hipEventDisableTiming) == hipSuccess;
         for (int b = 0; b < 2; ++b)
             ok = ok && hipEventCreateWithFlags(&copied[b], hipEventDisableTiming) == hipSuccess &&
                  hipEventCreateWithFlags(&done[b], hipEventDisableTiming) == hipSuccess;
+        return ok;
     }
+};
+
+// An EventSet created for one call and released at its end.
+struct Events : EventSet {
     ~Events()
     {
         // an event destroyed while still pending is released when it completes
@@ -70,14 +76,61 @@ struct Events {
     }
 };
 
-}  // namespace
+// The staging of hqq_quantize_streamed_static: a file-scope device array.
+// Host code uses only its per-device address from hipGetSymbolAddress (the
+// array's name in host code is a host-side stand-in, not a device address).
+// Nothing in it needs to start at zero: every byte a solve reads was copied
+// in by the same call first.
+constexpr int64_t kStaticStaging = HQQ_STATIC_STAGING_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticStaging];
 
-extern "C" {
+// Per device: the array's address there and the call's five events, set up
+// at the first call with that device current and kept to the end of the
+// process.
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+    bool ready = false;
+    void *ptr = nullptr;
+    EventSet ev;
+};
+StaticDevice g_static[kMaxDevices];
+std::mutex g_static_mu;
 
-int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int group_size, int axis,
-                          int iters, float p, float beta0, float kappa, void *staging,
-                          int64_t staging_bytes, void *copy_stream, void *compute_stream)
+StaticDevice *static_device()
 {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticDevice &d = g_static[dev];
+    if (!d.ready) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        EventSet ev;
+        if (!ev.create())
+            return nullptr;
+        d.ptr = p;
+        d.ev = ev;
+        d.ready = true;
+    }
+    return &d;
+}
+
+// The streamed solve.  use_static = false: through the caller's staging
+// buffer, with call_events created here for the call (after every argument
+// check; the caller's Events releases them); a block unit that does not fit
+// half of the buffer returns HQQ_EINVAL_SHAPE.  use_static = true: through
+// the static array and the device's kept events, set up (after every
+// argument check) at the first call on the current device; a block unit too
+// large for it returns HQQ_ESCRATCH.
+int streamed(const hqq_host_tensor *tensors, int n, int nbits, int group_size, int axis, int iters, float p,
+             float beta0, float kappa, void *staging, int64_t staging_bytes, void *copy_stream,
+             void *compute_stream, Events *call_events, bool use_static)
+{
+    const int too_big = use_static ? HQQ_ESCRATCH : HQQ_EINVAL_SHAPE;
+    if (use_static)
+        staging_bytes = kStaticStaging;
     if (n < 0)
         return HQQ_EINVAL_SHAPE;
     if (n > 0 && !tensors)
@@ -86,8 +139,11 @@ int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int 
         return st;
     if (n == 0)
         return HQQ_OK;
-    if (!staging || ((uintptr_t)staging & 15u) != 0)
+    if (!use_static && (!staging || ((uintptr_t)staging & 15u) != 0))
         return HQQ_EINVAL_PTR;
+    // the static array is 256-byte aligned: any aligned address stands in for
+    // it in the descriptor checks below
+    const void *check_w = use_static ? reinterpret_cast<const void *>(uintptr_t(256)) : staging;
     // two halves of the staging buffer, 256-byte multiples (both aligned)
     const int64_t half = staging_bytes > 0 ? (staging_bytes / 2) / 256 * 256 : 0;
 
@@ -98,13 +154,13 @@ int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int 
         const hqq_host_tensor &h = tensors[i];
         if (!h.W)
             return HQQ_EINVAL_PTR;
-        const hqq_tensor d{reinterpret_cast<const uint16_t *>(staging), h.rows, h.cols, h.packed,
+        const hqq_tensor d{reinterpret_cast<const uint16_t *>(check_w), h.rows, h.cols, h.packed,
                            h.scale, h.zero};
         if (const int st = hqq::check_tensor(d, nbits, group_size, axis))
             return st;
         const int64_t unit = row_unit(h.cols, nbits, group_size, axis);
         if (unit * h.cols * 2 > half)
-            return HQQ_EINVAL_SHAPE;
+            return too_big;
     }
 
     // chunks: consecutive row blocks (of one or more tensors) that fill a half
@@ -132,9 +188,17 @@ int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int 
     }
 
     const hipStream_t cs = (hipStream_t)copy_stream, ks = (hipStream_t)compute_stream;
-    Events ev;
-    if (!ev.ok)
+    EventSet *evs = call_events;
+    if (use_static) {
+        StaticDevice *d = static_device();
+        if (!d)
+            return HQQ_EHIP;
+        staging = d->ptr;
+        evs = &d->ev;
+    } else if (!call_events || !call_events->create()) {
         return HQQ_EHIP;
+    }
+    EventSet &ev = *evs;
     // the staging buffer may still be read by solves enqueued on the compute
     // stream before this call: the copies start after them
     if (hipEventRecord(ev.entry, ks) != hipSuccess || hipStreamWaitEvent(cs, ev.entry, 0) != hipSuccess)
@@ -177,6 +241,27 @@ int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int 
             return HQQ_EHIP;
     }
     return HQQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hqq_quantize_streamed(const hqq_host_tensor *tensors, int n, int nbits, int group_size, int axis,
+                          int iters, float p, float beta0, float kappa, void *staging,
+                          int64_t staging_bytes, void *copy_stream, void *compute_stream)
+{
+    Events ev;
+    return streamed(tensors, n, nbits, group_size, axis, iters, p, beta0, kappa, staging, staging_bytes,
+                    copy_stream, compute_stream, &ev, false);
+}
+
+int hqq_quantize_streamed_static(const hqq_host_tensor *tensors, int n, int nbits, int group_size, int axis,
+                                 int iters, float p, float beta0, float kappa, void *copy_stream,
+                                 void *compute_stream)
+{
+    return streamed(tensors, n, nbits, group_size, axis, iters, p, beta0, kappa, nullptr, 0, copy_stream,
+                    compute_stream, nullptr, true);
 }
 
 }  // extern "C"
