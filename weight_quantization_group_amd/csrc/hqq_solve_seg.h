@@ -70,32 +70,6 @@ __device__ __forceinline__ float seg_max(float v)
     return v;
 }
 
-// Eight clamped codes of a lane (bytes of d0: codes 0-3, d1: codes 4-7,
-// each <= qmax) folded into NB-bit fields, LSB first: 8 bits: the two words
-// as they are; 4 bits: one word; 2 bits: the low 16 bits; 1 bit: the low 8.
-template <int NB>
-__device__ __forceinline__ uint32_t fold_codes(uint32_t d0, uint32_t d1)
-{
-    if constexpr (NB == 4) {
-        const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
-        const uint32_t x1 = d1 | (d1 >> 4);
-        return __builtin_amdgcn_perm(x1, x0, 0x06040200u);
-    } else if constexpr (NB == 2) {
-        uint32_t x0 = d0 | (d0 >> 6);         // bits 0-3: c0 c1, bits 16-19: c2 c3
-        uint32_t x1 = d1 | (d1 >> 6);
-        x0 = (x0 | (x0 >> 12)) & 0xFFu;       // bits 0-7: c0 c1 c2 c3
-        x1 = (x1 | (x1 >> 12)) & 0xFFu;
-        return x0 | (x1 << 8);
-    } else {
-        static_assert(NB == 1, "8-bit codes are stored as bytes");
-        uint32_t x0 = d0 | (d0 >> 7);         // bits 0-1: c0 c1, bits 16-17: c2 c3
-        uint32_t x1 = d1 | (d1 >> 7);
-        x0 = (x0 | (x0 >> 14)) & 0xFu;        // bits 0-3: c0 c1 c2 c3
-        x1 = (x1 | (x1 >> 14)) & 0xFu;
-        return x0 | (x1 << 4);
-    }
-}
-
 // Occupancy target: the largest at which the kernel needs no scratch (the
 // out-of-line power of the frozen finish sets the register count; a spill
 // would make the wave wait for the next step's load at once).
