@@ -31,7 +31,9 @@ are seeded random, meta from a synthetic min/max distribution, activations
 N(0, 1).
 
 --op streamed measures the solve over weights held in host memory (models
-larger than HBM): the 7B stack in pinned host memory, hqq_quantize_streamed
+larger than HBM): the workload (default the 7B stack; the 70B mixed stack
+with --workload llama70b_stack80_mixed) in pinned host memory, quantized
+layer by layer: one hqq_quantize_streamed call per layer and format,
 copying double-buffered chunks of 512 MiB over PCIe while the solve runs.
 Its bound is the host-to-device link, reported beside a plain pinned copy
 of the same bytes.
@@ -532,28 +534,38 @@ def bench_streamed(args):
     hq.load_library()
     dev = torch.device("cuda:0")
     tensors = synth.workload(args.workload)
-    nb, gs, ax = tensors[0]["nbits"], tensors[0]["group_size"], tensors[0]["axis"]
-    assert all((t["nbits"], t["group_size"], t["axis"]) == (nb, gs, ax) for t in tensors)
     n_weights = sum(t["rows"] * t["cols"] for t in tensors)
-    host = torch.empty(n_weights, dtype=torch.int16, pin_memory=True)
-    items, off = [], 0
+    # every weight in pinned host memory, one allocation per tensor
+    # (generated on the device, copied out)
+    items, hosts = [], []
     for t in tensors:
+        nb, gs, ax = t["nbits"], t["group_size"], t["axis"]
         W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
         synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
-        h = host[off:off + W.numel()].view(t["rows"], t["cols"])
+        h = torch.empty((t["rows"], t["cols"]), dtype=torch.int16, pin_memory=True)
         h.copy_(W.view(torch.int16))
-        off += W.numel()
+        hosts.append(h)
         del W
         items.append((h, torch.empty(hq.packed_shape(t["rows"], t["cols"], nb, ax), dtype=torch.int32, device=dev),
                       torch.empty(hq.meta_shape(t["rows"], t["cols"], gs, ax), dtype=torch.float32, device=dev),
                       torch.empty(hq.meta_shape(t["rows"], t["cols"], gs, ax), dtype=torch.float32, device=dev)))
+    # layer by layer: one streamed call per run of consecutive tensors of one
+    # layer and one format (a 70B layer: attention 4b g64, then MLP 2b g16)
+    calls = []
+    for t, it in zip(tensors, items):
+        key = (t["layer"], t["nbits"], t["group_size"], t["axis"])
+        if calls and calls[-1][0] == key:
+            calls[-1][1].append(it)
+        else:
+            calls.append((key, [it]))
     staging = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cs, ks = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def step():
-        hq.hqq_quantize_streamed(items, nb, gs, ax, staging, copy_stream=cs, compute_stream=ks,
-                                 iters=args.iters)
+        for (_, nb, gs, ax), its in calls:
+            hq.hqq_quantize_streamed(its, nb, gs, ax, staging, copy_stream=cs, compute_stream=ks,
+                                     iters=args.iters)
 
     for _ in range(args.warmup):
         step()
@@ -564,19 +576,25 @@ def bench_streamed(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # the link alone: the same bytes, pinned host -> device, in 512 MiB pieces
+    # the link alone: the same bytes, pinned host -> device, in pieces of at
+    # most 512 MiB
     dst = staging.view(torch.int16)
     half = dst.numel() // 2
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(0, host.numel(), half):
-        dst[:min(half, host.numel() - i)].copy_(host[i:i + half], non_blocking=True)
+    for h in hosts:
+        flat = h.view(-1)
+        for i in range(0, flat.numel(), half):
+            n = min(half, flat.numel() - i)
+            dst[:n].copy_(flat[i:i + n], non_blocking=True)
     torch.cuda.synchronize()
     copy_ms = (time.perf_counter() - t0) * 1e3
     gbs = 2.0 * n_weights / (ms * 1e-3) / 1e9
     copy_gbs = 2.0 * n_weights / (copy_ms * 1e-3) / 1e9
+    fmts = sorted({(t["nbits"], t["group_size"], t["axis"]) for t in tensors})
+    fmt_s = ", ".join(f"{b}b g{g}" + (" axis 0" if a == 0 else "") for b, g, a in fmts)
     out = {
-        "metric": f"GB/s of fp16 weights quantized from pinned host memory (HQQ {nb}b g{gs}, {args.iters} it), "
+        "metric": f"GB/s of fp16 weights quantized from pinned host memory (HQQ {fmt_s}, {args.iters} it), "
                   f"workload {args.workload}",
         "value": round(gbs, 3),
         "unit": "GB/s",
@@ -590,8 +608,8 @@ def bench_streamed(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
-                   "staging_bytes": staging.numel(), "nbits": nb, "group_size": gs, "axis": ax,
-                   "iters": args.iters},
+                   "streamed_calls_per_step": len(calls), "staging_bytes": staging.numel(),
+                   "formats": [list(f) for f in fmts], "iters": args.iters},
         "roofline": {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
                      "pinned_copy_GBs": round(copy_gbs, 2), "frac_of_copy": round(gbs / copy_gbs, 4)},
