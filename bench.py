@@ -535,14 +535,19 @@ def bench_streamed(args):
     dev = torch.device("cuda:0")
     tensors = synth.workload(args.workload)
     n_weights = sum(t["rows"] * t["cols"] for t in tensors)
-    # every weight in pinned host memory, one allocation per tensor
-    # (generated on the device, copied out)
+    # Host weights (generated on the device, copied out), one tensor each.
+    # Up to 48 GiB they are all page-locked.  A larger model (the 70B stack,
+    # 137 GB) stays in ordinary host memory, as a checkpoint loaded into RAM
+    # would, and each layer passes through one of two page-locked layer
+    # buffers: the host copies layer L + 1 into one while the device streams
+    # layer L out of the other.
+    pool_mode = 2 * n_weights > (48 << 30)
     items, hosts = [], []
     for t in tensors:
         nb, gs, ax = t["nbits"], t["group_size"], t["axis"]
         W = torch.empty((t["rows"], t["cols"]), dtype=torch.float16, device=dev)
         synth.generate_gpu(W, t["seed"], t["layer"], t["tensor_id"])
-        h = torch.empty((t["rows"], t["cols"]), dtype=torch.int16, pin_memory=True)
+        h = torch.empty((t["rows"], t["cols"]), dtype=torch.int16, pin_memory=not pool_mode)
         h.copy_(W.view(torch.int16))
         hosts.append(h)
         del W
@@ -552,20 +557,50 @@ def bench_streamed(args):
     # layer by layer: one streamed call per run of consecutive tensors of one
     # layer and one format (a 70B layer: attention 4b g64, then MLP 2b g16)
     calls = []
-    for t, it in zip(tensors, items):
+    for i, t in enumerate(tensors):
         key = (t["layer"], t["nbits"], t["group_size"], t["axis"])
         if calls and calls[-1][0] == key:
-            calls[-1][1].append(it)
+            calls[-1][1].append(i)
         else:
-            calls.append((key, [it]))
+            calls.append((key, [i]))
     staging = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cs, ks = torch.cuda.Stream(), torch.cuda.Stream()
+    layers = []
+    for key, idx in calls:
+        if layers and layers[-1][0] == key[0]:
+            layers[-1][1].append((key, idx))
+        else:
+            layers.append((key[0], [(key, idx)]))
+    pool, freed = [], [None, None]
+    if pool_mode:
+        biggest = max(sum(hosts[i].numel() for _, idx in ls for i in idx) for _, ls in layers)
+        pool = [torch.empty(biggest, dtype=torch.int16, pin_memory=True) for _ in range(2)]
     torch.cuda.synchronize()
 
     def step():
-        for (_, nb, gs, ax), its in calls:
-            hq.hqq_quantize_streamed(its, nb, gs, ax, staging, copy_stream=cs, compute_stream=ks,
-                                     iters=args.iters)
+        if not pool_mode:
+            for (_, nb, gs, ax), idx in calls:
+                hq.hqq_quantize_streamed([items[i] for i in idx], nb, gs, ax, staging, copy_stream=cs,
+                                         compute_stream=ks, iters=args.iters)
+            return
+        for li, (_, ls) in enumerate(layers):
+            b = li % 2
+            if freed[b] is not None:
+                freed[b].synchronize()     # the copies out of this buffer are done
+            off = 0
+            for (_, nb, gs, ax), idx in ls:
+                its = []
+                for i in idx:
+                    n = hosts[i].numel()
+                    v = pool[b][off:off + n].view(hosts[i].shape)
+                    v.copy_(hosts[i])
+                    off += n
+                    its.append((v, *items[i][1:]))
+                hq.hqq_quantize_streamed(its, nb, gs, ax, staging, copy_stream=cs, compute_stream=ks,
+                                         iters=args.iters)
+            ev = torch.cuda.Event()
+            ev.record(cs)
+            freed[b] = ev
 
     for _ in range(args.warmup):
         step()
@@ -577,13 +612,15 @@ def bench_streamed(args):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # the link alone: the same bytes, pinned host -> device, in pieces of at
-    # most 512 MiB
+    # most 512 MiB (from the layer buffers in the pooled mode, without the
+    # host-side copies)
     dst = staging.view(torch.int16)
     half = dst.numel() // 2
+    srcs = [h.view(-1) for h in hosts] if not pool_mode else \
+        [pool[0][:h.numel()] for h in hosts]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for h in hosts:
-        flat = h.view(-1)
+    for flat in srcs:
         for i in range(0, flat.numel(), half):
             n = min(half, flat.numel() - i)
             dst[:n].copy_(flat[i:i + n], non_blocking=True)
@@ -594,7 +631,8 @@ def bench_streamed(args):
     fmts = sorted({(t["nbits"], t["group_size"], t["axis"]) for t in tensors})
     fmt_s = ", ".join(f"{b}b g{g}" + (" axis 0" if a == 0 else "") for b, g, a in fmts)
     out = {
-        "metric": f"GB/s of fp16 weights quantized from pinned host memory (HQQ {fmt_s}, {args.iters} it), "
+        "metric": f"GB/s of fp16 weights quantized from host memory, layer by layer (HQQ {fmt_s}, "
+                  f"{args.iters} it), "
                   f"workload {args.workload}",
         "value": round(gbs, 3),
         "unit": "GB/s",
@@ -609,6 +647,8 @@ def bench_streamed(args):
         "data": "synthetic",
         "config": {"workload": args.workload, "weights": n_weights, "tensors": len(tensors),
                    "streamed_calls_per_step": len(calls), "staging_bytes": staging.numel(),
+                   "host_weights": ("ordinary host memory through two page-locked layer buffers"
+                                    if pool_mode else "page-locked host memory"),
                    "formats": [list(f) for f in fmts], "iters": args.iters},
         "roofline": {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
