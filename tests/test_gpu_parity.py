@@ -302,7 +302,8 @@ def test_synth_gpu_generator_matches_numpy():
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3, 4, 5, 8, 50])
-@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1), (8, 128, 1)])
+@pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (2, 16, 0), (1, 32, 1), (4, 8, 1), (8, 128, 1),
+                                          (3, 64, 0), (3, 8, 0)])
 def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters, mapping):
     """Groups that stop before, at and after the point where the solve parks
     unfinished groups for later batches, and long runs, match the oracle."""
