@@ -295,12 +295,19 @@ def bench_linear(args):
     nl = len(LLAMA7B_LINEARS)
     outs = [torch.empty((M, N), dtype=cdt, device=dev) for (N, K) in LLAMA7B_LINEARS]
     calls = []
+    # one workspace for every call (they run in order on one stream): the
+    # tiled kernel may split K for many rows (hqq_linear_batch_ws)
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
+    work = None
+    if M > 1 and not args.no_split:
+        nmax = max(sum(LLAMA7B_LINEARS[i][0] for i in idx) for idx in groups)
+        work = torch.empty(hq.linear_workspace_bytes(M, [nmax]) // 4, dtype=torch.float32, device=dev)
     for li in range(LLAMA7B_LAYERS):
         ly = layers[li * nl:(li + 1) * nl]
-        for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+        for idx in groups:
             K = ly[idx[0]][1]
             items = [(ly[i][2], ly[i][3], ly[i][4], ly[i][0], outs[i]) for i in idx]
-            calls.append((K, hq.LinearBatch(items, nbits, gs, dtype=cdt)))
+            calls.append((K, hq.LinearBatch(items, nbits, gs, dtype=cdt, workspace=work)))
     torch.cuda.synchronize()
 
     def token():
@@ -444,7 +451,8 @@ def bench_linear(args):
                             "tokens_per_s": round(M * 1e3 / ms_per_layer, 3)} if ms_per_layer else None,
         "wall_ms_per_step": round(ms_wall, 4),
         "launch": ("eager" if args.eager else "hip graph") +
-                  " of 128 calls: hqq_linear_batch of (q, k, v), (o), (gate, up), (down) per layer",
+                  " of 128 calls: hqq_linear_batch of (q, k, v), (o), (gate, up), (down) per layer" +
+                  (", with a split-K workspace" if work is not None else ""),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = linear_cpu_baseline(nbits, gs)
@@ -681,6 +689,8 @@ def main():
                     help="solve: element type of the weights (bf16: the synthetic fp16 weights rounded to bf16)")
     ap.add_argument("--eager", action="store_true",
                     help="--op linear: plain launches instead of a captured HIP graph")
+    ap.add_argument("--no-split", action="store_true",
+                    help="--op linear: no workspace, so the tiled kernel never splits K")
     ap.add_argument("--op", choices=("solve", "linear", "streamed", "meta"), default="solve",
                     help="solve: quantize the 7B stack (default); linear: one decode token "
                          "through the quantized layers; streamed: the solve from pinned host memory")

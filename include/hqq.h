@@ -349,6 +349,23 @@ typedef struct hqq_linear_weight {
 HQQ_API int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
                              int count, int nbits, int group_size, int dtype, void *stream);
 
+/* hqq_linear_batch with a caller's device workspace (16-byte aligned,
+ * workspace_bytes long; NULL with 0 bytes is hqq_linear_batch).  For a batch
+ * of many rows (prefill chunks, lnwmold.com HQQ guide section 4.2) whose
+ * output tiles are too few to occupy the device, the tiled kernel may split
+ * K in 2, 4 or 8 parts: each part's fp32 partial products go to the
+ * workspace (splits x M x sum of N floats; the launcher takes the most
+ * splits the workspace holds when its time estimate is lower) and a second
+ * launch adds them in split order in fp32 and rounds each output once to
+ * the compute dtype.  The results stay within hqq_linear's bound (fp32 sums
+ * in some order) but need not equal hqq_linear_batch's bit for bit.  The
+ * workspace is in use until the stream reaches the end of the call's work.
+ * A misaligned workspace, negative bytes, or bytes with a NULL workspace:
+ * HQQ_EINVAL_PTR. */
+HQQ_API int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
+                                int count, int nbits, int group_size, int dtype, void *workspace,
+                                int64_t workspace_bytes, void *stream);
+
 /* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */
 HQQ_API int64_t hqq_packed_words(int64_t rows, int64_t cols, int nbits, int axis);

@@ -61,7 +61,8 @@ def test_exports_every_declared_symbol(lib):
                                "hqq_dequantize", "hqq_dequantize_ex",
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
                                "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
-                               "hqq_linear_ex", "hqq_linear_batch", "hqq_solve_mapping", "hqq_packed_words",
+                               "hqq_linear_ex", "hqq_linear_batch", "hqq_linear_batch_ws", "hqq_solve_mapping",
+                               "hqq_packed_words",
                                "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
@@ -209,6 +210,14 @@ def test_linear_batch_rejects(lib):
     assert call(ws(*([good] * 9), (None, 0x2000, 0x3000, 32, 0x4000)), 10) == E["PTR"]
     assert call(ws(good), 1, dtype=2) == E["DTYPE"]
     assert call(ws(good), 1, dtype=-1) == E["DTYPE"]
+    # the workspace of hqq_linear_batch_ws: aligned, and bytes only with a pointer
+    def call_ws(work, nbytes):
+        return lib.hqq_linear_batch_ws(A, 4, 128, ws(good), 1, 4, 64, 0, work, nbytes, None)
+
+    assert call_ws(MIS, 1 << 20) == E["PTR"]
+    assert call_ws(None, 1 << 20) == E["PTR"]
+    assert call_ws(A, -1) == E["PTR"]
+    assert lib.hqq_linear_batch_ws(A, 4, 128, ws(good), 1, 3, 64, 0, A, 1 << 20, None) == E["NBITS"]
     # the single-weight entry points
     assert lib.hqq_linear_ex(A, 4, 128, A, A, A, 32, 4, 64, 5, A, None) == E["DTYPE"]
     assert lib.hqq_linear_ex(A, 4, 128, A, A, A, 32, 3, 64, 1, A, None) == E["NBITS"]

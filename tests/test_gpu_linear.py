@@ -369,3 +369,65 @@ def test_linear_bf16_batch_equals_single_calls(hq, oracle_mod):
         Y1 = hq.hqq_linear(X, pk, sc, ze, N, nbits, gs)
         torch.cuda.synchronize()
         assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# split K (hqq_linear_batch_ws): the tiled kernel's K steps divided over 2, 4
+# or 8 workgroups per output tile, fp32 partials in the caller's workspace,
+# added in split order by a second launch.  The same bound holds (fp32 sums
+# in some order); HQQ_LINEAR_SPLITS forces each split count.
+
+SPLIT_CASES = [
+    # M, K, nbits, gs, Ns
+    (400, 512, 4, 64, [256]),              # 8 steps: 2, 4, 8 splits
+    (512, 640, 2, 32, [130]),              # 10 steps: 2 and 4 splits (8 would leave one empty)
+    (384, 128, 8, 64, [64]),               # 2 steps: 2 splits
+    (400, 512, 4, 32, [130, 256, 60]),     # three weights: per-weight partial slices
+    (448, 1024, 4, 128, [96]),             # a group spans two steps
+]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 8])
+@pytest.mark.parametrize("M,K,nbits,gs,Ns", SPLIT_CASES)
+def test_linear_split_k(hq, oracle_mod, monkeypatch, M, K, nbits, gs, Ns, splits):
+    import torch
+
+    steps = K // 64
+    per = -(-steps // splits)
+    if splits > 1 and (splits - 1) * per >= steps:
+        pytest.skip("a split would be empty: the launcher does not use this count")
+    monkeypatch.setenv("HQQ_LINEAR_SPLITS", str(splits))
+    rng = np.random.RandomState(M + K * 3 + nbits + gs + len(Ns) * 101)
+    X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+    Xd = _cuda(X16)
+    ws = [random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False) for N in Ns]
+    dev = [(_cuda(p), _cuda(s), _cuda(z), N) for (p, s, z), N in zip(ws, Ns)]
+    work = torch.empty(hq.linear_workspace_bytes(M, Ns) // 4, dtype=torch.float32, device="cuda")
+    outs = hq.hqq_linear_batch(Xd, dev, nbits, gs, workspace=work)
+    torch.cuda.synchronize()
+    for (p, s, z), N, Y in zip(ws, Ns, outs):
+        Yref, A = oracle_mod.linear(X16, p, s, z, N, nbits, gs, with_abs=True)
+        check(Y.cpu().numpy(), Yref, A, K, f"{M}x{N}x{K} b{nbits} g{gs} splits {splits}")
+    if splits == 1:
+        # no split: exactly the workspace-free call
+        ref = hq.hqq_linear_batch(Xd, dev, nbits, gs)
+        torch.cuda.synchronize()
+        for Y, R in zip(outs, ref):
+            assert torch.equal(Y.view(torch.int16), R.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [128, 256, 512])
+def test_linear_workspace_auto_mid_rows(hq, oracle_mod, M):
+    """With a workspace and the launcher's own choice (few output tiles: it
+    splits K), the outputs meet the bound."""
+    import torch
+
+    K, N, nbits, gs = 1024, 512, 4, 64
+    rng = np.random.RandomState(M + 7)
+    X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+    p, s, z = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    work = torch.empty(hq.linear_workspace_bytes(M, [N]) // 4, dtype=torch.float32, device="cuda")
+    (Y,) = hq.hqq_linear_batch(_cuda(X16), [(_cuda(p), _cuda(s), _cuda(z), N)], nbits, gs, workspace=work)
+    torch.cuda.synchronize()
+    Yref, A = oracle_mod.linear(X16, p, s, z, N, nbits, gs, with_abs=True)
+    check(Y.cpu().numpy(), Yref, A, K, f"auto {M}x{N}x{K}")

@@ -31,7 +31,7 @@ EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_q
            "hqq_quantize_streamed_static",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
            "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_ex", "hqq_linear_batch",
-           "hqq_solve_mapping", "hqq_packed_words", "hqq_strerror")
+           "hqq_linear_batch_ws", "hqq_solve_mapping", "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
 DTYPE_FP16, DTYPE_BF16 = 0, 1
@@ -117,6 +117,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_linear_ex.restype = i32
     L.hqq_linear_batch.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P]
     L.hqq_linear_batch.restype = i32
+    L.hqq_linear_batch_ws.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P, i64, P]
+    L.hqq_linear_batch_ws.restype = i32
     L.hqq_solve_mapping.argtypes = [i32, i32, i32, i32, i64]
     L.hqq_solve_mapping.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
@@ -335,10 +337,15 @@ class LinearBatch:
     the C descriptor array once; run(X) is then a single C-ABI call (one
     launch per 8 weights) on the current stream.  weights: list of (packed,
     scale, zero, N, Y) with Y a preallocated fp16 [M, N] CUDA tensor; the
-    tensors are kept alive by the object."""
+    tensors are kept alive by the object.  workspace: an optional CUDA tensor
+    the tiled kernel may use to split K (hqq_linear_batch_ws); see
+    linear_workspace_bytes."""
 
-    def __init__(self, weights, nbits: int, group_size: int, dtype=torch.float16):
+    def __init__(self, weights, nbits: int, group_size: int, dtype=torch.float16, workspace=None):
         self._lib = load_library()
+        self._ws = workspace
+        if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+            raise TypeError("workspace must be a contiguous CUDA tensor")
         self._items = [tuple(w) for w in weights]
         self.nbits, self.group_size = nbits, group_size
         self._code, _, ok = _compute_dtype(torch.empty(0, dtype=dtype))
@@ -356,22 +363,34 @@ class LinearBatch:
         for (_, _, _, N, Y) in self._items:
             if tuple(Y.shape) != (M, N):
                 raise ValueError(f"Y must be [{M}, {N}], got {tuple(Y.shape)}")
-        st = self._lib.hqq_linear_batch(_dev_ptr(X, "X", self._ok), M, K, self._arr, len(self._items),
-                                        self.nbits, self.group_size, self._code, _stream(X.device))
+        ws = self._ws
+        st = self._lib.hqq_linear_batch_ws(_dev_ptr(X, "X", self._ok), M, K, self._arr, len(self._items),
+                                           self.nbits, self.group_size, self._code,
+                                           ctypes.c_void_p(ws.data_ptr() if ws is not None else None),
+                                           ws.numel() * ws.element_size() if ws is not None else 0,
+                                           _stream(X.device))
         if st != 0:
-            raise HQQError("hqq_linear_batch", st)
+            raise HQQError("hqq_linear_batch_ws", st)
+        if ws is not None and not torch.cuda.is_current_stream_capturing():
+            ws.record_stream(torch.cuda.current_stream(X.device))
         return [it[4] for it in self._items]
 
 
-def hqq_linear_batch(X: torch.Tensor, weights, nbits: int, group_size: int):
+def linear_workspace_bytes(M: int, Ns) -> int:
+    """Workspace for the most K splits (8) of hqq_linear_batch_ws over
+    weights of output sizes Ns on M rows."""
+    return 8 * M * sum(Ns) * 4
+
+
+def hqq_linear_batch(X: torch.Tensor, weights, nbits: int, group_size: int, workspace=None):
     """[X . W_hat_i^T] for weights [(packed, scale, zero, N), ...] sharing X,
     in one C-ABI call, in X's compute dtype (fp16 or bfloat16).  Returns the
-    outputs."""
+    outputs.  workspace: see LinearBatch."""
     M = X.shape[0]
     _, tdt, _ = _compute_dtype(X)
     items = [(pk, sc, ze, N, torch.empty((M, N), dtype=tdt, device=X.device))
              for (pk, sc, ze, N) in weights]
-    return LinearBatch(items, nbits, group_size, dtype=tdt).run(X)
+    return LinearBatch(items, nbits, group_size, dtype=tdt, workspace=workspace).run(X)
 
 
 def hqq_quantize_streamed(items, nbits: int, group_size: int, axis: int, staging: torch.Tensor,

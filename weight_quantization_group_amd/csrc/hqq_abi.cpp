@@ -390,6 +390,13 @@ int hqq_unpack(const uint32_t *packed, int64_t rows, int64_t cols, int nbits, in
 int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws, int count,
                      int nbits, int group_size, int dtype, void *stream)
 {
+    return hqq_linear_batch_ws(X, M, K, ws, count, nbits, group_size, dtype, nullptr, 0, stream);
+}
+
+int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws, int count,
+                        int nbits, int group_size, int dtype, void *workspace, int64_t workspace_bytes,
+                        void *stream)
+{
     if (!hqq::valid_nbits(nbits) || nbits == 3)
         return HQQ_EINVAL_NBITS;
     if (dtype != HQQ_DTYPE_FP16 && dtype != HQQ_DTYPE_BF16)
@@ -423,7 +430,11 @@ int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_w
         if (!aligned16(ws[i].packed) || !aligned16(ws[i].scale) || !aligned16(ws[i].zero) ||
             !aligned16(ws[i].Y))
             return HQQ_EINVAL_PTR;
+    if (workspace_bytes < 0 || (workspace && !aligned16(workspace)) || (!workspace && workspace_bytes > 0))
+        return HQQ_EINVAL_PTR;
     hqq::LinearBatch b{};
+    b.work = reinterpret_cast<float *>(workspace);
+    b.work_floats = workspace ? workspace_bytes / 4 : 0;
     b.a.X = X;
     b.a.M = M;
     b.a.K = K;

@@ -96,6 +96,7 @@ struct LinearArgs {
     int64_t wpr;             // words per row of W: K * nbits / 32
     int64_t gpl;             // groups per row of W: K / gs
     int gs, gshift;          // group size and its log2
+    float *part;             // split K: fp32 partial sums [splits, M, N], else null
 };
 
 // Several weights that share X (and K and the code format) in one launch:
@@ -110,6 +111,13 @@ struct LinearBatch {
     const float *zero[kLinBatch];
     uint16_t *Y[kLinBatch];
     int64_t N[kLinBatch];
+    // split K (tiled kernel): a caller's workspace of work_floats fp32 values;
+    // the launcher sets splits and part[j] (weight j's [splits, M, N] slice)
+    float *work;
+    int64_t work_floats;
+    int splits;
+    float *part[kLinBatch];
+    uint32_t rblock0[kLinBatch + 1];   // reduction workgroups of each weight
 };
 
 // host-side argument checks shared by the entry points (HQQ_* status)

@@ -44,6 +44,8 @@
 // stays in cache).  The waves add their partial sums through LDS at the end.
 #include "hqq_internal.h"
 
+#include <stdlib.h>
+
 namespace hqq {
 namespace {
 
@@ -237,6 +239,7 @@ __device__ __forceinline__ LinearArgs batch_item(const LinearBatch &b, uint32_t 
     a.zero = b.zero[j];
     a.Y = b.Y[j];
     a.N = b.N[j];
+    a.part = b.splits > 1 ? b.part[j] : nullptr;
     bx -= b.tile0[j];
     return a;
 }
@@ -662,9 +665,13 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)bx * kTBN;
     const uint32_t K = (uint32_t)a.K;
-    const uint32_t steps = K / kTK;
+    // split K: workgroup z of gridDim.z takes steps s0 .. s0 + steps - 1 of
+    // the K / 64 (the host keeps every split non-empty)
+    const uint32_t all_steps = K / kTK, per = (all_steps + gridDim.z - 1) / gridDim.z;
+    const uint32_t s0 = blockIdx.z * per;
+    const uint32_t steps = all_steps - s0 < per ? all_steps - s0 : per;
     // past the last step the loads repeat it (in bounds, never used)
-    auto clampk = [&](uint32_t s_) { return (s_ < steps ? s_ : steps - 1) * kTK; };
+    auto clampk = [&](uint32_t s_) { return (s0 + (s_ < steps ? s_ : steps - 1)) * kTK; };
 
     if (wave < 4) {
         // MFMA wave: step st reads X from buffer st % 3 and W from st & 1
@@ -691,7 +698,7 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
 #pragma unroll
             for (int t = 0; t < TN; ++t)
                 acc[u][t] = float4v{0.f, 0.f, 0.f, 0.f};
-        dma_x(0, 0);
+        dma_x(clampk(0), 0);
         dma_x(clampk(1), 1);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): X(0) has landed
         lds_barrier();                        // and W(0) is in LDS
@@ -733,8 +740,12 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
                 for (int r = 0; r < 4; ++r) {
                     const int64_t m = m0 + wm * (BM / 2) + 16 * u + 4 * (lane >> 4) + r;
                     const int64_t n = n0 + wn * (kTBN / 2) + 16 * t + (lane & 15);
-                    if (m < a.M && n < a.N)
-                        a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
+                    if (m < a.M && n < a.N) {
+                        if (a.part)
+                            a.part[((int64_t)blockIdx.z * a.M + m) * a.N + n] = acc[u][t][r];
+                        else
+                            a.Y[m * a.N + n] = out1<BF>(acc[u][t][r]);
+                    }
                 }
     } else {
         // dequantization wave: thread p = tid - 256 dequantizes row p / 2,
@@ -773,7 +784,7 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
                 ws[b][wr * kWPitch + wr0 + j] = runs[j];
         };
         TileW<NB, G1> wb0, wb1;
-        load_w(0, wb0);
+        load_w(clampk(0), wb0);
         store_w(wb0, 0);
         load_w(clampk(1), wb1);
         load_w(clampk(2), wb0);
@@ -792,6 +803,38 @@ __global__ __launch_bounds__(512, 1) void linear_tiled_kernel(LinearBatch lb)
     }
 }
 
+// Split K, second pass: Y = the partial sums of the splits added in split
+// order in fp32, rounded once to the compute dtype.  Four outputs per
+// thread; workgroups rblock0[j] .. rblock0[j + 1] - 1 belong to weight j.
+constexpr int kReduceBlock = 256;
+
+template <bool BF>
+__global__ __launch_bounds__(kReduceBlock) void linear_reduce_kernel(LinearBatch lb)
+{
+    const uint32_t bx = blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < kLinBatch; ++k)
+        j = k < lb.count && bx >= lb.rblock0[k] ? k : j;
+    const int64_t total = lb.a.M * lb.N[j];
+    const int64_t i0 = ((int64_t)(bx - lb.rblock0[j]) * kReduceBlock + threadIdx.x) * 4;
+    if (i0 >= total)
+        return;
+    const float *part = lb.part[j];
+    uint16_t *Y = lb.Y[j];
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < lb.splits; ++z) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (i0 + e < total)
+                v[e] += part[z * total + i0 + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (i0 + e < total)
+            Y[i0 + e] = out1<BF>(v[e]);
+}
+
 // Time estimates of the two kernels (the row-block kernel re-derives W for
 // every 32 rows of X, so its time grows with ceil(M / 32) * N * K; the tiled
 // kernel's is its rounds of tiles over the 256 CUs times K / 64 steps), from
@@ -806,18 +849,70 @@ inline double skinny_us(const LinearBatch &b)
     return (double)((b.a.M + 31) / 32) * 9.1 * ((double)n * (double)b.a.K) / (4096.0 * 4096.0);
 }
 
-inline double tiled_us(const LinearBatch &b, int bm)
+inline double tiled_us(const LinearBatch &b, int bm, int splits = 1)
 {
-    int64_t cols = 0;
-    for (int j = 0; j < b.count; ++j)
+    int64_t cols = 0, n = 0;
+    for (int j = 0; j < b.count; ++j) {
         cols += (b.N[j] + kTBN - 1) / kTBN;
-    const int64_t tiles = cols * ((b.a.M + bm - 1) / bm);
-    return (double)((tiles + 255) / 256) * (double)(b.a.K / kTK) * (bm == 128 ? 0.74 : 0.92);
+        n += b.N[j];
+    }
+    const int64_t tiles = cols * ((b.a.M + bm - 1) / bm) * splits;
+    const int64_t steps = (b.a.K / kTK + splits - 1) / splits;
+    double t = (double)((tiles + 255) / 256) * (double)steps * (bm == 128 ? 0.74 : 0.92);
+    if (splits > 1)   // the second pass: read the partials, write Y, and its launch
+        t += 3.0 + (double)b.a.M * (double)n * (4.0 * splits + 2.0) / 4.0e6;
+    return t;
+}
+
+// The splits of K the workspace allows (every split non-empty): 1, 2, 4 or 8.
+inline bool splits_ok(const LinearBatch &b, int splits)
+{
+    const int64_t steps = b.a.K / kTK;
+    int64_t n = 0;
+    for (int j = 0; j < b.count; ++j)
+        n += b.N[j];
+    const int64_t per = (steps + splits - 1) / splits;
+    return splits == 1 || (b.work != nullptr && (splits - 1) * per < steps &&
+                           (int64_t)splits * b.a.M * n <= b.work_floats);
+}
+
+// HQQ_LINEAR_SPLITS=1|2|4|8 in the environment forces that many K splits
+// where the workspace allows them (tests use it to reach every split count);
+// 0: the estimate decides.
+inline int forced_splits()
+{
+    const char *e = getenv("HQQ_LINEAR_SPLITS");
+    if (!e)
+        return 0;
+    const int v = atoi(e);
+    return v == 1 || v == 2 || v == 4 || v == 8 ? v : 0;
+}
+
+// The tile height and split count of the smallest estimate.
+inline double tiled_best(const LinearBatch &b, int &bm, int &splits)
+{
+    double best = 0.0;
+    bm = 256;
+    splits = 1;
+    const int force = forced_splits();
+    for (int sp : {1, 2, 4, 8}) {
+        if (!splits_ok(b, sp) || (force && sp != force && splits_ok(b, force)))
+            continue;
+        for (int m : {256, 128}) {
+            const double t = tiled_us(b, m, sp);
+            if (best == 0.0 || t < best) {
+                best = t;
+                bm = m;
+                splits = sp;
+            }
+        }
+    }
+    return best;
 }
 
 #define HQQ_LAUNCH_TILED(BMV)                                                                           \
     {                                                                                                   \
-        const dim3 grid(cols, (unsigned)((b.a.M + BMV - 1) / BMV));                                     \
+        const dim3 grid(cols, (unsigned)((b.a.M + BMV - 1) / BMV), (unsigned)b.splits);                 \
         if (NB == 4 && b.a.gs >= 64)                                                                    \
             hipLaunchKernelGGL((linear_tiled_kernel<NB, true, BF, NB == 4, BMV>), grid, dim3(512), 0, s, b); \
         else if (b.a.gs >= 32)                                                                          \
@@ -831,10 +926,27 @@ template <int NB, bool BF>
 hipError_t launch_tiled(LinearBatch &b, hipStream_t s)
 {
     const uint32_t cols = fill_tiles(b, kTBN);
-    if (tiled_us(b, 128) < tiled_us(b, 256))
+    int bm, splits;
+    tiled_best(b, bm, splits);
+    b.splits = splits;
+    if (splits > 1) {
+        // weight j's partials: [splits, M, N_j], after those of weights < j
+        int64_t off = 0;
+        uint32_t rb = 0;
+        for (int j = 0; j < b.count; ++j) {
+            b.part[j] = b.work + off;
+            off += (int64_t)splits * b.a.M * b.N[j];
+            b.rblock0[j] = rb;
+            rb += (uint32_t)((b.a.M * b.N[j] + 4 * kReduceBlock - 1) / (4 * kReduceBlock));
+        }
+        b.rblock0[b.count] = rb;
+    }
+    if (bm == 128)
         HQQ_LAUNCH_TILED(128)
     else
         HQQ_LAUNCH_TILED(256)
+    if (splits > 1)
+        hipLaunchKernelGGL((linear_reduce_kernel<BF>), dim3(b.rblock0[b.count]), dim3(kReduceBlock), 0, s, b);
     return hipGetLastError();
 }
 #undef HQQ_LAUNCH_TILED
@@ -851,8 +963,8 @@ inline bool use_tiled(const LinearBatch &b)
         return false;
     if (a.M >= kTiledMinRows)
         return true;
-    const double t = tiled_us(b, 128) < tiled_us(b, 256) ? tiled_us(b, 128) : tiled_us(b, 256);
-    return t < skinny_us(b);
+    int bm, splits;
+    return tiled_best(b, bm, splits) < skinny_us(b);
 }
 
 template <int NB, bool BF>
