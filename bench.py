@@ -8,7 +8,7 @@
 
 A step quantizes every tensor of the workload once, with all fp16 inputs
 already resident in HBM: consecutive tensors of one format go to
-hqq_quantize_batch in chunks of up to 24 (one kernel launch per chunk).  The default
+hqq_quantize_batch in even chunks of up to 48 (one kernel launch per chunk).  The default
 workload is the 7B-shaped stack: 32 decoder layers of q/k/v/o [4096,4096],
 gate/up [11008,4096], down [4096,11008] -- 6,476,005,376 fp16 weights
 (12.95 GB) -- at nbits=4, group_size=64, axis=1, 20 iterations, p=0.7,
@@ -748,15 +748,22 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # launches: consecutive tensors of one format, up to MAX_BATCH per
-    # hqq_quantize_batch call (one kernel launch each)
-    chunks = []
+    # launches: runs of consecutive tensors of one format, each cut into as
+    # even pieces of at most MAX_BATCH as it allows (one hqq_quantize_batch
+    # call, one kernel launch each)
+    runs = []
     for i, t in enumerate(tensors):
         fmt = (t["nbits"], t["group_size"], t["axis"])
-        if chunks and chunks[-1][0] == fmt and len(chunks[-1][1]) < hq.MAX_BATCH:
-            chunks[-1][1].append(i)
+        if runs and runs[-1][0] == fmt:
+            runs[-1][1].append(i)
         else:
-            chunks.append((fmt, [i]))
+            runs.append((fmt, [i]))
+    chunks = []
+    for fmt, idx in runs:
+        parts = -(-len(idx) // hq.MAX_BATCH)
+        per = -(-len(idx) // parts)
+        for k in range(0, len(idx), per):
+            chunks.append((fmt, idx[k:k + per]))
     # the descriptor arrays are marshalled once (host metadata only); a step
     # is then one C-ABI call per launch
     calls = [(fmt, hq.QuantizeBatch([(ins[i], *outs[i]) for i in idx], *fmt, iters=args.iters,

@@ -116,7 +116,8 @@ typedef struct hqq_tensor {
  * set of solve parameters, with results identical to n hqq_quantize calls.
  * This is the pages' whole-model quantization (lnwmold.com HQQ guide section
  * 3.3, AutoHQQHFModel.quantize_model walks a model's Linear layers) in as few
- * kernel launches as possible: up to 24 tensors per launch, so the GPU is not
+ * kernel launches as possible: up to 48 tensors per launch (a call with more is
+ * cut into launches of as even a size as that allows), so the GPU is not
  * idle between small launches and a wave's tail overlaps other tensors' work.
  *   tensors  HOST array of n descriptors (read during the call only)
  * Every descriptor is validated before anything is enqueued.  n = 0 is a

@@ -237,7 +237,7 @@ static void test_certificate()
     free(ze);
 }
 
-// Batched launches: 30 tensors of mixed shapes, every format and axis, small
+// Batched launches: 100 tensors of mixed shapes, every format and axis, small
 // and large (the automatic mapping changes at seg_max_items groups per
 // launch), with the mapping automatic or forced either way.
 static void test_batches()
@@ -254,7 +254,7 @@ static void test_batches()
             for (int64_t scale : {(int64_t)1, (int64_t)40}) {
                 std::vector<hqq_tensor> ts;
                 std::vector<void *> mem;
-                for (int i = 0; i < 30; ++i) {
+                for (int i = 0; i < 100; ++i) {
                     const int64_t lines = 1 + rnd(3000) * scale, other = (int64_t)f[1] * (1 + rnd(40));
                     const int64_t rows = f[2] == 1 ? lines : other, cols = f[2] == 1 ? other : lines;
                     // pointers are only recorded, never dereferenced: one small
@@ -267,7 +267,11 @@ static void test_batches()
                 g_seg.clear();
                 CHECK(hqq_quantize_batch(ts.data(), (int)ts.size(), f[0], f[1], f[2], 20, 0.7f, 10.f, 1.01f,
                                          nullptr) == HQQ_OK);
-                CHECK(g_solve.size() >= 2);
+                CHECK(g_solve.size() >= 3);
+                // launches as even as kMaxBatch allows: 100 tensors -> 34, 33, 33
+                // (more launches only where a launch's workgroups would overflow)
+                for (const hqq::SolveArgs &a : g_solve)
+                    CHECK(a.n <= 34);
                 check_launches(ts, f[0], f[1], f[2]);
                 for (void *p : mem)
                     free(p);

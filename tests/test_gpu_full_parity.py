@@ -50,15 +50,20 @@ def hq():
 
 
 def _launch_chunks(tensors, max_batch):
-    """The benchmark's launches: consecutive tensors of one format, up to
-    max_batch per hqq_quantize_batch call."""
-    chunks = []
+    """The benchmark's launches: runs of consecutive tensors of one format,
+    each cut into as even pieces of at most max_batch as it allows (one
+    hqq_quantize_batch call each)."""
+    runs = []
     for i, t in enumerate(tensors):
         fmt = (t["nbits"], t["group_size"], t["axis"])
-        if chunks and chunks[-1][0] == fmt and len(chunks[-1][1]) < max_batch:
-            chunks[-1][1].append(i)
+        if runs and runs[-1][0] == fmt:
+            runs[-1][1].append(i)
         else:
-            chunks.append((fmt, [i]))
+            runs.append((fmt, [i]))
+    chunks = []
+    for fmt, idx in runs:
+        per = -(-len(idx) // -(-len(idx) // max_batch))
+        chunks += [(fmt, idx[k:k + per]) for k in range(0, len(idx), per)]
     return chunks
 
 

@@ -248,13 +248,14 @@ def test_determinism_and_streams(hq):
 
 @pytest.mark.parametrize("nbits,gs,axis", [(4, 64, 1), (3, 64, 0), (2, 16, 1), (1, 16, 0)])
 def test_batch_equals_single_calls(hq, oracle_mod, nbits, gs, axis):
-    """hqq_quantize_batch over 30 same-format tensors of mixed shapes (two
-    launches) equals per-tensor calls bit for bit, and the oracle on a few."""
+    """hqq_quantize_batch over 60 same-format tensors of mixed shapes (two
+    launches of 30) equals per-tensor calls bit for bit, and the oracle on a
+    few."""
     import torch
 
     rng = np.random.RandomState(nbits * 100 + gs + axis)
     items, Ws = [], []
-    for i in range(30):
+    for i in range(60):
         lines = 1 + rng.randint(0, 40)
         other = gs * (1 + rng.randint(0, 12))
         shape = (lines, other) if axis == 1 else (other, lines)

@@ -86,8 +86,8 @@ def test_streamed_one_chunk_covers_all(hq, oracle_mod):
 
 
 def test_streamed_many_small_tensors_over_batch_limit(hq, oracle_mod):
-    # more than 24 row blocks fit a half: chunks close at 24 pieces
-    _check(hq, oracle_mod, [(8, 64)] * 30, 4, 64, 1, 2 << 20, 7)
+    # more than 48 row blocks fit a half: chunks close at 48 pieces
+    _check(hq, oracle_mod, [(8, 64)] * 60, 4, 64, 1, 2 << 20, 7)
 
 
 def test_streamed_back_to_back_calls_share_staging(hq, oracle_mod):

@@ -37,7 +37,7 @@ EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_q
 DTYPE_FP16, DTYPE_BF16 = 0, 1
 
 # tensors per kernel launch of hqq_quantize_batch
-MAX_BATCH = 24
+MAX_BATCH = 48
 # weights per kernel launch of hqq_linear_batch
 LINEAR_BATCH = 8
 # meta arrays per kernel launch of hqq_quantize_meta_batch / hqq_dequantize_meta_batch
@@ -223,7 +223,7 @@ def hqq_quantize(W: torch.Tensor, nbits: int, group_size: int, axis: int,
 class QuantizeBatch:
     """Several same-format tensors for hqq_quantize_batch, validated and
     marshalled into the C descriptor array once; run() is then a single
-    C-ABI call (one launch per 24 tensors) on the current stream.
+    C-ABI call (one launch per 48 tensors) on the current stream.
     items: list of (W, packed, scale, zero) CUDA tensors (outputs
     preallocated); the tensors are kept alive by the object."""
 

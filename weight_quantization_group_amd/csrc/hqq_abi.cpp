@@ -238,12 +238,15 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
     const int64_t lb = hqq::lcm_c(group_size, C);
     const int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
     const bool seg_ok = hqq::seg_format(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16);
+    // launches of as even a number of tensors as kMaxBatch allows
+    const int launches = (n + hqq::kMaxBatch - 1) / hqq::kMaxBatch;
+    const int per_launch = (n + launches - 1) / launches;
     int i = 0;
     while (i < n) {
         // the tensors of this launch, and its work items
         a.n = 0;
         int64_t items = 0;
-        while (i + a.n < n && a.n < hqq::kMaxBatch) {
+        while (i + a.n < n && a.n < per_launch) {
             const hqq_tensor &t = tensors[i + a.n];
             hqq::SolveTensor &d = a.t[a.n];
             const int64_t L = axis == 1 ? t.cols : t.rows;

@@ -25,8 +25,11 @@ struct SolveTensor {
     double rdiv;         // 1 / (axis 1: nblk, axis 0: cols), for the item -> (line, block) split
 };
 
-// Up to this many same-format tensors share one launch (kernel-argument size).
-constexpr int kMaxBatch = 24;
+// Up to this many same-format tensors share one launch (kernel-argument size:
+// SolveArgs stays within 4 KiB).  Fewer, larger launches leave fewer
+// partially filled ends of a launch: on the 7B stack 48 tensors per launch
+// ran 5.3% faster than 24.
+constexpr int kMaxBatch = 48;
 // Threads per workgroup of the solve kernels.
 constexpr int kSolveBlock = 256;
 // A workgroup solves depth * kSolveBlock work items (depth steps per lane);
@@ -69,6 +72,7 @@ struct SolveArgs {
     int64_t block0[kMaxBatch];   // first workgroup of each tensor (increasing)
     SolveTensor t[kMaxBatch];
 };
+static_assert(sizeof(SolveArgs) <= 4096, "solve kernel arguments within 4 KiB");
 
 struct CodecArgs {
     const uint32_t *packed_in;

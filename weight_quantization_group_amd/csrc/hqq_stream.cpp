@@ -11,7 +11,7 @@
 // before the call (an earlier call's solves may still read the staging
 // buffer), a solve waits for its chunk's copy, and a copy into a half waits
 // for the solve that last read it.  Each chunk is one batched solve launch
-// (up to 24 row blocks), so results are identical to hqq_quantize on device
+// (up to 48 row blocks), so results are identical to hqq_quantize on device
 // copies of the weights.
 #include "hqq.h"
 #include "hqq_internal.h"
