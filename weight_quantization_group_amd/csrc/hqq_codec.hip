@@ -203,9 +203,10 @@ HQQ_DEFINE_LAUNCH(unpack, unpack_kernel)
 // Array of a meta batch that workgroup blk belongs to (uniform; count <= 64).
 __device__ inline int meta_item(const MetaBatch &b, int64_t blk)
 {
+    // a launch has fewer than 2^31 workgroups: 32-bit scalar compares
     int j = 0;
     for (int k = 1; k < b.count; ++k)
-        j = blk >= b.block0[k] ? k : j;
+        j = (uint32_t)blk >= (uint32_t)b.block0[k] ? k : j;
     return j;
 }
 

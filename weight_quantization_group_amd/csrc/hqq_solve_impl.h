@@ -1083,11 +1083,12 @@ void solve_kernel(SolveArgs a)
     __shared__ Stage<GS, AXIS> stage[kWaves];
 
     // the launch's tensor of this workgroup: block0 is increasing and
-    // tensors start on workgroup boundaries (uniform, no dependent loads)
+    // tensors start on workgroup boundaries (uniform, no dependent loads;
+    // a launch has fewer than 2^31 workgroups, so 32-bit scalar compares)
     int ti = 0;
 #pragma unroll
     for (int j = 1; j < kMaxBatch; ++j)
-        ti += (j < a.n && (int64_t)blockIdx.x >= a.block0[j]) ? 1 : 0;
+        ti = (j < a.n && blockIdx.x >= (uint32_t)a.block0[j]) ? j : ti;
     const SolveTensor &T = a.t[ti];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     Stage<GS, AXIS> &st = stage[wave];

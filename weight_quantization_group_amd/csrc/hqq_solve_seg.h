@@ -93,7 +93,7 @@ void solve_seg_kernel(SolveArgs a)
     int ti = 0;
 #pragma unroll
     for (int j = 1; j < kMaxBatch; ++j)
-        ti += (j < a.n && (int64_t)blockIdx.x >= a.block0[j]) ? 1 : 0;
+        ti = (j < a.n && blockIdx.x >= (uint32_t)a.block0[j]) ? j : ti;
     ti = __builtin_amdgcn_readfirstlane(ti);
     const SolveTensor &T = a.t[ti];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
