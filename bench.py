@@ -296,12 +296,15 @@ def bench_linear(args):
     outs = [torch.empty((M, N), dtype=cdt, device=dev) for (N, K) in LLAMA7B_LINEARS]
     calls = []
     # one workspace for every call (they run in order on one stream): the
-    # tiled kernel may split K for many rows (hqq_linear_batch_ws)
+    # tiled kernel may split K for many rows, and from 256 rows the library
+    # dequantizes each weight into it and runs a GEMM (hqq_linear_batch_ws);
+    # the largest W_hat is 11008 x 4096 (gate, up; down is 4096 x 11008)
     groups = ((0, 1, 2), (3,), (4, 5), (6,))
     work = None
     if M > 1 and not args.no_split:
         nmax = max(sum(LLAMA7B_LINEARS[i][0] for i in idx) for idx in groups)
-        work = torch.empty(hq.linear_workspace_bytes(M, [nmax]) // 4, dtype=torch.float32, device=dev)
+        wbytes = max(hq.linear_workspace_bytes(M, [nmax]), hq.linear_workspace_bytes(M, [11008], 4096))
+        work = torch.empty(wbytes // 4, dtype=torch.float32, device=dev)
     for li in range(LLAMA7B_LAYERS):
         ly = layers[li * nl:(li + 1) * nl]
         for idx in groups:
@@ -421,9 +424,13 @@ def bench_linear(args):
         # bf16 inputs, fp32 accumulation)
         flops = 2.0 * M * LLAMA7B_WEIGHTS
         tfs = flops / (ms_ev * 1e-3) / 1e12
+        # the route the library takes for the largest call (gate and up)
+        wb = work.numel() * work.element_size() if work is not None else 0
+        gemm = hq.hqq_linear_route(M, 4096, 2, 11008, wb) == hq.ROUTE_GEMM
         roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tfs / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "linear_tiled_kernel (4-bit, g64)" if M > 32 else "linear_skinny_kernel (4-bit, g64)",
+                    "kernel": ("dequant_kernel + hipBLASLt GEMM (4-bit, g64)" if gemm else
+                               "linear_tiled_kernel (4-bit, g64)" if M > 32 else "linear_skinny_kernel (4-bit, g64)"),
                     "flops_per_step": flops}
     out = {
         "metric": metric if args.cdtype == "f16" else metric + ", compute dtype bf16",
@@ -690,7 +697,7 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="--op linear: plain launches instead of a captured HIP graph")
     ap.add_argument("--no-split", action="store_true",
-                    help="--op linear: no workspace, so the tiled kernel never splits K")
+                    help="--op linear: no workspace: the fused kernels only, without K splits")
     ap.add_argument("--op", choices=("solve", "linear", "streamed", "meta"), default="solve",
                     help="solve: quantize the 7B stack (default); linear: one decode token "
                          "through the quantized layers; streamed: the solve from pinned host memory")

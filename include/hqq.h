@@ -351,21 +351,49 @@ HQQ_API int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_
                              int count, int nbits, int group_size, int dtype, void *stream);
 
 /* hqq_linear_batch with a caller's device workspace (16-byte aligned,
- * workspace_bytes long; NULL with 0 bytes is hqq_linear_batch).  For a batch
- * of many rows (prefill chunks, lnwmold.com HQQ guide section 4.2) whose
- * output tiles are too few to occupy the device, the tiled kernel may split
- * K in 2, 4 or 8 parts: each part's fp32 partial products go to the
- * workspace (splits x M x sum of N floats; the launcher takes the most
- * splits the workspace holds when its time estimate is lower) and a second
- * launch adds them in split order in fp32 and rounds each output once to
- * the compute dtype.  The results stay within hqq_linear's bound (fp32 sums
- * in some order) but need not equal hqq_linear_batch's bit for bit.  The
- * workspace is in use until the stream reaches the end of the call's work.
- * A misaligned workspace, negative bytes, or bytes with a NULL workspace:
- * HQQ_EINVAL_PTR. */
+ * workspace_bytes long; NULL with 0 bytes is hqq_linear_batch).  Two uses,
+ * for batches of many rows (prefill chunks, lnwmold.com HQQ guide section
+ * 4.2; section 4.1: a backend fuses the dequantization into the product or
+ * dequantizes and runs a dense GEMM):
+ *  - where the workspace holds the largest weight's W_hat (N x K values of
+ *    the compute dtype, rounded up to 256 bytes) and the batch has many rows
+ *    (see hqq_linear_route), each weight is dequantized into it exactly as
+ *    hqq_dequantize_ex writes W_hat, and one hipBLASLt GEMM with fp32
+ *    accumulation forms Y = X . W_hat^T; the rest of the workspace is the
+ *    GEMM's.  The first such call on a device creates a hipBLASLt handle and
+ *    the call's plan (kept until the process ends; make it outside stream
+ *    capture).  Where hipBLASLt offers no algorithm for a shape, the fused
+ *    kernels run.
+ *  - otherwise the fused kernels run; for output tiles too few to occupy the
+ *    device the tiled kernel may split K in 2, 4 or 8 parts: each part's fp32
+ *    partial products go to the workspace (splits x M x sum of N floats; the
+ *    launcher takes the most splits the workspace holds when its time
+ *    estimate is lower) and a second launch adds them in split order in fp32
+ *    and rounds each output once to the compute dtype.
+ * Either way the results stay within hqq_linear's bound (fp32 sums of the
+ * exact products in some order, rounded once) but need not equal
+ * hqq_linear_batch's bit for bit.  The environment variable
+ * HQQ_LINEAR_PATH=fused or =gemm, read at each call, forces a route (gemm
+ * only where the workspace holds W_hat).  The workspace is in use until the
+ * stream reaches the end of the call's work.  A misaligned workspace,
+ * negative bytes, or bytes with a NULL workspace: HQQ_EINVAL_PTR. */
 HQQ_API int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws,
                                 int count, int nbits, int group_size, int dtype, void *workspace,
                                 int64_t workspace_bytes, void *stream);
+
+/* Which route hqq_linear_batch_ws takes (host query, no GPU call) for M rows,
+ * depth K, count weights of at most n_max outputs and a workspace of
+ * workspace_bytes: HQQ_ROUTE_GEMM (dequantize, then a hipBLASLt GEMM) where
+ * the workspace holds n_max x K 2-byte values rounded up to 256 bytes and
+ * M >= 2048, or count = 1, K <= 4096 and M >= 1024 (measured on MI355X at
+ * the 7B shapes: there the dense GEMM on W_hat is the faster; below, the
+ * fused kernels are as fast or faster), else HQQ_ROUTE_FUSED;
+ * HQQ_LINEAR_PATH as for that call.  The call itself still runs the fused
+ * kernels where hipBLASLt has no algorithm.  M, K, count or n_max < 1:
+ * HQQ_EINVAL_SHAPE; workspace_bytes < 0: HQQ_EINVAL_PTR. */
+#define HQQ_ROUTE_FUSED 0
+#define HQQ_ROUTE_GEMM 1
+HQQ_API int hqq_linear_route(int64_t M, int64_t K, int count, int64_t n_max, int64_t workspace_bytes);
 
 /* Number of uint32 words of the packed layout; a negative HQQ_E* status for
  * invalid arguments.  Host only, no HIP call. */

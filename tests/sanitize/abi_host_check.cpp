@@ -30,6 +30,16 @@ static int g_fail = 0;
 static std::vector<hqq::SolveArgs> g_solve;
 static std::vector<bool> g_seg;
 
+// linear layer routes: a log of (kind, weight's Y or W_hat, ...) in call order
+struct LinCall {
+    char kind;   // 'd' dequantize, 'g' GEMM, 'f' fused launch
+    const void *a, *b;
+    int64_t M, N, K;
+    size_t ws;
+};
+static std::vector<LinCall> g_lin;
+static bool g_gemm_ok = true;
+
 namespace hqq {
 hipError_t launch_solve(int nbits, int gs, int axis, bool bf16, bool seg, const SolveArgs &a, hipStream_t)
 {
@@ -39,10 +49,27 @@ hipError_t launch_solve(int nbits, int gs, int axis, bool bf16, bool seg, const 
     g_seg.push_back(seg);
     return hipSuccess;
 }
-hipError_t launch_dequantize(int, int, const CodecArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t)
+{
+    g_lin.push_back({'d', a.packed_in, a.W_hat, a.rows, nbits, axis, (size_t)a.n_words});
+    return hipSuccess;
+}
 hipError_t launch_pack(int, int, const CodecArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_unpack(int, int, const CodecArgs &, hipStream_t) { return hipSuccess; }
-hipError_t launch_linear(int, bool, LinearBatch &, hipStream_t) { return hipSuccess; }
+hipError_t launch_linear(int, bool, LinearBatch &b, hipStream_t)
+{
+    g_lin.push_back({'f', b.Y[0], nullptr, b.a.M, b.count, b.a.K, 0});
+    return hipSuccess;
+}
+bool gemm_available(int64_t, int64_t, int64_t, bool, size_t) { return g_gemm_ok; }
+hipError_t gemm_xwt(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, bool, void *ws,
+                    size_t ws_bytes, hipStream_t)
+{
+    g_lin.push_back({'g', Y, W, M, N, K, ws_bytes});
+    (void)X;
+    (void)ws;
+    return hipSuccess;
+}
 hipError_t launch_quantize_meta(MetaBatch &, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_dequantize_meta(MetaBatch &, int, hipStream_t) { return hipSuccess; }
 }  // namespace hqq
@@ -422,8 +449,73 @@ static void test_streamed_static()
     free(big.zero);
 }
 
+// The linear layer's route: dequantize + GEMM per weight where the workspace
+// holds the largest W_hat and M >= 2048 (or HQQ_LINEAR_PATH=gemm), the fused
+// launch otherwise (also when hipBLASLt has no algorithm); W_hat at the
+// workspace's start, the GEMM's workspace after it (256-byte rounded).  A
+// batch of three weights here, so the one-weight threshold does not apply.
+static void test_linear_routes()
+{
+    const int64_t K = 4096;
+    const int64_t Ns[3] = {4096, 11008, 1024};
+    uint16_t *X = (uint16_t *)aligned(256);
+    char *work = (char *)aligned(1 << 20);
+    std::vector<hqq_linear_weight> w;
+    std::vector<void *> mem{X, work};
+    for (int i = 0; i < 3; ++i) {
+        void *p = aligned(256);
+        mem.push_back(p);
+        w.push_back(hqq_linear_weight{(const uint32_t *)p, (const float *)p, (const float *)p, Ns[i],
+                                      (uint16_t *)aligned(256)});
+        mem.push_back(w.back().Y);
+    }
+    const int64_t what = (11008 * K * 2 + 255) / 256 * 256;
+    const int64_t big = what + (32 << 20);   // bytes claimed (the stubs never touch them)
+    struct Case {
+        const char *env;
+        int64_t M, bytes;
+        bool gemm_ok;
+        bool want_gemm;
+    } cases[] = {
+        {nullptr, 2048, big, true, true},    {nullptr, 2047, big, true, false},
+        {nullptr, 1024, big, true, false},   {nullptr, 2048, what, true, true},
+        {nullptr, 2048, what - 256, true, false}, {nullptr, 2048, 0, true, false},
+        {"fused", 2048, big, true, false},   {"gemm", 1, big, true, true},
+        {"gemm", 64, what - 1, true, false}, {nullptr, 4096, big, false, false},
+    };
+    for (const Case &c : cases) {
+        if (c.env)
+            setenv("HQQ_LINEAR_PATH", c.env, 1);
+        else
+            unsetenv("HQQ_LINEAR_PATH");
+        g_gemm_ok = c.gemm_ok;
+        g_lin.clear();
+        CHECK(hqq_linear_batch_ws(X, c.M, K, w.data(), 3, 4, 64, HQQ_DTYPE_FP16, c.bytes ? work : nullptr, c.bytes,
+                                  nullptr) == HQQ_OK);
+        if (c.want_gemm) {
+            CHECK(g_lin.size() == 6);
+            for (size_t i = 0; i + 1 < g_lin.size() && i < 6; i += 2) {
+                const int j = (int)(i / 2);
+                CHECK(g_lin[i].kind == 'd' && g_lin[i].a == w[j].packed && g_lin[i].b == work &&
+                      g_lin[i].M == Ns[j] && g_lin[i].N == 4 && g_lin[i].K == 1 &&
+                      (int64_t)g_lin[i].ws == hqq_packed_words(Ns[j], K, 4, 1));
+                CHECK(g_lin[i + 1].kind == 'g' && g_lin[i + 1].a == w[j].Y && g_lin[i + 1].b == work &&
+                      g_lin[i + 1].M == c.M && g_lin[i + 1].N == Ns[j] && g_lin[i + 1].K == K &&
+                      (int64_t)g_lin[i + 1].ws == c.bytes - what);
+            }
+        } else {
+            CHECK(g_lin.size() == 1 && g_lin[0].kind == 'f' && g_lin[0].N == 3);
+        }
+    }
+    unsetenv("HQQ_LINEAR_PATH");
+    g_gemm_ok = true;
+    for (void *p : mem)
+        free(p);
+}
+
 int main()
 {
+    test_linear_routes();
     test_validation();
     test_certificate();
     test_batches();

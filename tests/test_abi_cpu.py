@@ -62,7 +62,7 @@ def test_exports_every_declared_symbol(lib):
                                "hqq_pack", "hqq_unpack", "hqq_quantize_meta", "hqq_dequantize_meta",
                                "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear",
                                "hqq_linear_ex", "hqq_linear_batch", "hqq_linear_batch_ws", "hqq_solve_mapping",
-                               "hqq_packed_words",
+                               "hqq_linear_route", "hqq_packed_words",
                                "hqq_strerror"])
     for name in declared:
         assert hasattr(lib, name), name
@@ -71,6 +71,35 @@ def test_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
     exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
     assert exported == declared, exported
+
+
+def test_linear_route(lib, monkeypatch):
+    """The linear route query: dequantize + GEMM from 2048 rows, or from 1024
+    rows for one weight with K <= 4096, where the workspace holds the largest
+    W_hat (256-byte rounded); as forced by HQQ_LINEAR_PATH; invalid arguments
+    give the usual status codes."""
+    monkeypatch.delenv("HQQ_LINEAR_PATH", raising=False)
+    what = (4096 * 4096 * 2 + 255) // 256 * 256
+    assert lib.hqq_linear_route(2048, 4096, 3, 4096, what) == 1
+    assert lib.hqq_linear_route(2047, 4096, 3, 4096, what) == 0
+    assert lib.hqq_linear_route(1024, 4096, 1, 4096, what) == 1
+    assert lib.hqq_linear_route(1023, 4096, 1, 4096, what) == 0
+    assert lib.hqq_linear_route(1024, 4096, 2, 4096, what) == 0
+    assert lib.hqq_linear_route(1024, 4097, 1, 4096, 2 * what) == 0
+    assert lib.hqq_linear_route(2048, 4096, 1, 4096, what - 1) == 0
+    assert lib.hqq_linear_route(2048, 4096, 1, 4096, 0) == 0
+    assert lib.hqq_linear_route(2048, 100, 1, 3, 768) == 1          # 600 bytes round up to 768
+    assert lib.hqq_linear_route(2048, 100, 1, 3, 767) == 0
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "fused")
+    assert lib.hqq_linear_route(4096, 4096, 1, 4096, what) == 0
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "gemm")
+    assert lib.hqq_linear_route(1, 4096, 5, 4096, what) == 1
+    assert lib.hqq_linear_route(1, 4096, 1, 4096, what - 1) == 0
+    assert lib.hqq_linear_route(0, 4096, 1, 4096, what) == -4
+    assert lib.hqq_linear_route(1, 0, 1, 4096, what) == -4
+    assert lib.hqq_linear_route(1, 4096, 0, 4096, what) == -4
+    assert lib.hqq_linear_route(1, 4096, 1, 0, what) == -4
+    assert lib.hqq_linear_route(1, 4096, 1, 4096, -1) == -5
 
 
 def test_solve_mapping(lib, monkeypatch):

@@ -397,6 +397,7 @@ def test_linear_split_k(hq, oracle_mod, monkeypatch, M, K, nbits, gs, Ns, splits
     if splits > 1 and (splits - 1) * per >= steps:
         pytest.skip("a split would be empty: the launcher does not use this count")
     monkeypatch.setenv("HQQ_LINEAR_SPLITS", str(splits))
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "fused")   # the split-K kernels, not the GEMM route
     rng = np.random.RandomState(M + K * 3 + nbits + gs + len(Ns) * 101)
     X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
     Xd = _cuda(X16)
@@ -416,18 +417,104 @@ def test_linear_split_k(hq, oracle_mod, monkeypatch, M, K, nbits, gs, Ns, splits
             assert torch.equal(Y.view(torch.int16), R.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [128, 256, 512])
-def test_linear_workspace_auto_mid_rows(hq, oracle_mod, M):
-    """With a workspace and the launcher's own choice (few output tiles: it
-    splits K), the outputs meet the bound."""
+@pytest.mark.parametrize("M", [128, 256, 512, 1024])
+def test_linear_workspace_auto_mid_rows(hq, oracle_mod, monkeypatch, M):
+    """With a workspace and the library's own choice (up to 512 rows the
+    fused kernels, which split K over few output tiles; at 1024 rows one
+    weight with K <= 4096 takes dequantize + GEMM), the outputs meet the
+    bound."""
     import torch
 
     K, N, nbits, gs = 1024, 512, 4, 64
     rng = np.random.RandomState(M + 7)
     X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
     p, s, z = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
-    work = torch.empty(hq.linear_workspace_bytes(M, [N]) // 4, dtype=torch.float32, device="cuda")
+    monkeypatch.delenv("HQQ_LINEAR_PATH", raising=False)
+    wb = hq.linear_workspace_bytes(M, [N], K)
+    assert hq.hqq_linear_route(M, K, 1, N, wb) == (hq.ROUTE_GEMM if M >= 1024 else hq.ROUTE_FUSED)
+    work = torch.empty(wb // 4, dtype=torch.float32, device="cuda")
     (Y,) = hq.hqq_linear_batch(_cuda(X16), [(_cuda(p), _cuda(s), _cuda(z), N)], nbits, gs, workspace=work)
     torch.cuda.synchronize()
     Yref, A = oracle_mod.linear(X16, p, s, z, N, nbits, gs, with_abs=True)
     check(Y.cpu().numpy(), Yref, A, K, f"auto {M}x{N}x{K}")
+
+
+# The dequantize-then-GEMM route of hqq_linear_batch_ws: each weight's W_hat
+# (bit-exact, as hqq_dequantize writes it) goes to the workspace and a
+# hipBLASLt GEMM with fp32 accumulation forms X . W_hat^T, so each output is
+# an fp32 sum of the exact products in some order, rounded once: the same
+# bound as the fused kernels.
+
+GEMM_CASES = [
+    # M, K, nbits, gs, Ns
+    (1, 256, 4, 64, [128]),
+    (33, 128, 1, 32, [96]),
+    (64, 1024, 2, 32, [300, 64]),            # two weights, N not a multiple of 8
+    (300, 512, 8, 128, [256]),
+    (256, 4096, 4, 64, [1024, 512]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("M,K,nbits,gs,Ns", GEMM_CASES)
+def test_linear_gemm_route(hq, oracle_mod, monkeypatch, M, K, nbits, gs, Ns, dtype):
+    import torch
+
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "gemm")
+    rng = np.random.RandomState(M * 7 + K + nbits * 3 + gs + len(Ns))
+    if dtype == "bf16":
+        Xh = random_bf16(rng, (M, K))
+        Xd = torch.from_numpy(Xh.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        Xh = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+        Xd = _cuda(Xh)
+    ws = [random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False) for N in Ns]
+    dev = [(_cuda(p), _cuda(s), _cuda(z), N) for (p, s, z), N in zip(ws, Ns)]
+    work = torch.empty(hq.linear_workspace_bytes(M, Ns, K) // 4, dtype=torch.float32, device="cuda")
+    work.fill_(float("nan"))   # stale contents must not leak into the outputs
+    outs = hq.hqq_linear_batch(Xd, dev, nbits, gs, workspace=work)
+    torch.cuda.synchronize()
+    for (p, s, z), N, Y in zip(ws, Ns, outs):
+        tag = f"gemm {dtype} {M}x{N}x{K} b{nbits} g{gs}"
+        if dtype == "bf16":
+            Yref, A = oracle_mod.linear(Xh, p, s, z, N, nbits, gs, with_abs=True, dtype="bf16")
+            check_bf16(Y.view(torch.int16).cpu().numpy().view(np.uint16), Yref, A, K, tag)
+        else:
+            Yref, A = oracle_mod.linear(Xh, p, s, z, N, nbits, gs, with_abs=True)
+            check(Y.cpu().numpy(), Yref, A, K, tag)
+
+
+def test_linear_gemm_route_identity_gives_w_hat(hq, oracle_mod, monkeypatch):
+    """X = I through the GEMM route: Y = W_hat^T, bit for bit (one nonzero
+    product per output)."""
+    import torch
+
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "gemm")
+    rng = np.random.RandomState(3)
+    K, N, nbits, gs = 256, 192, 4, 64
+    packed, scale, zero = random_quantized(oracle_mod, rng, N, K, nbits, gs)
+    X = np.eye(K, dtype=np.float16).view(np.uint16)
+    work = torch.empty(hq.linear_workspace_bytes(K, [N], K) // 4, dtype=torch.float32, device="cuda")
+    (Y,) = hq.hqq_linear_batch(_cuda(X), [(_cuda(packed), _cuda(scale), _cuda(zero), N)], nbits, gs,
+                               workspace=work)
+    torch.cuda.synchronize()
+    W = oracle_mod.dequantize(packed, scale, zero, N, K, nbits, gs, 1)
+    assert np.array_equal(Y.cpu().numpy().view(np.uint16), np.ascontiguousarray(W.T))
+
+
+def test_linear_gemm_route_without_room_is_fused(hq, oracle_mod, monkeypatch):
+    """A workspace too small for W_hat: the fused kernels run (bit-identical to
+    the workspace-free call), whatever HQQ_LINEAR_PATH asks."""
+    import torch
+
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "gemm")
+    rng = np.random.RandomState(4)
+    M, K, N, nbits, gs = 64, 512, 256, 4, 64
+    X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+    p, s, z = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    dev = [(_cuda(p), _cuda(s), _cuda(z), N)]
+    small = torch.empty((N * K * 2 - 256) // 4, dtype=torch.float32, device="cuda")
+    (Y,) = hq.hqq_linear_batch(_cuda(X16), dev, nbits, gs, workspace=small)
+    (R,) = hq.hqq_linear_batch(_cuda(X16), dev, nbits, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), R.view(torch.int16))

@@ -31,7 +31,7 @@ EXPORTS = ("hqq_quantize", "hqq_quantize_batch", "hqq_quantize_batch_ex", "hqq_q
            "hqq_quantize_streamed_static",
            "hqq_dequantize", "hqq_dequantize_ex", "hqq_pack", "hqq_unpack", "hqq_quantize_meta",
            "hqq_dequantize_meta", "hqq_quantize_meta_batch", "hqq_dequantize_meta_batch", "hqq_linear", "hqq_linear_ex", "hqq_linear_batch",
-           "hqq_linear_batch_ws", "hqq_solve_mapping", "hqq_packed_words", "hqq_strerror")
+           "hqq_linear_batch_ws", "hqq_solve_mapping", "hqq_linear_route", "hqq_packed_words", "hqq_strerror")
 
 # element types of include/hqq.h
 DTYPE_FP16, DTYPE_BF16 = 0, 1
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH):
     L.hqq_linear_batch_ws.restype = i32
     L.hqq_solve_mapping.argtypes = [i32, i32, i32, i32, i64]
     L.hqq_solve_mapping.restype = i32
+    L.hqq_linear_route.argtypes = [i64, i64, i32, i64, i64]
+    L.hqq_linear_route.restype = i32
     L.hqq_packed_words.argtypes = [i64, i64, i32, i32]
     L.hqq_packed_words.restype = i64
     L.hqq_strerror.argtypes = [i32]
@@ -143,6 +145,19 @@ def hqq_solve_mapping(nbits: int, group_size: int, axis: int, wdtype: int, work_
 
 
 MAPPING_LANE, MAPPING_SEG = 0, 1
+
+
+def hqq_linear_route(M: int, K: int, count: int, n_max: int, workspace_bytes: int) -> int:
+    """ROUTE_FUSED or ROUTE_GEMM: the route hqq_linear_batch_ws takes for M
+    rows, depth K, count weights of at most n_max outputs and the workspace
+    size."""
+    r = load_library().hqq_linear_route(M, K, count, n_max, workspace_bytes)
+    if r < 0:
+        raise HQQError("hqq_linear_route", r)
+    return int(r)
+
+
+ROUTE_FUSED, ROUTE_GEMM = 0, 1
 
 
 def hqq_packed_words(rows: int, cols: int, nbits: int, axis: int) -> int:
@@ -338,8 +353,8 @@ class LinearBatch:
     launch per 8 weights) on the current stream.  weights: list of (packed,
     scale, zero, N, Y) with Y a preallocated fp16 [M, N] CUDA tensor; the
     tensors are kept alive by the object.  workspace: an optional CUDA tensor
-    the tiled kernel may use to split K (hqq_linear_batch_ws); see
-    linear_workspace_bytes."""
+    for hqq_linear_batch_ws (the tiled kernel's K splits, or W_hat and the
+    GEMM of the dequantize-then-GEMM route); see linear_workspace_bytes."""
 
     def __init__(self, weights, nbits: int, group_size: int, dtype=torch.float16, workspace=None):
         self._lib = load_library()
@@ -376,10 +391,19 @@ class LinearBatch:
         return [it[4] for it in self._items]
 
 
-def linear_workspace_bytes(M: int, Ns) -> int:
-    """Workspace for the most K splits (8) of hqq_linear_batch_ws over
-    weights of output sizes Ns on M rows."""
-    return 8 * M * sum(Ns) * 4
+GEMM_WORKSPACE_BYTES = 32 << 20
+
+
+def linear_workspace_bytes(M: int, Ns, K: int | None = None) -> int:
+    """Workspace for hqq_linear_batch_ws over weights of output sizes Ns on M
+    rows: the most K splits (8) of the fused kernels, and, given K, room for
+    the dequantize-then-GEMM route (the largest W_hat, max(Ns) x K 2-byte
+    values rounded up to 256 bytes, plus GEMM_WORKSPACE_BYTES for the GEMM)."""
+    split = 8 * M * sum(Ns) * 4
+    if K is None:
+        return split
+    what = -(-max(Ns) * K * 2 // 256) * 256
+    return max(split, what + GEMM_WORKSPACE_BYTES)
 
 
 def hqq_linear_batch(X: torch.Tensor, weights, nbits: int, group_size: int, workspace=None):

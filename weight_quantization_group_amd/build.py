@@ -26,7 +26,7 @@ SOURCES = ["hqq_abi.cpp", "hqq_stream.cpp", "hqq_solve.hip", "hqq_solve_b1.hip",
            "hqq_solve_b3.hip", "hqq_solve_b4.hip", "hqq_solve_b8.hip",
            "hqq_solve_b1_bf16.hip", "hqq_solve_b2_bf16.hip", "hqq_solve_b3_bf16.hip",
            "hqq_solve_b4_bf16.hip", "hqq_solve_b8_bf16.hip", "hqq_codec.hip",
-           "hqq_linear.hip"]
+           "hqq_linear.hip", "hqq_gemm.cpp"]
 
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
@@ -49,7 +49,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -396,6 +396,38 @@ int hqq_linear_batch(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_w
     return hqq_linear_batch_ws(X, M, K, ws, count, nbits, group_size, dtype, nullptr, 0, stream);
 }
 
+namespace {
+
+// The linear layer's two routes: the fused kernels, or, where the caller's
+// workspace holds the largest weight's W_hat (fp16 or bf16 [N, K], rounded up
+// to 256 bytes), each weight dequantized into it and multiplied by one
+// hipBLASLt GEMM (the rest of the workspace is the GEMM's).  Measured on
+// MI355X (4-bit g64, the 7B shapes, graph-replayed calls), dequantize + GEMM
+// is the faster route for every call from kGemmMinRows rows (one weight or a
+// q/k/v or gate/up batch), and for one weight with K <= 4096 from
+// kGemmMinRowsOne rows; below, the fused kernels (whose tiles span all weights
+// of a batch) are as fast or faster.  HQQ_LINEAR_PATH=fused or =gemm forces a
+// route (gemm only where the workspace allows it; tests run both on the same
+// inputs).
+constexpr int64_t kGemmMinRows = 2048;
+constexpr int64_t kGemmMinRowsOne = 1024;
+
+int64_t what_bytes(int64_t n_max, int64_t K) { return (n_max * K * 2 + 255) / 256 * 256; }
+
+bool use_gemm_route(int64_t M, int64_t K, int count, int64_t n_max, const void *workspace, int64_t workspace_bytes)
+{
+    if (!workspace || workspace_bytes < what_bytes(n_max, K))
+        return false;
+    const char *e = getenv("HQQ_LINEAR_PATH");
+    if (e && strcmp(e, "fused") == 0)
+        return false;
+    if (e && strcmp(e, "gemm") == 0)
+        return true;
+    return M >= kGemmMinRows || (count == 1 && K <= 4096 && M >= kGemmMinRowsOne);
+}
+
+}  // namespace
+
 int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linear_weight *ws, int count,
                         int nbits, int group_size, int dtype, void *workspace, int64_t workspace_bytes,
                         void *stream)
@@ -435,6 +467,38 @@ int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linea
             return HQQ_EINVAL_PTR;
     if (workspace_bytes < 0 || (workspace && !aligned16(workspace)) || (!workspace && workspace_bytes > 0))
         return HQQ_EINVAL_PTR;
+    const bool bf16 = dtype == HQQ_DTYPE_BF16;
+    int64_t n_max = 0;
+    for (int i = 0; i < count; ++i)
+        n_max = ws[i].N > n_max ? ws[i].N : n_max;
+    if (count > 0 && use_gemm_route(M, K, count, n_max, workspace, workspace_bytes)) {
+        const int64_t wb = what_bytes(n_max, K);
+        uint16_t *W_hat = reinterpret_cast<uint16_t *>(workspace);
+        char *rest = reinterpret_cast<char *>(workspace) + wb;
+        const size_t rest_bytes = (size_t)(workspace_bytes - wb);
+        bool ok = true;
+        for (int i = 0; i < count && ok; ++i)
+            ok = hqq::gemm_available(M, ws[i].N, K, bf16, rest_bytes);
+        if (ok) {
+            for (int i = 0; i < count; ++i) {
+                hqq::CodecArgs ca{};
+                ca.packed_in = ws[i].packed;
+                ca.scale = ws[i].scale;
+                ca.zero = ws[i].zero;
+                ca.W_hat = W_hat;
+                ca.out_bf16 = bf16;
+                ca.rows = ws[i].N;
+                ca.cols = K;
+                ca.group_size = group_size;
+                ca.n_words = hqq_packed_words(ws[i].N, K, nbits, 1);
+                if (hqq::launch_dequantize(nbits, 1, ca, (hipStream_t)stream) != hipSuccess ||
+                    hqq::gemm_xwt(X, W_hat, ws[i].Y, M, ws[i].N, K, bf16, rest_bytes ? rest : nullptr, rest_bytes,
+                                  (hipStream_t)stream) != hipSuccess)
+                    return HQQ_EHIP;
+            }
+            return HQQ_OK;
+        }
+    }
     hqq::LinearBatch b{};
     b.work = reinterpret_cast<float *>(workspace);
     b.work_floats = workspace ? workspace_bytes / 4 : 0;
@@ -461,6 +525,19 @@ int hqq_linear_batch_ws(const uint16_t *X, int64_t M, int64_t K, const hqq_linea
             return HQQ_EHIP;
     }
     return HQQ_OK;
+}
+
+int hqq_linear_route(int64_t M, int64_t K, int count, int64_t n_max, int64_t workspace_bytes)
+{
+    if (M < 1 || K < 1 || count < 1 || n_max < 1)
+        return HQQ_EINVAL_SHAPE;
+    if (workspace_bytes < 0)
+        return HQQ_EINVAL_PTR;
+    // the rule looks at the workspace's size only; any non-null stands in
+    static const char stand_in = 0;
+    return use_gemm_route(M, K, count, n_max, workspace_bytes ? &stand_in : nullptr, workspace_bytes)
+               ? HQQ_ROUTE_GEMM
+               : HQQ_ROUTE_FUSED;
 }
 
 int hqq_linear_ex(const uint16_t *X, int64_t M, int64_t K, const uint32_t *packed,

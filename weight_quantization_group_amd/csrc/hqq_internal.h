@@ -136,6 +136,12 @@ hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_unpack(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_linear(int nbits, bool bf16, LinearBatch &b, hipStream_t s);
+// Y [M, N] = X [M, K] . W [N, K]^T, row-major fp16 (or bf16) through hipBLASLt;
+// ws: workspace the library's algorithm may use (hqq_gemm.cpp).  gemm_available:
+// whether hipBLASLt has an algorithm for the shape within ws_bytes.
+bool gemm_available(int64_t M, int64_t N, int64_t K, bool bf16, size_t ws_bytes);
+hipError_t gemm_xwt(const void *X, const void *W, void *Y, int64_t M, int64_t N, int64_t K, bool bf16,
+                    void *ws, size_t ws_bytes, hipStream_t s);
 // meta arrays per launch of the meta kernels (descriptors by value)
 constexpr int kMetaBatch = 64;
 
