@@ -518,3 +518,29 @@ def test_linear_gemm_route_without_room_is_fused(hq, oracle_mod, monkeypatch):
     (R,) = hq.hqq_linear_batch(_cuda(X16), dev, nbits, gs)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), R.view(torch.int16))
+
+
+def test_linear_gemm_route_many_row_counts(hq, oracle_mod, monkeypatch):
+    """300 distinct row counts through the GEMM route: more shapes than the
+    library keeps plans for, so its plan cache starts over on the way; the
+    outputs before and after meet the bound."""
+    import torch
+
+    monkeypatch.setenv("HQQ_LINEAR_PATH", "gemm")
+    rng = np.random.RandomState(12)
+    K, N, nbits, gs = 128, 64, 4, 64
+    p, s, z = random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False)
+    dev = [(_cuda(p), _cuda(s), _cuda(z), N)]
+    X16 = random_f16(rng, (300, K), std=1.0, outlier_frac=0.0)
+    Xd = _cuda(X16)
+    work = torch.empty(hq.linear_workspace_bytes(300, [N], K) // 4, dtype=torch.float32, device="cuda")
+    checked = 0
+    for M in range(1, 301):
+        (Y,) = hq.hqq_linear_batch(Xd[:M], dev, nbits, gs, workspace=work)
+        if M in (1, 7, 255, 256, 257, 300):
+            torch.cuda.synchronize()
+            Yref, A = oracle_mod.linear(X16[:M], p, s, z, N, nbits, gs, with_abs=True)
+            check(Y.cpu().numpy(), Yref, A, K, f"gemm route M={M}")
+            checked += 1
+    torch.cuda.synchronize()
+    assert checked == 6

@@ -36,6 +36,22 @@ using PlanKey = std::tuple<int, int64_t, int64_t, int64_t, bool, size_t>;
 std::mutex g_mu;
 std::map<int, hipblasLtHandle_t> g_handle;
 std::map<PlanKey, GemmPlan> g_plan;
+// plans kept at most (M is part of the key: callers with varying row counts
+// would otherwise grow the map without bound); past it the map starts over
+constexpr size_t kMaxPlans = 256;
+
+void destroy(GemmPlan &p)
+{
+    if (p.c)
+        hipblasLtMatrixLayoutDestroy(p.c);
+    if (p.b)
+        hipblasLtMatrixLayoutDestroy(p.b);
+    if (p.a)
+        hipblasLtMatrixLayoutDestroy(p.a);
+    if (p.desc)
+        hipblasLtMatmulDescDestroy(p.desc);
+    p = GemmPlan{};
+}
 
 bool make_plan(hipblasLtHandle_t h, int64_t M, int64_t N, int64_t K, bool bf16, size_t ws_cap, GemmPlan &p)
 {
@@ -90,8 +106,16 @@ const GemmPlan *plan_for(int64_t M, int64_t N, int64_t K, bool bf16, size_t ws_b
     const PlanKey key{dev, M, N, K, bf16, ws_bytes};
     auto pi = g_plan.find(key);
     if (pi == g_plan.end()) {
+        if (g_plan.size() >= kMaxPlans) {
+            // every enqueued matmul has taken what it needs from its plan
+            for (auto &kv : g_plan)
+                destroy(kv.second);
+            g_plan.clear();
+        }
         GemmPlan p;
         p.ok = make_plan(h, M, N, K, bf16, ws_bytes, p);
+        if (!p.ok)
+            destroy(p);
         pi = g_plan.emplace(key, p).first;
     }
     return pi->second.ok ? &pi->second : nullptr;
