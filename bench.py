@@ -126,8 +126,9 @@ def work_items(t, nbits, group_size, axis):
 
 def solve_kernel_name(hq, fmt, wdtype, items):
     nb, gs, ax = fmt
-    if hq.hqq_solve_mapping(nb, gs, ax, wdtype, items) == hq.MAPPING_SEG:
-        return f"solve_seg_kernel<{nb},{gs}>"
+    m = hq.hqq_solve_mapping(nb, gs, ax, wdtype, items)
+    if m != hq.MAPPING_LANE:
+        return f"solve_seg_kernel<{nb},{gs},{2 if m == hq.MAPPING_SEG16 else 1}>"
     return f"solve_kernel<{nb},{gs},{ax},{'true' if wdtype == hq.DTYPE_BF16 else 'false'}>"
 
 

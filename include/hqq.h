@@ -142,13 +142,17 @@ HQQ_API int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype,
  * it is one group), HQQ_MAPPING_LANE: one lane per work item, the whole group
  * in its registers; HQQ_MAPPING_SEG: group_size / 8 lanes per group with 8
  * weights each, for axis 1, 32 <= group_size <= 128, fp16 weights and every
- * width but 3 bits, taken for launches too small to fill the device with one
- * lane per group (a threshold per width).  Both give identical outputs.
- * The environment variable HQQ_SOLVE_MAPPING=lane or =seg, read at each
- * call, forces one where the format allows it.  Invalid arguments: a
+ * width but 3 bits; HQQ_MAPPING_SEG16: group_size / 16 lanes per group with
+ * 16 weights each, for the same formats (1-bit codes from group_size 64).
+ * The several-lanes kernels are taken for launches too small to fill the
+ * device with one lane per group (a threshold per width): SEG16 for 4- and
+ * 8-bit codes, SEG for 1 and 2 bits.  All give identical outputs.  The environment variable
+ * HQQ_SOLVE_MAPPING=lane, =seg or =seg16, read at each call, forces one
+ * (where the format lacks it: one lane per work item).  Invalid arguments: a
  * negative HQQ_E* status. */
 #define HQQ_MAPPING_LANE 0
 #define HQQ_MAPPING_SEG 1
+#define HQQ_MAPPING_SEG16 2
 HQQ_API int hqq_solve_mapping(int nbits, int group_size, int axis, int wdtype, int64_t work_items);
 
 /* One tensor of a streamed quantize call: W in HOST memory, outputs on the

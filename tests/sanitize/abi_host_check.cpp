@@ -28,7 +28,7 @@ static int g_fail = 0;
 
 // ---------------------------------------------------------------- stubs
 static std::vector<hqq::SolveArgs> g_solve;
-static std::vector<bool> g_seg;
+static std::vector<int> g_seg;   // the mapping of each launch
 
 // linear layer routes: a log of (kind, weight's Y or W_hat, ...) in call order
 struct LinCall {
@@ -41,9 +41,10 @@ static std::vector<LinCall> g_lin;
 static bool g_gemm_ok = true;
 
 namespace hqq {
-hipError_t launch_solve(int nbits, int gs, int axis, bool bf16, bool seg, const SolveArgs &a, hipStream_t)
+hipError_t launch_solve(int nbits, int gs, int axis, bool bf16, int seg, const SolveArgs &a, hipStream_t)
 {
-    if (seg && !seg_format(nbits, gs, axis, bf16))
+    if ((seg == kMapSeg && !seg_format(nbits, gs, axis, bf16)) ||
+        (seg == kMapSeg16 && !seg16_format(nbits, gs, axis, bf16)))
         return hipErrorInvalidValue;
     g_solve.push_back(a);
     g_seg.push_back(seg);
@@ -144,24 +145,30 @@ static void check_launches(const std::vector<hqq_tensor> &ts, int nbits, int gs,
     const char *force = getenv("HQQ_SOLVE_MAPPING");
     for (size_t li = 0; li < g_solve.size(); ++li) {
         const hqq::SolveArgs &a = g_solve[li];
-        const bool seg = g_seg[li];
+        const int seg = g_seg[li];
         CHECK(a.n >= 1 && a.n <= hqq::kMaxBatch);
         CHECK(a.depth >= 1 && a.depth <= hqq::kMaxDepth);
         // several lanes per group: only where the format allows it, always
-        // when forced, never when one lane per item is forced
-        if (!hqq::seg_format(nbits, gs, axis, false))
-            CHECK(!seg);
+        // when forced (16 per lane: where the format has it), never when one
+        // lane per item is forced
+        const bool ok8 = hqq::seg_format(nbits, gs, axis, false), ok16 = hqq::seg16_format(nbits, gs, axis, false);
+        if (!ok8)
+            CHECK(seg == hqq::kMapLane);
         else if (force && strcmp(force, "seg") == 0)
-            CHECK(seg);
+            CHECK(seg == hqq::kMapSeg);
+        else if (force && strcmp(force, "seg16") == 0)
+            CHECK(seg == (ok16 ? hqq::kMapSeg16 : hqq::kMapLane));
         else if (force && strcmp(force, "lane") == 0)
-            CHECK(!seg);
-        const int64_t per = (seg ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(gs)
-                                 : (int64_t)hqq::kSolveBlock) * a.depth;
+            CHECK(seg == hqq::kMapLane);
+        const int64_t per = (seg != hqq::kMapLane ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(gs, seg)
+                                                  : (int64_t)hqq::kSolveBlock) * a.depth;
         int64_t items = 0;
         for (int j = 0; j < a.n; ++j)
             items += a.t[j].n_items;
-        if (!force && hqq::seg_format(nbits, gs, axis, false))
-            CHECK(seg == (items < hqq::seg_max_items(nbits)));
+        if (!force && ok8)
+            CHECK(seg == (items >= hqq::seg_max_items(nbits) ? hqq::kMapLane
+                          : ok16 && nbits >= 4             ? hqq::kMapSeg16
+                                                           : hqq::kMapSeg));
         int64_t b = 0;
         for (int j = 0; j < a.n; ++j, ++k) {
             CHECK(k < ts.size());
@@ -266,11 +273,11 @@ static void test_certificate()
 
 // Batched launches: 100 tensors of mixed shapes, every format and axis, small
 // and large (the automatic mapping changes at seg_max_items groups per
-// launch), with the mapping automatic or forced either way.
+// launch), with the mapping automatic or forced each way.
 static void test_batches()
 {
-    const int fmts[][3] = {{4, 64, 1}, {3, 64, 0}, {2, 16, 1}, {1, 16, 0}, {8, 128, 1}, {4, 32, 1}, {2, 64, 1}};
-    for (const char *force : {(const char *)nullptr, "lane", "seg"}) {
+    const int fmts[][3] = {{4, 64, 1}, {3, 64, 0}, {2, 16, 1}, {1, 16, 0}, {8, 128, 1}, {4, 32, 1}, {2, 64, 1}, {1, 32, 1}, {1, 64, 1}};
+    for (const char *force : {(const char *)nullptr, "lane", "seg", "seg16"}) {
         if (force)
             setenv("HQQ_SOLVE_MAPPING", force, 1);
         else

@@ -104,19 +104,26 @@ def test_linear_route(lib, monkeypatch):
 
 def test_solve_mapping(lib, monkeypatch):
     """The mapping query: several lanes per group only for the formats that
-    allow it, below each width's size threshold, and as forced by
-    HQQ_SOLVE_MAPPING; invalid arguments give the usual status codes."""
+    allow it, below each width's size threshold (16 weights per lane for 4-
+    and 8-bit codes, 8 for 1 and 2 bits), and as forced by HQQ_SOLVE_MAPPING;
+    invalid arguments give the usual status codes."""
     import weight_quantization_group_amd as hq
 
     f16, bf16 = hq.DTYPE_FP16, hq.DTYPE_BF16
     monkeypatch.delenv("HQQ_SOLVE_MAPPING", raising=False)
-    assert lib.hqq_solve_mapping(4, 64, 1, f16, 65536) == 1
+    assert lib.hqq_solve_mapping(4, 64, 1, f16, 65536) == 2
     assert lib.hqq_solve_mapping(4, 64, 1, f16, 10 ** 7) == 0
-    assert lib.hqq_solve_mapping(1, 64, 1, f16, 10 ** 6) == 1
+    assert lib.hqq_solve_mapping(1, 64, 1, f16, 10 ** 6) == 1      # 1 and 2 bits: 8 weights per lane
+    assert lib.hqq_solve_mapping(2, 32, 1, f16, 10 ** 5) == 1
+    assert lib.hqq_solve_mapping(8, 128, 1, f16, 10 ** 4) == 2
     for nb, gs, ax, dt in [(3, 64, 1, f16), (4, 16, 1, f16), (4, 256, 1, f16), (4, 64, 0, f16), (4, 64, 1, bf16)]:
         assert lib.hqq_solve_mapping(nb, gs, ax, dt, 1000) == 0, (nb, gs, ax, dt)
     monkeypatch.setenv("HQQ_SOLVE_MAPPING", "seg")
     assert lib.hqq_solve_mapping(4, 64, 1, f16, 10 ** 9) == 1
+    assert lib.hqq_solve_mapping(3, 64, 1, f16, 10) == 0
+    monkeypatch.setenv("HQQ_SOLVE_MAPPING", "seg16")
+    assert lib.hqq_solve_mapping(4, 64, 1, f16, 10 ** 9) == 2
+    assert lib.hqq_solve_mapping(1, 32, 1, f16, 10) == 0
     assert lib.hqq_solve_mapping(3, 64, 1, f16, 10) == 0
     monkeypatch.setenv("HQQ_SOLVE_MAPPING", "lane")
     assert lib.hqq_solve_mapping(4, 64, 1, f16, 10) == 0

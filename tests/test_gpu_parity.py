@@ -39,13 +39,25 @@ def seg_format(nbits, gs, axis):
     return axis == 1 and nbits != 3 and 32 <= gs <= 128
 
 
-@pytest.fixture(params=["lane", "seg"])
+def seg16_format(nbits, gs, axis):
+    """Formats the solve can also run with 16 weights per lane."""
+    return seg_format(nbits, gs, axis) and (nbits != 1 or gs >= 64)
+
+
+@pytest.fixture(params=["lane", "seg", "seg16"])
 def mapping(request, monkeypatch):
-    """Force the solve's mapping: one lane per work item, or gs/8 lanes per
-    group (the library picks by launch size; both must give identical
-    results)."""
+    """Force the solve's mapping: one lane per work item, gs/8 lanes per group
+    or gs/16 lanes per group (the library picks by launch size; all must give
+    identical results)."""
     monkeypatch.setenv("HQQ_SOLVE_MAPPING", request.param)
     return request.param
+
+
+def skip_mapping(mapping, nbits, gs, axis):
+    if mapping == "seg" and not seg_format(nbits, gs, axis):
+        pytest.skip("one mapping for this format")
+    if mapping == "seg16" and not seg16_format(nbits, gs, axis):
+        pytest.skip("no 16-weights-per-lane kernel for this format")
 
 
 def _dev16(W16: np.ndarray):
@@ -153,8 +165,7 @@ def _format_cases():
 
 @pytest.mark.parametrize("nbits,gs,axis", _format_cases())
 def test_quantize_formats(hq, oracle_mod, nbits, gs, axis, mapping):
-    if mapping == "seg" and not seg_format(nbits, gs, axis):
-        pytest.skip("one mapping for this format")
+    skip_mapping(mapping, nbits, gs, axis)
     rng = np.random.RandomState(nbits * 1000 + gs * 2 + axis)
     # several work items per wave plus a ragged last block along the line
     ngroups = 7 if gs <= 64 else 3
@@ -185,8 +196,7 @@ def test_quantize_formats(hq, oracle_mod, nbits, gs, axis, mapping):
     (1, 64, 1, 0.7, 100.0, 1.01),
 ])
 def test_quantize_shrink_paths(hq, oracle_mod, nbits, gs, axis, p, beta0, kappa, mapping):
-    if mapping == "seg" and not seg_format(nbits, gs, axis):
-        pytest.skip("one mapping for this format")
+    skip_mapping(mapping, nbits, gs, axis)
     rng = np.random.RandomState(int(p * 100) + nbits * 7 + gs + axis)
     shape = (64, gs * 9) if axis == 1 else (gs * 9, 64)
     W16 = random_f16(rng, shape, std=0.05, outlier_frac=0.01)
@@ -308,8 +318,7 @@ def test_synth_gpu_generator_matches_numpy():
 def test_iteration_counts(hq, oracle_mod, nbits, gs, axis, iters, mapping):
     """Groups that stop before, at and after the point where the solve parks
     unfinished groups for later batches, and long runs, match the oracle."""
-    if mapping == "seg" and not seg_format(nbits, gs, axis):
-        pytest.skip("one mapping for this format")
+    skip_mapping(mapping, nbits, gs, axis)
     rng = np.random.RandomState(iters * 100 + nbits * 10 + gs + axis)
     shape = (96, 1024) if axis == 1 else (1024, 96)
     W16 = random_f16(rng, shape, std=0.02, outlier_frac=0.001)

@@ -136,15 +136,15 @@ def hqq_strerror(status: int) -> str:
 
 
 def hqq_solve_mapping(nbits: int, group_size: int, axis: int, wdtype: int, work_items: int) -> int:
-    """MAPPING_LANE or MAPPING_SEG: the solve kernel a launch of work_items
-    work items of this format runs."""
+    """MAPPING_LANE, MAPPING_SEG or MAPPING_SEG16: the solve kernel a launch
+    of work_items work items of this format runs."""
     m = load_library().hqq_solve_mapping(nbits, group_size, axis, wdtype, work_items)
     if m < 0:
         raise HQQError("hqq_solve_mapping", m)
     return int(m)
 
 
-MAPPING_LANE, MAPPING_SEG = 0, 1
+MAPPING_LANE, MAPPING_SEG, MAPPING_SEG16 = 0, 1, 2
 
 
 def hqq_linear_route(M: int, K: int, count: int, n_max: int, workspace_bytes: int) -> int:

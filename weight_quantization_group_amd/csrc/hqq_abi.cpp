@@ -36,28 +36,42 @@ bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 bool finite_pos(float v) { return isfinite(v) && v > 0.0f; }
 
-// HQQ_SOLVE_MAPPING=lane or =seg forces the solve's mapping where the format
-// allows it (tests exercise both on the same inputs); otherwise the size of
-// the launch decides.  0: automatic, 1: one lane per work item, 2: several
-// lanes per group.
+// HQQ_SOLVE_MAPPING=lane, =seg or =seg16 forces the solve's mapping where
+// the format allows it (tests exercise each on the same inputs); otherwise the
+// size of the launch decides.  -1: automatic, else the forced SolveMapping.
 int mapping_override()
 {
     const char *e = getenv("HQQ_SOLVE_MAPPING");
     if (!e)
-        return 0;
+        return -1;
     if (strcmp(e, "lane") == 0)
-        return 1;
+        return hqq::kMapLane;
     if (strcmp(e, "seg") == 0)
-        return 2;
-    return 0;
+        return hqq::kMapSeg;
+    if (strcmp(e, "seg16") == 0)
+        return hqq::kMapSeg16;
+    return -1;
 }
 
-// The solve's mapping for a launch of `items` work items of a format that
-// allows both (seg_ok).
-bool use_seg(bool seg_ok, int nbits, int64_t items)
+// The solve's mapping for a launch of `items` work items of this format: one
+// lane per work item from seg_max_items groups; below it 16 weights per lane
+// for 4- and 8-bit codes and 8 for 1- and 2-bit codes (measured on lone
+// tensors: 16 per lane halves the per-group work per weight, but low widths
+// freeze many groups, whose exact finish runs a few groups at a time per wave,
+// so they gain more from more, smaller waves).  A forced mapping the format
+// lacks falls back to one lane per work item.
+int pick_mapping(int nbits, int gs, int axis, bool bf16, int64_t items)
 {
+    const bool seg_ok = hqq::seg_format(nbits, gs, axis, bf16);
+    const bool seg16_ok = hqq::seg16_format(nbits, gs, axis, bf16);
     const int force = mapping_override();
-    return seg_ok && (force == 2 || (force == 0 && items < hqq::seg_max_items(nbits)));
+    if (force == hqq::kMapSeg)
+        return seg_ok ? hqq::kMapSeg : hqq::kMapLane;
+    if (force == hqq::kMapSeg16)
+        return seg16_ok ? hqq::kMapSeg16 : hqq::kMapLane;
+    if (force == hqq::kMapLane || !seg_ok || items >= hqq::seg_max_items(nbits))
+        return hqq::kMapLane;
+    return seg16_ok && nbits >= 4 ? hqq::kMapSeg16 : hqq::kMapSeg;
 }
 
 // Threshold below which the lp shrinkage is provably inactive in every
@@ -237,7 +251,6 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
     const int C = hqq::codes_per_word(nbits);
     const int64_t lb = hqq::lcm_c(group_size, C);
     const int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
-    const bool seg_ok = hqq::seg_format(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16);
     // launches of as even a number of tensors as kMaxBatch allows
     const int launches = (n + hqq::kMaxBatch - 1) / hqq::kMaxBatch;
     const int per_launch = (n + launches - 1) / launches;
@@ -264,10 +277,11 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
         }
         // the mapping: one lane per work item, or gs / 8 lanes per group for
         // launches too small to fill the device that way
-        const bool seg = use_seg(seg_ok, nbits, items);
+        const int map = pick_mapping(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, items);
         // work items per workgroup at depth 1 (one item per lane, or
-        // 512 / gs groups per wave)
-        const int64_t unit = seg ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(group_size)
+        // seg_groups_per_wave groups per wave)
+        const int64_t unit = map != hqq::kMapLane
+                                 ? (int64_t)(hqq::kSolveBlock / 64) * hqq::seg_groups_per_wave(group_size, map)
                                  : (int64_t)hqq::kSolveBlock;
         // items per lane (or per wave's group slot): deep enough to overlap
         // each item's loads with the previous item's solve, shallow enough
@@ -286,7 +300,7 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
         }
         a.n = used;
         i += used;
-        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, seg, a,
+        const hipError_t e = hqq::launch_solve(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, map, a,
                                                (hipStream_t)stream);
         if (e != hipSuccess)
             return HQQ_EHIP;
@@ -307,9 +321,11 @@ int hqq_solve_mapping(int nbits, int group_size, int axis, int wdtype, int64_t w
         return HQQ_EINVAL_GROUP;
     if (work_items < 0)
         return HQQ_EINVAL_SHAPE;
-    return use_seg(hqq::seg_format(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16), nbits, work_items)
-               ? HQQ_MAPPING_SEG
-               : HQQ_MAPPING_LANE;
+    switch (pick_mapping(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, work_items)) {
+    case hqq::kMapSeg: return HQQ_MAPPING_SEG;
+    case hqq::kMapSeg16: return HQQ_MAPPING_SEG16;
+    default: return HQQ_MAPPING_LANE;
+    }
 }
 
 int hqq_quantize(const uint16_t *W, int64_t rows, int64_t cols, int nbits, int group_size,

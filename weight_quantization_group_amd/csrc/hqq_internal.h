@@ -38,19 +38,26 @@ constexpr int kSolveBlock = 256;
 constexpr int kMaxDepth = 8;
 constexpr int64_t kTargetBlocks = 8192;
 
-// The axis = 1 solve can also spread a group over gs / 8 lanes (8 weights per
-// lane, 512 / gs groups per wave): formats 32 <= gs <= 128, fp16 weights,
-// every code width but 3 bits.  The host takes it for launches of fewer than
-// seg_max_items groups (measured crossovers): below them one lane per group
-// leaves most of the device idle and a wave waits for the slowest of its 64
-// groups.  1-bit groups often need the exact finish, which runs up to
-// 64 / gs groups at a time per wave: many more waves win there at every size
-// measured.
+// The axis = 1 solve can also spread a group over several lanes: gs / 8 lanes
+// with 8 weights each (kMapSeg, 512 / gs groups per wave) or gs / 16 lanes with
+// 16 (kMapSeg16, 1024 / gs groups per wave): formats 32 <= gs <= 128, fp16
+// weights, every code width but 3 bits (16 per lane: 1-bit codes from gs = 64).
+// The host takes them for launches of fewer than seg_max_items groups
+// (measured crossovers; 16 per lane for 4- and 8-bit codes, 8 for 1 and 2
+// bits): below them one lane per group leaves most of the device idle and a
+// wave waits for the slowest of its 64 groups.  1-bit groups
+// often need the exact finish, which runs up to 64 / gs groups at a time per
+// wave: many more waves win there at every size measured.
+enum SolveMapping { kMapLane = 0, kMapSeg = 1, kMapSeg16 = 2 };
 constexpr bool seg_format(int nbits, int gs, int axis, bool bf16)
 {
     return axis == 1 && !bf16 && nbits != 3 && gs >= 32 && gs <= 128;
 }
-constexpr int seg_groups_per_wave(int gs) { return 512 / gs; }
+constexpr bool seg16_format(int nbits, int gs, int axis, bool bf16)
+{
+    return seg_format(nbits, gs, axis, bf16) && (nbits != 1 || gs >= 64);
+}
+constexpr int seg_groups_per_wave(int gs, int map) { return (map == kMapSeg16 ? 1024 : 512) / gs; }
 constexpr int64_t seg_max_items(int nbits)
 {
     return nbits == 1 ? (int64_t(1) << 23) : nbits == 8 ? (int64_t(1) << 16) : int64_t(320) << 10;
@@ -129,8 +136,9 @@ int check_params(int iters, float p, float beta0, float kappa);
 int check_tensor(const ::hqq_tensor &t, int nbits, int group_size, int axis);
 
 // launchers (return hipError_t of the launch)
-// seg: the several-lanes-per-group kernel (a format seg_format accepts)
-hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, bool seg, const SolveArgs &a,
+// map: kMapLane, or a several-lanes-per-group kernel (kMapSeg for a format
+// seg_format accepts, kMapSeg16 for one seg16_format accepts)
+hipError_t launch_solve(int nbits, int group_size, int axis, bool bf16, int map, const SolveArgs &a,
                         hipStream_t s);
 hipError_t launch_dequantize(int nbits, int axis, const CodecArgs &a, hipStream_t s);
 hipError_t launch_pack(int nbits, int axis, const CodecArgs &a, hipStream_t s);

@@ -4,5 +4,5 @@
 #include "hqq_solve_impl.h"
 
 namespace hqq {
-template hipError_t launch_solve_nb<2, true>(int, int, bool, const SolveArgs &, hipStream_t);
+template hipError_t launch_solve_nb<2, true>(int, int, int, const SolveArgs &, hipStream_t);
 }  // namespace hqq

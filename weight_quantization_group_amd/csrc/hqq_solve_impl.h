@@ -388,13 +388,14 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
     }
 }
 
-// Sum over the SEG lanes of a compact group (aligned blocks of 4, 8 or 16
+// Sum over the SEG lanes of a group (aligned blocks of 2, 4, 8 or 16
 // lanes) with DPP row permutations; every lane gets the total.
 template <int SEG>
 __device__ __forceinline__ int seg_sum(int v)
 {
     v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);          // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);          // quad_perm [2,3,0,1]
+    if constexpr (SEG >= 4)
+        v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);      // quad_perm [2,3,0,1]
     if constexpr (SEG >= 8)
         v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);     // row_half_mirror
     if constexpr (SEG >= 16)
@@ -418,7 +419,8 @@ template <int SEG>
 __device__ __forceinline__ double seg_sum_f64(double v)
 {
     v += dpp_f64<0xB1>(v);
-    v += dpp_f64<0x4E>(v);
+    if constexpr (SEG >= 4)
+        v += dpp_f64<0x4E>(v);
     if constexpr (SEG >= 8)
         v += dpp_f64<0x141>(v);
     if constexpr (SEG >= 16)
@@ -1170,17 +1172,31 @@ hipError_t launch_gs(int group_size, const SolveArgs &a, hipStream_t st)
 // launcher of the NB-bit solve kernels for fp16 (BF = false) or bf16 inputs
 // (defined in hqq_solve_b<NB>.hip and hqq_solve_b<NB>_bf16.hip)
 template <int NB, bool BF>
-hipError_t launch_solve_nb(int group_size, int axis, bool seg, const SolveArgs &a, hipStream_t st)
+hipError_t launch_solve_nb(int group_size, int axis, int map, const SolveArgs &a, hipStream_t st)
 {
-    if (seg) {
+    if (map != kMapLane) {
         if constexpr (NB != 3 && !BF) {
             const dim3 block(kBlock);
             const dim3 grid((unsigned)a.blocks);
-            switch (group_size) {
-            case 32: hipLaunchKernelGGL((solve_seg_kernel<NB, 32>), grid, block, 0, st, a); break;
-            case 64: hipLaunchKernelGGL((solve_seg_kernel<NB, 64>), grid, block, 0, st, a); break;
-            case 128: hipLaunchKernelGGL((solve_seg_kernel<NB, 128>), grid, block, 0, st, a); break;
-            default: return hipErrorInvalidValue;
+            if (map == kMapSeg) {
+                switch (group_size) {
+                case 32: hipLaunchKernelGGL((solve_seg_kernel<NB, 32, 1>), grid, block, 0, st, a); break;
+                case 64: hipLaunchKernelGGL((solve_seg_kernel<NB, 64, 1>), grid, block, 0, st, a); break;
+                case 128: hipLaunchKernelGGL((solve_seg_kernel<NB, 128, 1>), grid, block, 0, st, a); break;
+                default: return hipErrorInvalidValue;
+                }
+            } else {
+                switch (group_size) {
+                case 32:
+                    if constexpr (NB != 1)
+                        hipLaunchKernelGGL((solve_seg_kernel<NB, 32, 2>), grid, block, 0, st, a);
+                    else
+                        return hipErrorInvalidValue;
+                    break;
+                case 64: hipLaunchKernelGGL((solve_seg_kernel<NB, 64, 2>), grid, block, 0, st, a); break;
+                case 128: hipLaunchKernelGGL((solve_seg_kernel<NB, 128, 2>), grid, block, 0, st, a); break;
+                default: return hipErrorInvalidValue;
+                }
             }
             return hipGetLastError();
         }
