@@ -544,3 +544,46 @@ def test_linear_gemm_route_many_row_counts(hq, oracle_mod, monkeypatch):
             checked += 1
     torch.cuda.synchronize()
     assert checked == 6
+
+
+@pytest.mark.parametrize("path", ["gemm", "fused"])
+def test_linear_routes_in_a_replayed_graph(hq, oracle_mod, monkeypatch, path):
+    """Both routes captured in a HIP graph (after an eager call, which creates
+    the GEMM plan outside capture), replayed three times with eager work and
+    synchronizations between the replays: every replay's outputs meet the
+    bound and equal the eager call's."""
+    import torch
+
+    monkeypatch.setenv("HQQ_LINEAR_PATH", path)
+    rng = np.random.RandomState(21)
+    M, K, nbits, gs, Ns = 320, 1024, 4, 64, [512, 256]
+    X16 = random_f16(rng, (M, K), std=1.0, outlier_frac=0.0)
+    Xd = _cuda(X16)
+    ws = [random_quantized(oracle_mod, rng, N, K, nbits, gs, solve=False) for N in Ns]
+    items = [(_cuda(p), _cuda(s), _cuda(z), N, torch.empty((M, N), dtype=torch.float16, device="cuda"))
+             for (p, s, z), N in zip(ws, Ns)]
+    work = torch.empty(hq.linear_workspace_bytes(M, Ns, K) // 4, dtype=torch.float32, device="cuda")
+    b = hq.LinearBatch(items, nbits, gs, workspace=work)
+    eager = [Y.clone() for Y in b.run(Xd)]
+    torch.cuda.synchronize()
+    refs = [oracle_mod.linear(X16, p, s, z, N, nbits, gs, with_abs=True) for (p, s, z), N in zip(ws, Ns)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            b.run(Xd)
+    torch.cuda.synchronize()
+    other = torch.randn(512, 512, device="cuda")
+    for rep in range(3):
+        for it in items:
+            it[4].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for it, E, (Yref, A), N in zip(items, eager, refs, Ns):
+            Y = it[4]
+            check(Y.cpu().numpy(), Yref, A, K, f"{path} replay {rep} N={N}")
+            assert torch.equal(Y.view(torch.int16), E.view(torch.int16)), f"{path} replay {rep} differs from eager"
+        other = (other @ other).clamp_(-1, 1)   # eager work between replays
+        torch.cuda.synchronize()
