@@ -275,8 +275,9 @@ int hqq_quantize_batch_ex(const hqq_tensor *tensors, int n, int wdtype, int nbit
             items += d.n_items;
             ++a.n;
         }
-        // the mapping: one lane per work item, or gs / 8 lanes per group for
-        // launches too small to fill the device that way
+        // the mapping: one lane per work item, or several lanes per group
+        // (8 or 16 weights each) for launches too small to fill the device
+        // that way
         const int map = pick_mapping(nbits, group_size, axis, wdtype == HQQ_DTYPE_BF16, items);
         // work items per workgroup at depth 1 (one item per lane, or
         // seg_groups_per_wave groups per wave)
