@@ -34,9 +34,12 @@ constexpr int kMaxBatch = 48;
 constexpr int kSolveBlock = 256;
 // A workgroup solves depth * kSolveBlock work items (depth steps per lane);
 // the host picks depth so that a launch still has about kTargetBlocks
-// workgroups.
-constexpr int kMaxDepth = 8;
-constexpr int64_t kTargetBlocks = 8192;
+// workgroups.  Deeper workgroups overlap more loads with solves but end a
+// launch more raggedly: on the 7B stack's 44-tensor launches depth 4 ran 2%
+// faster than 8, and 2 ran 0.7% slower than 4; depth 1 cost 6% on one 7B
+// layer at 2 bits (axis 0).
+constexpr int kMaxDepth = 4;
+constexpr int64_t kTargetBlocks = 16384;
 
 // The axis = 1 solve can also spread a group over several lanes: gs / 8 lanes
 // with 8 weights each (kMapSeg, 512 / gs groups per wave) or gs / 16 lanes with
