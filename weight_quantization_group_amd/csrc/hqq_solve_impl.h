@@ -785,7 +785,11 @@ __device__ __forceinline__ uint32_t code_sum(const float (&w)[GS], float s, floa
 // Fast iterations of the lanes with r.run, up to iters: a lane freezes its
 // group at the first iteration whose certificate fails, and stops once its
 // zero is a fixed point (r.it = iters then).  With wf: compact mode once at
-// most Compact::B groups of the wave still iterate.
+// most Compact::B groups of the wave still iterate.  The loop is divergent:
+// a lane leaves it when its group freezes or is done (the hardware's exec
+// mask carries that state, so the loop keeps no per-lane flags), and the
+// wave-wide choices -- compact mode, the clamp at qmax -- are ballots over
+// the lanes still in it.
 template <int NB, int GS, bool BF>
 __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[GS], const GroupInit &g,
                                            LaneRun &r, WaveFinish<GS> *wf = nullptr)
@@ -796,53 +800,61 @@ __device__ __forceinline__ void fast_iters(const SolveArgs &a, const float (&w)[
     const float thr_s = a.thr * s;
     const float lim = a.thr_m * s;
     const double ssw = (double)s * g.sw;
-    if (a.iters == 0)
-        r.run = false;
-    while (__any(r.run)) {
-        if constexpr (Compact<GS>::ON) {
-            if (wf != nullptr && __popcll(__ballot(r.run)) <= Compact<GS>::B) {
-                compact_iters<NB, GS, BF>(a, *wf, w, g, r);
+    float z = r.z, beta = r.beta;
+    int it = r.it;
+    bool frozen = false, compact = false;
+    if (r.run && a.iters > 0) {
+        while (true) {
+            if constexpr (Compact<GS>::ON) {
+                if (wf != nullptr && __popcll(__ballot(1)) <= Compact<GS>::B) {
+                    compact = true;
+                    break;
+                }
+            }
+            const float tmin = __builtin_fmaf(g.mn, s, z);
+            const float tmax = __builtin_fmaf(g.mx, s, z);
+            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
+            const bool est_ok = __builtin_fmaf(g.amag, s, fabsf(z)) + QMAX <= lim;
+            if (!(est_ok && bound <= thr_s)) {
+                frozen = true;
                 break;
             }
-        }
-        const float tmax = __builtin_fmaf(g.mx, s, r.z);
-        if (r.run) {
-            const float tmin = __builtin_fmaf(g.mn, s, r.z);
-            const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
-            const bool est_ok = __builtin_fmaf(g.amag, s, fabsf(r.z)) + QMAX <= lim;
-            if (!(est_ok && bound <= thr_s)) {
-                r.run = false;
-                r.frozen = true;
-            }
-        }
-        // The clamp at qmax can bind only where the largest weight's t
-        // rounds above qmax (the fma is monotone in w); when no running lane
-        // of the wave is there (uniform branch), the codes are summed
-        // without it.  8-bit codes never need it: the conversion saturates
-        // at 255.
-        const bool top = NB < 8 && __any(r.run && !(tmax < QMAX + 0.5f));
-        uint32_t sq = 0;
-        if (top) {
-            if (r.run)
-                sq = code_sum<NB, GS, true>(w, s, r.z);
-        } else {
-            if (r.run)
-                sq = code_sum<NB, GS, false>(w, s, r.z);
-        }
-        if (r.run) {
-            const float z = r.z;
+            // The clamp at qmax can bind only where the largest weight's t
+            // rounds above qmax (the fma is monotone in w); when no lane of
+            // the wave still iterating is there (uniform branch), the codes
+            // are summed without it.  8-bit codes never need it: the
+            // conversion saturates at 255.
+            const bool top = NB < 8 && __any(!(tmax < QMAX + 0.5f));
+            // (the clamped variant adds +0 to the zero, which changes no
+            // code -- t = +-0 gives code 0 either way -- and keeps the two
+            // variants' fmas apart: merged above the branch, their gs
+            // results would all be live at once)
+            uint32_t sq;
+            if (top)
+                sq = code_sum<NB, GS, true>(w, s, z + 0.0f);
+            else
+                sq = code_sum<NB, GS, false>(w, s, z);
             const float zn = (float)(((double)sq - ssw) * INV_GS);
             // Fixed point: the next zero depends on the current one only
             // through the codes, which are equal for equal zeros (+0 and -0
             // included), and the certificate is the same for every remaining
             // iteration; so every later iteration returns zn again, bit for
             // bit, and the group is done.
-            r.it = zn == z ? a.iters : r.it + 1;
-            r.beta = r.beta * a.kappa;
-            r.z = zn;
-            if (r.it >= a.iters)
-                r.run = false;
+            it = zn == z ? a.iters : it + 1;
+            beta = beta * a.kappa;
+            z = zn;
+            if (it >= a.iters)
+                break;
         }
+    }
+    r.z = z;
+    r.beta = beta;
+    r.it = it;
+    r.frozen = frozen;
+    r.run = compact;
+    if constexpr (Compact<GS>::ON) {
+        if (__any(compact))
+            compact_iters<NB, GS, BF>(a, *wf, w, g, r);
     }
 }
 
