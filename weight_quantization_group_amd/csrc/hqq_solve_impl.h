@@ -698,37 +698,37 @@ __device__ __forceinline__ void compact_iters(const SolveArgs &a, WaveFinish<GS>
     const double ssw = (double)s * st.sw;
     float z = st.z, beta = st.beta;
     int it = st.it;
-    bool run = act, frozen = false;
-    while (__any(run)) {
-        if (run) {
+    bool frozen = false;
+    // a divergent loop: a group's SEG lanes take every decision from the
+    // same sums, so they leave it together, and the DPP sums only read lanes
+    // of the group, which are then all still in it
+    if (act) {
+        while (true) {
             const float tmin = __builtin_fmaf(st.mn, s, z);
             const float tmax = __builtin_fmaf(st.mx, s, z);
             const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
             const bool est_ok = __builtin_fmaf(st.amag, s, fabsf(z)) + QMAX <= lim;
             if (!(est_ok && bound <= thr_s)) {
-                run = false;
                 frozen = true;
+                break;
             }
-        }
-        // every lane computes (the DPP sums read whole blocks of lanes)
-        uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[0], s, z), 0, 0u);
-        uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4], s, z), 0, 0u);
+            uint32_t d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[0], s, z), 0, 0u);
+            uint32_t d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4], s, z), 0, 0u);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) {
-            d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[j], s, z), j, d0);
-            d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 + j], s, z), j, d1);
-        }
-        const uint32_t c = __builtin_amdgcn_sad_u8(d1, 0u, __builtin_amdgcn_sad_u8(d0, 0u, 0u));
-        const uint32_t q = __builtin_amdgcn_sad_u8(d1, QB, __builtin_amdgcn_sad_u8(d0, QB, 0u));
-        const int tot = seg_sum<K::SEG>((int)c - (int)q);
-        const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
-        const float zn = (float)(((double)sq - ssw) * INV_GS);
-        if (run) {
+            for (int j = 1; j < 4; ++j) {
+                d0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[j], s, z), j, d0);
+                d1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 + j], s, z), j, d1);
+            }
+            const uint32_t c = __builtin_amdgcn_sad_u8(d1, 0u, __builtin_amdgcn_sad_u8(d0, 0u, 0u));
+            const uint32_t q = __builtin_amdgcn_sad_u8(d1, QB, __builtin_amdgcn_sad_u8(d0, QB, 0u));
+            const int tot = seg_sum<K::SEG>((int)c - (int)q);
+            const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
+            const float zn = (float)(((double)sq - ssw) * INV_GS);
             it = zn == z ? a.iters : it + 1;
             beta = beta * a.kappa;
             z = zn;
             if (it >= a.iters)
-                run = false;
+                break;
         }
     }
     wave_sync();

@@ -170,41 +170,41 @@ void solve_seg_kernel(SolveArgs a)
         const float lim = a.thr_m * s;
         const double ssw = (double)s * sw;
 
-        // iterations under the certificate, as in the lane-per-group kernel
+        // iterations under the certificate, as in the lane-per-group kernel.
+        // The loop is divergent: a group's lanes take every decision from the
+        // same sums, so they leave it together, and the DPP sums only read
+        // lanes of the group, which are then all still in it.
         float beta = a.beta0;
         int it = 0;
-        bool run = valid && a.iters > 0, frozen = false;
-        while (__any(run)) {
-            if (run) {
+        bool frozen = false;
+        if (valid && a.iters > 0) {
+            while (true) {
                 const float tmin = __builtin_fmaf(mn, s, z);
                 const float tmax = __builtin_fmaf(mx, s, z);
                 const float bound = fmaxf(0.5f, fmaxf(-tmin, tmax - QMAX));
                 const bool est_ok = __builtin_fmaf(amag, s, fabsf(z)) + QMAX <= lim;
                 if (!(est_ok && bound <= thr_s)) {
-                    run = false;
                     frozen = true;
+                    break;
                 }
-            }
-            // every lane computes (the DPP sums read whole blocks of lanes)
-            uint32_t c = 0u, q = 0u;
+                uint32_t c = 0u, q = 0u;
 #pragma unroll
-            for (int h = 0; h < 2 * CH; ++h) {
-                uint32_t d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 * h], s, z), 0, 0u);
+                for (int h = 0; h < 2 * CH; ++h) {
+                    uint32_t d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 * h], s, z), 0, 0u);
 #pragma unroll
-                for (int k = 1; k < 4; ++k)
-                    d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 * h + k], s, z), k, d);
-                c = __builtin_amdgcn_sad_u8(d, 0u, c);
-                q = __builtin_amdgcn_sad_u8(d, QB, q);
-            }
-            const int tot = seg_sum<S::SEG>((int)c - (int)q);
-            const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
-            const float zn = (float)(((double)sq - ssw) * INV_GS);
-            if (run) {
+                    for (int k = 1; k < 4; ++k)
+                        d = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(we[4 * h + k], s, z), k, d);
+                    c = __builtin_amdgcn_sad_u8(d, 0u, c);
+                    q = __builtin_amdgcn_sad_u8(d, QB, q);
+                }
+                const int tot = seg_sum<S::SEG>((int)c - (int)q);
+                const uint32_t sq = (uint32_t)(tot + GS * ((1 << NB) - 1)) >> 1;
+                const float zn = (float)(((double)sq - ssw) * INV_GS);
                 it = zn == z ? a.iters : it + 1;
                 beta = beta * a.kappa;
                 z = zn;
                 if (it >= a.iters)
-                    run = false;
+                    break;
             }
         }
 
