@@ -323,15 +323,14 @@ __device__ __forceinline__ uint32_t fold_codes(uint32_t d0, uint32_t d1)
 }
 
 // Pack a group's final codes into the work item's words.  8-bit: a word is
-// four clamped bytes.  4-bit groups that start on a word: eight codes per
-// word as bytes (v_cvt_pk_u8_f32 of the
-// clamped value: round half to even of clamp(t) equals clamp of the rounded
-// t), nibble pairs folded with a shift-or, and the four nibble-pair bytes
-// gathered with v_perm_b32.  2- and 1-bit groups of whole bytes: eight
-// codes as bytes, folded into their fields.  Other formats: code by code.
-// TOP = false: the caller has shown that no t of the group rounds above qmax
-// and that t is never NaN; the conversion's saturation at 0 is then the whole
-// clamp.
+// four clamped bytes.  4-, 2- and 1-bit groups of whole bytes: the codes as
+// bytes (v_cvt_pk_u8_f32 of the clamped value: round half to even of
+// clamp(t) equals clamp of the rounded t) in R = 8 / nbits byte words whose
+// byte k holds code R k + r of the word's run, so the packed word (or the
+// group's part of one) is (R - 1) shift-ors of them, LSB first.  Other
+// formats: code by code.  TOP = false: the caller has shown that no t of the
+// group rounds above qmax and that t is never NaN; the conversion's
+// saturation at 0 is then the whole clamp.
 template <int NB, int GS, int G, int WPB, bool TOP = true>
 __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float z,
                                            uint32_t (&words)[WPB])
@@ -342,32 +341,23 @@ __device__ __forceinline__ void pack_codes(const float (&w)[GS], float s, float 
         const float t = __builtin_fmaf(x, s, z);
         return TOP ? __builtin_amdgcn_fmed3f(t, 0.0f, QMAX) : t;
     };
-    if constexpr (NB == 4 && (G * GS) % 8 == 0 && GS % 8 == 0) {
+    if constexpr ((NB == 4 || NB == 2 || NB == 1) && GS % 8 == 0 && (G * GS) % (C < GS ? C : GS) == 0) {
+        constexpr int R = 8 / NB;                       // byte words per packed word
+        constexpr int RUN = C < GS ? C : GS;            // codes per run (a word, or the group's part of one)
+        constexpr int NBYTE = RUN / R;                  // bytes per byte word
 #pragma unroll
-        for (int q = 0; q < GS / 8; ++q) {
-            uint32_t d0 = 0, d1 = 0;
+        for (int q = 0; q < GS / RUN; ++q) {
+            uint32_t x = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d0 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + j]), j, d0);
-                d1 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + 4 + j]), j, d1);
+            for (int r = 0; r < R; ++r) {
+                uint32_t d = 0;
+#pragma unroll
+                for (int k = 0; k < NBYTE; ++k)
+                    d = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[RUN * q + R * k + r]), k, d);
+                x = r == 0 ? d : (d << (NB * r)) | x;
             }
-            const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
-            const uint32_t x1 = d1 | (d1 >> 4);
-            words[(G * GS) / 8 + q] |= __builtin_amdgcn_perm(x1, x0, 0x06040200u);
-        }
-    } else if constexpr ((NB == 2 || NB == 1) && (G * GS) % 8 == 0 && GS % 8 == 0) {
-        // eight codes at a time as bytes, folded into NB-bit fields
-        constexpr int C2 = codes_per_word(NB);
-#pragma unroll
-        for (int q = 0; q < GS / 8; ++q) {
-            uint32_t d0 = 0, d1 = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d0 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + j]), j, d0);
-                d1 = __builtin_amdgcn_cvt_pk_u8_f32(clamped(w[8 * q + 4 + j]), j, d1);
-            }
-            const int n0 = G * GS + 8 * q;
-            words[n0 / C2] |= fold_codes<NB>(d0, d1) << ((n0 % C2) * NB);
+            const int n0 = G * GS + RUN * q;
+            words[n0 / C] |= x << ((n0 % C) * NB);
         }
     } else if constexpr (NB == 8) {
         // four codes per word: the word is the four clamped bytes
