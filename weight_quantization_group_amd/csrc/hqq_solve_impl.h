@@ -296,32 +296,6 @@ struct WaveFinish {
     CompactGroup cg[Compact<GS>::ON ? Compact<GS>::B : 1];
 };
 
-// Eight clamped codes of a lane (bytes of d0: codes 0-3, d1: codes 4-7,
-// each <= qmax) folded into NB-bit fields, LSB first: 4 bits: one word;
-// 2 bits: the low 16 bits; 1 bit: the low 8.
-template <int NB>
-__device__ __forceinline__ uint32_t fold_codes(uint32_t d0, uint32_t d1)
-{
-    if constexpr (NB == 4) {
-        const uint32_t x0 = d0 | (d0 >> 4);   // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
-        const uint32_t x1 = d1 | (d1 >> 4);
-        return __builtin_amdgcn_perm(x1, x0, 0x06040200u);
-    } else if constexpr (NB == 2) {
-        uint32_t x0 = d0 | (d0 >> 6);         // bits 0-3: c0 c1, bits 16-19: c2 c3
-        uint32_t x1 = d1 | (d1 >> 6);
-        x0 = (x0 | (x0 >> 12)) & 0xFFu;       // bits 0-7: c0 c1 c2 c3
-        x1 = (x1 | (x1 >> 12)) & 0xFFu;
-        return x0 | (x1 << 8);
-    } else {
-        static_assert(NB == 1, "8-bit codes are stored as bytes");
-        uint32_t x0 = d0 | (d0 >> 7);         // bits 0-1: c0 c1, bits 16-17: c2 c3
-        uint32_t x1 = d1 | (d1 >> 7);
-        x0 = (x0 | (x0 >> 14)) & 0xFu;        // bits 0-3: c0 c1 c2 c3
-        x1 = (x1 | (x1 >> 14)) & 0xFu;
-        return x0 | (x1 << 4);
-    }
-}
-
 // Pack a group's final codes into the work item's words.  8-bit: a word is
 // four clamped bytes.  4-, 2- and 1-bit groups of whole bytes: the codes as
 // bytes (v_cvt_pk_u8_f32 of the clamped value: round half to even of

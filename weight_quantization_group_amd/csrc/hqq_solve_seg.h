@@ -245,29 +245,41 @@ void solve_seg_kernel(SolveArgs a)
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             const int p = k * S::SEG + j;
-            uint32_t d0 = 0, d1 = 0;
+            auto code = [&](int e) { return __builtin_amdgcn_fmed3f(__builtin_fmaf(we[8 * k + e], s, z), 0.0f, QMAX); };
+            // the chunk's eight codes packed LSB first (8 bits: two words of
+            // bytes; else R = 8 / nbits byte words, byte i of word r holding
+            // code R i + r, joined by R - 1 shift-ors)
+            uint32_t d0 = 0, d1 = 0, h = 0;
+            if constexpr (NB == 8) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d0 = __builtin_amdgcn_cvt_pk_u8_f32(
-                    __builtin_amdgcn_fmed3f(__builtin_fmaf(we[8 * k + e], s, z), 0.0f, QMAX), e, d0);
-                d1 = __builtin_amdgcn_cvt_pk_u8_f32(
-                    __builtin_amdgcn_fmed3f(__builtin_fmaf(we[8 * k + 4 + e], s, z), 0.0f, QMAX), e, d1);
+                for (int e = 0; e < 4; ++e) {
+                    d0 = __builtin_amdgcn_cvt_pk_u8_f32(code(e), e, d0);
+                    d1 = __builtin_amdgcn_cvt_pk_u8_f32(code(4 + e), e, d1);
+                }
+            } else {
+                constexpr int R = 8 / NB;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint32_t d = 0;
+#pragma unroll
+                    for (int i = 0; i < 8 / R; ++i)
+                        d = __builtin_amdgcn_cvt_pk_u8_f32(code(R * i + r), i, d);
+                    h = r == 0 ? d : (d << (NB * r)) | h;
+                }
             }
             if constexpr (NB == 8) {
                 if (valid)
                     *reinterpret_cast<uint2 *>(gw + 2 * p) = uint2{d0, d1};
             } else if constexpr (NB == 4) {
                 if (valid)
-                    gw[p] = fold_codes<4>(d0, d1);
+                    gw[p] = h;
             } else if constexpr (NB == 2) {
                 // a word holds the 16 codes of chunks p, p + 1 (lanes j, j + 1, j even)
-                const uint32_t h = fold_codes<2>(d0, d1);
                 const uint32_t w = h | ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xB1, 0xF, 0xF, false) << 16);
                 if (valid && (j & 1) == 0)
                     gw[p >> 1] = w;
             } else {
                 // a word holds the 32 codes of chunks p .. p + 3 (lanes j .. j + 3, j % 4 == 0)
-                const uint32_t h = fold_codes<1>(d0, d1);
                 const uint32_t w = h | ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0x55, 0xF, 0xF, false) << 8) |
                                    ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xAA, 0xF, 0xF, false) << 16) |
                                    ((uint32_t)__builtin_amdgcn_mov_dpp((int)h, 0xFF, 0xF, 0xF, false) << 24);
